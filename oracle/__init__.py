@@ -1,0 +1,43 @@
+"""Float64 CPU oracle for the polynomial-method sketch and the exact streaming path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or helper
+with the HIP library; the only thing both sides share is the seeded input
+generator in ``synthetic/``, which holds none of the method's arithmetic.
+
+What it follows (the pages are summaries of a theory paper and print no formula,
+listing or worked example for this path; the readings taken are listed in the
+repository's design notes):
+
+* "Rumo a Limites Estritos para Atenção em Streaming" (gist.science, pt),
+  section "Definição do Problema": a query q is answered against the stream of
+  key/value pairs seen so far; the quantities wanted are the kernel-density
+  normaliser (softmax KDE) and the attention vector.  The naive answer keeps every
+  pair.  -> ``exact.exact_attention`` (kernel exp<q, k>, no extra scale).
+* Same page, "Metodologia", pillar "O Método Polinomial" (and the French page
+  "Vers des Bornes Serrées pour l'Attention en Flux", "Méthodologie", "La Méthode
+  Polynomiale"): the head of the exponential kernel is replaced by a truncated
+  Taylor expansion and the stream is summarised by its low-degree moments.
+  -> ``sketch.sketch_direct`` (the value the method reaches, written as its plain
+  definition) and ``sketch.MomentSketch`` (the method's steps: feature map,
+  moments, query).
+* Same section, closing paragraph on Merge-and-Reduce: summaries of sub-streams
+  are merged.  Moments are sums, so the merge is an addition.
+  -> ``sketch.MomentSketch.merge``.
+* ``bounds``: the Lagrange form of the Taylor remainder, carried through the sums
+  (derived here; the pages state only asymptotic space bounds).
+
+Pins: every function here is checked in ``tests/test_oracle.py`` against brute
+force on tiny inputs, closed forms, identities and library routines (see the
+docstrings there).  No function of this package is "parity unpinned".
+"""
+
+from .exact import exact_attention
+from .sketch import taylor_exp, sketch_direct, MomentSketch, feature_map
+from .bounds import (taylor_term_bound, kde_relative_bound, attention_abs_bound,
+                     measured_radius)
+
+__all__ = ["exact_attention", "taylor_exp", "sketch_direct", "MomentSketch",
+           "feature_map", "taylor_term_bound", "kde_relative_bound",
+           "attention_abs_bound", "measured_radius"]

@@ -1,0 +1,276 @@
+"""Pin checks for the float64 oracle, written against an implementation object.
+
+Each ``pin_*`` function takes ``impl`` (anything with the attributes
+``exact_attention``, ``sketch_direct``, ``MomentSketch`` and ``taylor_exp``, such as
+the ``oracle`` package itself) and returns the largest error it finds against a
+reference that does not come from the oracle: brute-force Kronecker powers
+(``np.kron``), closed forms, identities, hand-worked examples, library routines
+(``scipy.special``, ``mpmath``).  ``tests/test_oracle.py`` asserts the errors are at
+rounding level; ``tests/test_oracle_mutants.py`` plants mistakes in copies of the
+oracle and asserts that some pin catches each one.
+"""
+
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import scipy.special
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def relmax(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300)))
+
+
+def absmax(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def kron_power(x, j):
+    """x^(x)j built by repeated np.kron (independent of the oracle's features)."""
+    r = np.ones(1)
+    for _ in range(j):
+        r = np.kron(r, x)
+    return r
+
+
+def taylor_coeffs(p):
+    """Taylor coefficients of exp at 0 from mpmath's numerical differentiation."""
+    return [float(c) for c in mpmath.taylor(mpmath.exp, 0, p)]
+
+
+def _small(seed, n, m, d, dv, scale=0.7):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((n, d)) * scale
+    V = rng.standard_normal((n, dv))
+    Q = rng.standard_normal((m, d)) * scale
+    return K, V, Q
+
+
+# P1: brute force with explicit tensor powers --------------------------------------
+
+def pin_bruteforce(impl, d, p, n=23, m=4, dv=3, seed=1):
+    K, V, Q = _small(seed + 10 * d + p, n, m, d, dv)
+    coef = taylor_coeffs(p)
+    Zb = np.zeros(m)
+    Nb = np.zeros((m, dv))
+    for qi in range(m):
+        for i in range(n):
+            w = sum(coef[j] * float(kron_power(Q[qi], j) @ kron_power(K[i], j))
+                    for j in range(p + 1))
+            Zb[qi] += w
+            Nb[qi] += w * V[i]
+    ob = Nb / Zb[:, None]
+    od, Zd = impl.sketch_direct(K, V, Q, p)
+    sk = impl.MomentSketch(d, dv, p).update(K, V, chunk=7)
+    om, Zm = sk.query(Q)
+    err = max(relmax(Zd, Zb), relmax(Zm, Zb), absmax(od, ob), absmax(om, ob))
+    # the state itself: level j rows hold sum_i k_i^(x)j and sum_i k_i^(x)j v_i^T
+    S = sk.canonical_state()
+    off = 0
+    for j in range(p + 1):
+        Mj = sum(kron_power(K[i], j) for i in range(n))
+        Nj = sum(np.outer(kron_power(K[i], j), V[i]) for i in range(n))
+        err = max(err, absmax(S[off:off + d ** j, 0], Mj),
+                  absmax(S[off:off + d ** j, 1:], Nj))
+        off += d ** j
+    if S.shape != (off, 1 + dv):
+        return math.inf
+    return err
+
+
+# P2: moment route equals the direct route ----------------------------------------
+
+def pin_moment_equals_direct(impl, K, V, Q, p, chunk=64):
+    od, Zd = impl.sketch_direct(K, V, Q, p)
+    sk = impl.MomentSketch(K.shape[1], V.shape[1], p).update(K, V, chunk=chunk)
+    om, Zm = sk.query(Q)
+    return max(relmax(Zm, Zd), absmax(om, od))
+
+
+# P3: a stream of identical keys ---------------------------------------------------
+
+def pin_identical_keys(impl, p, n=50, d=5, dv=3, seed=3):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal(d) * 0.4
+    K = np.tile(k, (n, 1))
+    V = rng.standard_normal((n, dv))
+    Q = rng.standard_normal((6, d)) * 0.4
+    coef = taylor_coeffs(p)
+    s = Q @ k
+    z_closed = n * np.array([sum(c * x ** j for j, c in enumerate(coef)) for x in s])
+    vbar = V.mean(axis=0)
+    od, Zd = impl.sketch_direct(K, V, Q, p)
+    om, Zm = impl.MomentSketch(d, dv, p).update(K, V).query(Q)
+    oe, Ze = impl.exact_attention(K, V, Q)
+    ze_closed = n * np.array([math.exp(x) for x in s])
+    return max(relmax(Zd, z_closed), relmax(Zm, z_closed), relmax(Ze, ze_closed),
+               absmax(od, np.tile(vbar, (6, 1))), absmax(om, np.tile(vbar, (6, 1))),
+               absmax(oe, np.tile(vbar, (6, 1))))
+
+
+# P4: q = 0 -------------------------------------------------------------------------
+
+def pin_zero_query(impl, p, n=40, d=4, dv=3, seed=4):
+    K, V, _ = _small(seed, n, 1, d, dv)
+    Q = np.zeros((2, d))
+    vbar = np.tile(V.mean(axis=0), (2, 1))
+    od, Zd = impl.sketch_direct(K, V, Q, p)
+    om, Zm = impl.MomentSketch(d, dv, p).update(K, V).query(Q)
+    oe, Ze = impl.exact_attention(K, V, Q)
+    return max(relmax(Zd, [n, n]), relmax(Zm, [n, n]), relmax(Ze, [n, n]),
+               absmax(od, vbar), absmax(om, vbar), absmax(oe, vbar))
+
+
+# P5: p = 0 and p = 1 closed forms (linear attention) -------------------------------
+
+def pin_low_orders(impl, n=30, d=4, dv=3, seed=5):
+    K, V, Q = _small(seed, n, 5, d, dv)
+    vbar = np.tile(V.mean(axis=0), (5, 1))
+    err = 0.0
+    od, Zd = impl.sketch_direct(K, V, Q, 0)
+    om, Zm = impl.MomentSketch(d, dv, 0).update(K, V).query(Q)
+    err = max(err, relmax(Zd, np.full(5, n)), relmax(Zm, np.full(5, n)),
+              absmax(od, vbar), absmax(om, vbar))
+    z1 = n + Q @ K.sum(axis=0)
+    n1 = (1.0 + Q @ K.T) @ V
+    od, Zd = impl.sketch_direct(K, V, Q, 1)
+    om, Zm = impl.MomentSketch(d, dv, 1).update(K, V).query(Q)
+    err = max(err, relmax(Zd, z1), relmax(Zm, z1),
+              absmax(od, n1 / z1[:, None]), absmax(om, n1 / z1[:, None]))
+    return err
+
+
+# P6: merge is exact -----------------------------------------------------------------
+
+def pin_merge(impl, p=3, d=3, dv=2, seed=6):
+    K, V, Q = _small(seed, 90, 7, d, dv)
+    a = impl.MomentSketch(d, dv, p).update(K[:40], V[:40])
+    b = impl.MomentSketch(d, dv, p).update(K[40:], V[40:])
+    whole = impl.MomentSketch(d, dv, p).update(K, V)
+    a.merge(b)
+    if a.count != whole.count or b.count != 50:
+        return math.inf
+    oa, Za = a.query(Q)
+    ow, Zw = whole.query(Q)
+    return max(absmax(a.canonical_state(), whole.canonical_state()),
+               relmax(Za, Zw), absmax(oa, ow))
+
+
+# P7: convergence to exp as p grows --------------------------------------------------
+
+def pin_convergence(impl, seed=7):
+    """Returns (max error at p=20 via the direct route, max error at p=8 via moments,
+    number of increases of the error as p goes 0..14)."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((200, 2))
+    K = g / np.linalg.norm(g, axis=1, keepdims=True)
+    V = rng.uniform(-1, 1, (200, 2))
+    g = rng.standard_normal((9, 2))
+    Q = g / np.linalg.norm(g, axis=1, keepdims=True)
+    oe, Ze = impl.exact_attention(K, V, Q)
+    errs = []
+    for p in range(0, 21):
+        _, Zd = impl.sketch_direct(K, V, Q, p)
+        errs.append(relmax(Zd, Ze))
+    rises = sum(1 for a, b in zip(errs[:14], errs[1:15]) if b > a)
+    _, Zm = impl.MomentSketch(2, 2, 8).update(K, V).query(Q)
+    bound8 = 1.0 ** 9 / math.factorial(9) * math.exp(2.0)
+    return errs[20], max(0.0, relmax(Zm, Ze) - bound8), rises
+
+
+# P11: affine maps of the values -----------------------------------------------------
+
+def pin_affine_values(impl, p=3, seed=11):
+    K, V, Q = _small(seed, 60, 5, 3, 2)
+    alpha, beta = -1.75, 0.625
+    od, _ = impl.sketch_direct(K, V, Q, p)
+    od2, _ = impl.sketch_direct(K, alpha * V + beta, Q, p)
+    om, _ = impl.MomentSketch(3, 2, p).update(K, V).query(Q)
+    om2, _ = impl.MomentSketch(3, 2, p).update(K, alpha * V + beta).query(Q)
+    oe, _ = impl.exact_attention(K, V, Q)
+    oe2, _ = impl.exact_attention(K, alpha * V + beta, Q)
+    return max(absmax(od2, alpha * od + beta), absmax(om2, alpha * om + beta),
+               absmax(oe2, alpha * oe + beta))
+
+
+# P12: textbook softmax attention -----------------------------------------------------
+
+def pin_textbook_attention(impl, seed=12):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((300, 6)) * 1.3
+    V = rng.standard_normal((300, 4))
+    Q = rng.standard_normal((11, 6)) * 1.3
+    S = Q @ K.T
+    o_ref = scipy.special.softmax(S, axis=1) @ V
+    z_ref = np.exp(scipy.special.logsumexp(S, axis=1))
+    oe, Ze = impl.exact_attention(K, V, Q, max_block_entries=900)  # several blocks
+    return max(relmax(Ze, z_ref), absmax(oe, o_ref))
+
+
+# P14: exact path by plain Python sums -----------------------------------------------
+
+def pin_exact_python(impl, seed=14):
+    rng = np.random.default_rng(seed)
+    n, d, dv = 17, 3, 2
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, dv))
+    Q = rng.standard_normal((3, d))
+    Zr, Or = [], []
+    for q in Q:
+        e = [math.exp(math.fsum(q[a] * K[i, a] for a in range(d))) for i in range(n)]
+        z = math.fsum(e)
+        Zr.append(z)
+        Or.append([math.fsum(e[i] * V[i, c] for i in range(n)) / z for c in range(dv)])
+    oe, Ze = impl.exact_attention(K, V, Q)
+    return max(relmax(Ze, Zr), absmax(oe, Or))
+
+
+# hand-worked examples (tests/golden/hand_worked.json) -------------------------------
+
+def pin_hand_worked(impl):
+    with open(os.path.join(GOLDEN, "hand_worked.json")) as f:
+        data = json.load(f)
+    err = 0.0
+    for ex in data["examples"]:
+        K = np.array(ex["K"])
+        V = np.array(ex["V"])
+        Q = np.array(ex["Q"])
+        p = ex["p"]
+        zhat = ex["zhat"][0] / ex["zhat"][1]
+        ohat = np.array([[a / b for a, b in ex["ohat"]]])
+        od, Zd = impl.sketch_direct(K, V, Q, p)
+        sk = impl.MomentSketch(ex["d"], ex["dv"], p).update(K, V)
+        om, Zm = sk.query(Q)
+        e = [math.exp(x) for x in ex["exact_exponents"]]
+        z = math.fsum(e)
+        o = np.array([[math.fsum(ei * V[i, c] for i, ei in enumerate(e)) / z
+                       for c in range(V.shape[1])]])
+        oe, Ze = impl.exact_attention(K, V, Q)
+        err = max(err, relmax(Zd, [zhat]), relmax(Zm, [zhat]), absmax(od, ohat),
+                  absmax(om, ohat), relmax(Ze, [z]), absmax(oe, o))
+        if "canonical_state" in ex:
+            err = max(err, absmax(sk.canonical_state(), np.array(ex["canonical_state"])))
+    return err
+
+
+# taylor_exp against the incomplete gamma identity -----------------------------------
+
+def pin_taylor_gamma(impl):
+    """For x >= 0: T_p(x) = e^x * Q(p+1, x) (regularised upper incomplete gamma);
+    for x < 0 the Taylor coefficients from mpmath."""
+    err = 0.0
+    xs = np.linspace(0.0, 6.0, 61)
+    for p in range(0, 12):
+        ref = np.exp(xs) * scipy.special.gammaincc(p + 1, xs)
+        err = max(err, relmax(impl.taylor_exp(xs, p), ref))
+        coef = taylor_coeffs(p)
+        xn = np.linspace(-3.0, -0.05, 30)
+        refn = np.array([math.fsum(c * x ** j for j, c in enumerate(coef)) for x in xn])
+        err = max(err, absmax(impl.taylor_exp(xn, p), refn) / max(1.0, np.abs(refn).max()))
+    return err

@@ -1,0 +1,153 @@
+"""Plant plausible mistakes in copies of the oracle and check a pin catches each.
+
+Every mutant is a small subclass or wrapper built here, on the CPU; the oracle
+package itself is never modified.  A mutant "survives" if every pin it is run
+against stays at rounding level; the test fails in that case.
+"""
+
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sketch as osk
+from tests import oracle_pins as pins
+
+
+def _impl(**over):
+    base = dict(exact_attention=oracle.exact_attention,
+                sketch_direct=oracle.sketch_direct,
+                MomentSketch=oracle.MomentSketch,
+                taylor_exp=oracle.taylor_exp)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+class NoFactorial(oracle.MomentSketch):
+    """Drops the 1/j! weights at query time."""
+
+    def query(self, Q):
+        Q = np.asarray(Q, dtype=np.float64)
+        Z = np.zeros(Q.shape[0])
+        Nt = np.zeros((Q.shape[0], self.dv))
+        for j, F in enumerate(osk.feature_map(Q, self.p)):
+            Z += F @ self.M[j]
+            Nt += F @ self.N[j]
+        return Nt / Z[:, None], Z
+
+
+class DroppedTopLevel(oracle.MomentSketch):
+    """Forgets the degree-p level when answering."""
+
+    def query(self, Q):
+        Q = np.asarray(Q, dtype=np.float64)
+        Z = np.zeros(Q.shape[0])
+        Nt = np.zeros((Q.shape[0], self.dv))
+        for j, F in enumerate(osk.feature_map(Q, self.p)[:-1]):
+            Z += (F @ self.M[j]) / math.factorial(j)
+            Nt += (F @ self.N[j]) / math.factorial(j)
+        return Nt / Z[:, None], Z
+
+
+class SwappedColumns(oracle.MomentSketch):
+    """Stores the value moment of the first value coordinate in the M column."""
+
+    def canonical_state(self):
+        S = super().canonical_state()
+        return S[:, [1, 0] + list(range(2, S.shape[1]))]
+
+
+class SubtractMerge(oracle.MomentSketch):
+    def merge(self, other):
+        for j in range(self.p + 1):
+            self.M[j] -= other.M[j]
+            self.N[j] -= other.N[j]
+        self.count += other.count
+        return self
+
+
+class LastChunkOnly(oracle.MomentSketch):
+    """Overwrites instead of accumulating across chunks."""
+
+    def update(self, K, V, chunk=256):
+        K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64)
+        for c0 in range(0, K.shape[0], chunk):
+            for j, F in enumerate(osk.feature_map(K[c0:c0 + chunk], self.p)):
+                self.M[j] = F.sum(axis=0)
+                self.N[j] = F.T @ V[c0:c0 + chunk]
+        self.count += K.shape[0]
+        return self
+
+
+def taylor_off_by_one(x, p):
+    """Sums only up to degree p - 1."""
+    return oracle.taylor_exp(x, max(p - 1, 0)) if p > 0 else oracle.taylor_exp(x, 0) * 0 + 1
+
+
+def direct_off_by_one(K, V, Q, p, max_block_entries=1 << 24):
+    return oracle.sketch_direct(K, V, Q, max(p - 1, 0) if p else 0, max_block_entries)
+
+
+def direct_no_constant(K, V, Q, p, max_block_entries=1 << 24):
+    """Leaves out the j = 0 term."""
+    o, Z = oracle.sketch_direct(K, V, Q, p, max_block_entries)
+    n = np.asarray(K).shape[0]
+    Nt = o * Z[:, None] - np.asarray(V, np.float64).sum(axis=0)[None, :]
+    Z = Z - n
+    return Nt / Z[:, None], Z
+
+
+def exact_wrong_sign(K, V, Q, max_block_entries=1 << 24):
+    return oracle.exact_attention(K, V, -np.asarray(Q), max_block_entries)
+
+
+def exact_transposed_values(K, V, Q, max_block_entries=1 << 24):
+    """Uses the reversed key order for the values (a transposed/misindexed operand)."""
+    return oracle.exact_attention(K, np.asarray(V)[::-1], Q, max_block_entries)
+
+
+def exact_missing_shift(K, V, Q, max_block_entries=1 << 24):
+    """Forgets to scale Z back by e^mu."""
+    o, Z = oracle.exact_attention(K, V, Q, max_block_entries)
+    S = np.asarray(Q, np.float64) @ np.asarray(K, np.float64).T
+    return o, Z / np.exp(S.max(axis=1))
+
+
+def _all_pins(impl):
+    errs = [pins.pin_bruteforce(impl, 3, 3), pins.pin_bruteforce(impl, 2, 4),
+            pins.pin_identical_keys(impl, 3), pins.pin_zero_query(impl, 3),
+            pins.pin_low_orders(impl), pins.pin_merge(impl),
+            pins.pin_affine_values(impl), pins.pin_textbook_attention(impl),
+            pins.pin_exact_python(impl), pins.pin_hand_worked(impl),
+            pins.pin_taylor_gamma(impl)]
+    e20, excess8, rises = pins.pin_convergence(impl)
+    errs += [e20 * 1e-2, excess8, float(rises)]
+    return max(errs)
+
+
+MUTANTS = {
+    "no_factorial": _impl(MomentSketch=NoFactorial),
+    "dropped_top_level": _impl(MomentSketch=DroppedTopLevel),
+    "swapped_state_columns": _impl(MomentSketch=SwappedColumns),
+    "subtract_merge": _impl(MomentSketch=SubtractMerge),
+    "last_chunk_only": _impl(MomentSketch=LastChunkOnly),
+    "taylor_off_by_one": _impl(taylor_exp=taylor_off_by_one),
+    "direct_off_by_one": _impl(sketch_direct=direct_off_by_one),
+    "direct_no_constant": _impl(sketch_direct=direct_no_constant),
+    "exact_wrong_sign": _impl(exact_attention=exact_wrong_sign),
+    "exact_transposed_values": _impl(exact_attention=exact_transposed_values),
+    "exact_missing_shift": _impl(exact_attention=exact_missing_shift),
+}
+
+
+def test_unmutated_passes_all_pins():
+    assert _all_pins(_impl()) < 1e-12
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    with np.errstate(all="ignore"):
+        assert _all_pins(MUTANTS[name]) > 1e-6, f"mutant {name} survived every pin"
