@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the polynomial-sketch hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input of the workload:
+reset, ingest every key through sketch_update in the workload's chunks (and the
+sub-stream merges), answer all m queries with sketch_query, and run exact_attend
+for the same queries (the exact path that measures the sketch's error).
+
+Printed: one JSON line.  ``value`` = (keys ingested + queries answered) per
+second of the whole step; the line also carries the per-phase rates, the
+roofline of the dominant kernel (the moment update, fp32 MFMA) and the float64
+oracle timed on a bounded sample on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "sketch keys/s + queries/s (MFMA % of peak); exact-path HBM GB/s"
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="workload id 1..5 (default 2: d=16, p=4, 64K keys)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, K, V, Q, budget):
+    """The float64 oracle as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    K0, V0, Q0 = K[0], V[0], Q[0]
+    # keys: the moment route on a prefix, grown until a third of the budget is used
+    nk, t_u = 256, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.MomentSketch(w.d, w.dv, w.p).update(K0[:nk], V0[:nk], chunk=64)
+        t_u = time.perf_counter() - t0
+        if t_u > budget / 3 or nk >= w.n:
+            break
+        nk = min(w.n, nk * 2)
+    sk = oracle.MomentSketch(w.d, w.dv, w.p).update(K0[:256], V0[:256], chunk=64)
+    mq = min(w.m, 64)
+    t0 = time.perf_counter()
+    sk.query(Q0[:mq])
+    t_q = time.perf_counter() - t0
+    me = min(w.m, 32)
+    t0 = time.perf_counter()
+    oracle.exact_attention(K0, V0, Q0[:me])
+    t_e = time.perf_counter() - t0
+    per_key, per_q, per_eq = t_u / nk, t_q / mq, t_e / me
+    t_full = w.h * (w.n * per_key + w.m * (per_q + per_eq))
+    return {
+        "value": w.h * (w.n + w.m) / t_full,
+        "unit": "keys+queries/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0: moment-route update of {nk} keys ({t_u:.1f} s), "
+                   f"moment-route query of {mq} queries ({t_q:.2f} s), exact path for "
+                   f"{me} queries over all {w.n} keys ({t_e:.2f} s); projected to the "
+                   f"whole step of {w.h} head(s)"),
+        "keys_per_s": 1.0 / per_key,
+        "queries_per_s": 1.0 / per_q,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sketch shards by sub-stream with one sum all-reduce; see the design "
+              "notes)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import exp_density_sketching_amd as E
+    from exp_density_sketching_amd.workload import ingest
+    from synthetic import CONFIGS, generate
+
+    w = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    K, V, Q = generate(w)
+    Kg = torch.from_numpy(K).cuda()
+    Vg = torch.from_numpy(V).cuda()
+    Qg = torch.from_numpy(Q).cuda()
+    out_s = torch.empty((w.h, w.m, w.dv), device="cuda")
+    z_s = torch.empty((w.h, w.m), device="cuda")
+    out_e = torch.empty_like(out_s)
+    z_e = torch.empty_like(z_s)
+    S = max(1, w.substreams)
+    sketches = [E.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    n_calls = sum(-(-(w.n * (i + 1) // S - w.n * i // S) // (w.chunk or w.n))
+                  for i in range(S))
+
+    def step(rec):
+        for sk in sketches:
+            E.sketch_reset(sk)
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record()
+        ingest(w, Kg, Vg, sketches)
+        e1.record()
+        E.sketch_query(sketches[0], Qg, out_s, z_s)
+        e2.record()
+        E.exact_attend(Kg, Vg, Qg, out_e, z_e)
+        e3.record()
+        rec.append((e0, e1, e2, e3))
+
+    warm = []
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_upd = np.mean([a.elapsed_time(b) for a, b, _, _ in rec]) / 1e3
+    t_qry = np.mean([b.elapsed_time(c) for _, b, c, _ in rec]) / 1e3
+    t_ex = np.mean([c.elapsed_time(d) for _, _, c, d in rec]) / 1e3
+    t_step = wall / args.steps
+
+    # dominant kernel: the moment update, timed per call on its stream
+    sk = sketches[0]
+    E.sketch_reset(sk)
+    chunk = w.chunk or w.n
+    per_call = []
+    for c0 in range(0, w.n, chunk):
+        a, b = ev(), ev()
+        a.record()
+        E.sketch_update(sk, Kg[:, c0:c0 + chunk], Vg[:, c0:c0 + chunk])
+        b.record()
+        per_call.append((a, b, min(chunk, w.n - c0)))
+    torch.cuda.synchronize()
+    dur = np.mean([a.elapsed_time(b) for a, b, _ in per_call]) / 1e3
+    keys_per_call = np.mean([k for _, _, k in per_call])
+    flop_per_key = 2.0 * w.D * (1 + w.dv)
+    achieved = flop_per_key * keys_per_call * w.h / dur
+
+    # exact path in decode mode (one query per head), streaming the whole KV
+    dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
+    dec_z = torch.empty((w.h, 1), device="cuda")
+    q1 = Qg[:, :1].contiguous()
+    for _ in range(2):
+        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(args.decode_steps):
+        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
+    b.record()
+    torch.cuda.synchronize()
+    t_dec = a.elapsed_time(b) / 1e3 / args.decode_steps
+    kv_bytes = 4.0 * w.h * w.n * (w.d + w.dv)
+
+    line = {
+        "metric": METRIC,
+        "value": w.h * (w.n + w.m) / t_step,
+        "unit": "keys+queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "d": w.d, "dv": w.dv, "p": w.p, "D": w.D,
+                   "n": w.n, "m": w.m, "heads": w.h, "chunk": w.chunk,
+                   "substreams": w.substreams, "update_calls": n_calls},
+        "keys_per_s": w.h * w.n / t_upd,
+        "queries_per_s": w.h * w.m / t_qry,
+        "update_ms": t_upd * 1e3,
+        "query_ms": t_qry * 1e3,
+        "exact_ms": t_ex * 1e3,
+        "query_mfma_frac": flop_per_key * w.h * w.m / t_qry / PEAK_FP32_MFMA,
+        "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
+                         "kv_bytes": kv_bytes,
+                         "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
+        "roofline": {"kernel": "sk_update_kernel (+ split reduce)", "bound": "mfma",
+                     "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
+                     "traffic": None,
+                     "flop_per_launch": flop_per_key * keys_per_call * w.h,
+                     "launch_us": dur * 1e6},
+    }
+    for s_ in sketches:
+        s_.destroy()
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, K, V, Q, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,17 @@
+"""MI355X-native polynomial-method streaming sketch of the exp kernel, with the
+exact streaming attention path beside it.
+
+The compute lives in hand-written HIP kernels for gfx950 behind a C ABI
+(include/expsketch.h, built into libexpsketch.so); this package is the thin
+Python binding with the same call names.  Source of the method: "Rumo a Limites
+Estritos para Atenção em Streaming" (gist.science, pt), sections "Definição do
+Problema" and "Metodologia" (pillar "O Método Polinomial", Merge-and-Reduce).
+"""
+
+from ._binding import (LIB_PATH, EXPORTED, Sketch, SketchError, sketch_create,
+                       sketch_destroy, sketch_reset, sketch_update, sketch_merge,
+                       sketch_query, sketch_export, sketch_state, exact_attend, raw)
+
+__all__ = ["LIB_PATH", "EXPORTED", "Sketch", "SketchError", "sketch_create",
+           "sketch_destroy", "sketch_reset", "sketch_update", "sketch_merge",
+           "sketch_query", "sketch_export", "sketch_state", "exact_attend", "raw"]

@@ -1,0 +1,224 @@
+"""ctypes binding of libexpsketch.so: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+include/expsketch.h.  PyTorch supplies device memory (CUDA/HIP tensors) and the
+current stream.  There is no CPU path: if the library is not built, loading it
+raises immediately.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libexpsketch.so")
+
+SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
+
+EXPORTED = ("sketch_create", "sketch_destroy", "sketch_set_stream", "sketch_reset",
+            "sketch_update", "sketch_merge", "sketch_query", "exact_attend",
+            "sketch_state", "sketch_export", "sketch_info", "sk_strerror", "sk_version")
+
+
+class SketchError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        msg = _lib().sk_strerror(code).decode() if _LIB is not None else str(code)
+        super().__init__(f"{where}: {msg} (status {code})")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m exp_density_sketching_amd.build` (there is no CPU fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        c_int, c_i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        sig = {
+            "sketch_create": (c_int, [c_int, c_int, c_int, c_int, vp, ctypes.POINTER(vp)]),
+            "sketch_destroy": (c_int, [vp]),
+            "sketch_set_stream": (c_int, [vp, vp]),
+            "sketch_reset": (c_int, [vp]),
+            "sketch_update": (c_int, [vp, vp, vp, c_i64]),
+            "sketch_merge": (c_int, [vp, vp]),
+            "sketch_query": (c_int, [vp, vp, c_i64, vp, vp]),
+            "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
+                                     vp, vp]),
+            "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
+            "sketch_export": (c_int, [vp, vp]),
+            "sketch_info": (c_int, [vp, ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                    ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                    ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
+            "sk_strerror": (ctypes.c_char_p, [c_int]),
+            "sk_version": (c_int, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(code, where):
+    if code != SK_OK:
+        raise SketchError(code, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dims):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous float32")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _heads(t, name):
+    """Accept [n, x] (one head) or [h, n, x]; return the 3-d view."""
+    if t.dim() == 2:
+        return t.unsqueeze(0)
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [n, x] or [h, n, x]")
+    return t
+
+
+class Sketch:
+    """A handle of the C library (sketch_create ... sketch_destroy)."""
+
+    def __init__(self, d, dv, p, h=1):
+        lib = _lib()
+        handle = ctypes.c_void_p()
+        _check(lib.sketch_create(d, dv, p, h, _stream(), ctypes.byref(handle)),
+               "sketch_create")
+        self._h = handle
+        self.d, self.dv, self.p, self.h = d, dv, p, h
+
+    def _handle(self):
+        if self._h is None:
+            raise RuntimeError("sketch destroyed")
+        _check(_lib().sketch_set_stream(self._h, _stream()), "sketch_set_stream")
+        return self._h
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            h, self._h = self._h, None
+            _check(_lib().sketch_destroy(h), "sketch_destroy")
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    @property
+    def D(self):
+        return sum(self.d ** j for j in range(self.p + 1))
+
+    @property
+    def count(self):
+        c = ctypes.c_int64()
+        _check(_lib().sketch_info(self._h, None, None, None, None, None, ctypes.byref(c)),
+               "sketch_info")
+        return c.value
+
+
+def sketch_create(d, dv, p, h=1):
+    return Sketch(d, dv, p, h)
+
+
+def sketch_destroy(s):
+    s.destroy()
+
+
+def sketch_reset(s):
+    _check(_lib().sketch_reset(s._handle()), "sketch_reset")
+
+
+def sketch_update(s, K, V):
+    """K [h, n, d] (or [n, d]), V [h, n, dv] (or [n, dv]) float32 GPU tensors."""
+    K, V = _heads(K, "K"), _heads(V, "V")
+    if K.shape[0] != s.h or V.shape[0] != s.h or K.shape[2] != s.d or V.shape[2] != s.dv \
+            or K.shape[1] != V.shape[1]:
+        raise ValueError(f"shape mismatch: K {tuple(K.shape)}, V {tuple(V.shape)} for "
+                         f"h={s.h}, d={s.d}, dv={s.dv}")
+    n = K.shape[1]
+    _check(_lib().sketch_update(s._handle(), _dev(K, "K", 3), _dev(V, "V", 3), n),
+           "sketch_update")
+
+
+def sketch_merge(dst, src):
+    _check(_lib().sketch_merge(dst._handle(), src._h), "sketch_merge")
+
+
+def sketch_query(s, Q, out=None, Z=None):
+    """Q [h, m, d] (or [m, d]) -> (out [h, m, dv], Z [h, m]) float32 GPU tensors."""
+    squeeze = Q.dim() == 2
+    Q = _heads(Q, "Q")
+    if Q.shape[0] != s.h or Q.shape[2] != s.d:
+        raise ValueError(f"Q {tuple(Q.shape)} does not match h={s.h}, d={s.d}")
+    m = Q.shape[1]
+    if out is None:
+        out = torch.empty((s.h, m, s.dv), dtype=torch.float32, device=Q.device)
+    if Z is None:
+        Z = torch.empty((s.h, m), dtype=torch.float32, device=Q.device)
+    _check(_lib().sketch_query(s._handle(), _dev(Q, "Q", 3), m, _dev(out, "out", 3),
+                               _dev(Z, "Z", 2)), "sketch_query")
+    return (out[0], Z[0]) if squeeze else (out, Z)
+
+
+def sketch_export(s, dst=None, device=None):
+    """Canonical [M | N] view into a new (or given) tensor [h, D, 1 + dv]."""
+    if dst is None:
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        dst = torch.empty((s.h, s.D, 1 + s.dv), dtype=torch.float32, device=dev)
+    _check(_lib().sketch_export(s._handle(), _dev(dst, "dst", 3)), "sketch_export")
+    return dst
+
+
+def sketch_state(s):
+    """(device pointer, D, cols, count) of the library-owned canonical view."""
+    ptr = ctypes.c_void_p()
+    D = ctypes.c_int64()
+    cols = ctypes.c_int()
+    cnt = ctypes.c_int64()
+    _check(_lib().sketch_state(s._handle(), ctypes.byref(ptr), ctypes.byref(D),
+                               ctypes.byref(cols), ctypes.byref(cnt)), "sketch_state")
+    return ptr.value, D.value, cols.value, cnt.value
+
+
+def exact_attend(K, V, Q, out=None, Z=None):
+    """Exact KDE normaliser and softmax attention: K [h,n,d], V [h,n,dv], Q [h,m,d]."""
+    squeeze = Q.dim() == 2
+    K, V, Q = _heads(K, "K"), _heads(V, "V"), _heads(Q, "Q")
+    h, n, d = K.shape
+    dv = V.shape[2]
+    m = Q.shape[1]
+    if V.shape[:2] != (h, n) or Q.shape[0] != h or Q.shape[2] != d:
+        raise ValueError(f"shape mismatch: K {tuple(K.shape)}, V {tuple(V.shape)}, "
+                         f"Q {tuple(Q.shape)}")
+    if out is None:
+        out = torch.empty((h, m, dv), dtype=torch.float32, device=Q.device)
+    if Z is None:
+        Z = torch.empty((h, m), dtype=torch.float32, device=Q.device)
+    _check(_lib().exact_attend(_dev(K, "K", 3), _dev(V, "V", 3), n, d, dv, h,
+                               _dev(Q, "Q", 3), m, _dev(out, "out", 3), _dev(Z, "Z", 2),
+                               _stream()), "exact_attend")
+    return (out[0], Z[0]) if squeeze else (out, Z)
+
+
+def raw():
+    """The loaded ctypes library (for tests of the C ABI itself)."""
+    return _lib()

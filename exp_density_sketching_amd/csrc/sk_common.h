@@ -1,0 +1,51 @@
+// Common device-side definitions for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4v __attribute__((ext_vector_type(4)));
+
+#define SK_WG 256          // threads per workgroup in every GEMM-shaped kernel
+#define SK_KB 32           // keys (update) or feature rows (query) per LDS stage
+#define SK_PAD 32          // LDS row padding: lanes 32..63 land on other banks
+#define SK_MAXDIG 8        // max Kronecker digits on either side of a level split
+
+// v_mfma_f32_32x32x2_f32: D(32x32) += A(32x2) * B(2x32), fp32 in and out.
+// Lane l supplies A[l%32][l/32] and B[l/32][l%32]; accumulator register r of
+// lane l holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ floatx16 mfma32x32x2(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// Tile descriptor of the moment update: one (level, row tile, column tile) of the
+// level's GEMM  X_j[a_hi][(a_lo, e)] += sum_keys L[a_hi](k) * R[(a_lo, e)](k, v)
+// with L = k^(x)s (s leading digits) and R = k^(x)t (x) u, u = [k, v] below the
+// top level and u = v at the top level.
+struct UpdTile {
+  long long xoff;   // float offset of level j inside one head's state
+  int level;
+  int s, t;         // digits on the row side and on the column side (s + t = j)
+  int C;            // the level's row width (d + dv, or dv at the top)
+  int top;          // 1 at j == p
+  int M, N;         // GEMM rows (d^s) and columns (d^t * C)
+  int row0, col0;   // tile origin inside the level GEMM
+  int wc;           // waves along the column side: 1, 2 or 4 (tile 256/wc x 64*wc)
+  int pad_;
+};
+
+// Tile descriptor of the query GEMM  Y[q][e] = sum_a Psi_j[q][a] X_j[a][e]
+// over a range of feature rows a of level j and 32 columns e.
+struct QryTile {
+  long long xoff;   // float offset of level j inside one head's state
+  long long a0, a1; // feature-row range [a0, a1) of level j
+  int level;
+  int C;            // row width of the level
+  int top;
+  int e0;           // first column of the 32-column slice
+};

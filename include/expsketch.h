@@ -1,0 +1,156 @@
+/*
+ * expsketch.h -- C ABI of the polynomial-method streaming sketch of the exp kernel
+ * and of the exact streaming attention path, for AMD Instinct MI355X (gfx950).
+ *
+ * The method: "Rumo a Limites Estritos para Atenção em Streaming" (gist.science,
+ * pt) and its French twin "Vers des Bornes Serrées pour l'Attention en Flux".
+ *   - "Definição do Problema": a stream of key/value pairs (k_i, v_i) arrives in
+ *     order; a query q asks for the kernel-density normaliser and the attention
+ *     vector over everything seen so far.  Kernel: exp<q, k> (temperature is set
+ *     by the radius of keys and queries, so no 1/sqrt(d) factor).
+ *   - "Metodologia", pillar "O Método Polinomial": the head of the kernel is a
+ *     truncated Taylor expansion; the stream is summarised by its low-degree
+ *     moments.  Reading used here, for degree p:
+ *         M_j = sum_i k_i^(x)j,   N_j = sum_i k_i^(x)j v_i^T        (j = 0..p)
+ *         Zhat(q) = sum_j <q^(x)j, M_j> / j!
+ *         ohat(q) = (sum_j <q^(x)j, N_j> / j!) / Zhat(q)
+ *     which equals sum_i T_p(<q,k_i>) [1, v_i] / ... with T_p(x) = sum_{j<=p} x^j/j!.
+ *   - "Metodologia", closing paragraph (Merge-and-Reduce): sketches of
+ *     sub-streams are merged; moments are sums, so a merge is an addition.
+ *
+ * Conventions for every call below
+ *   - All float arrays are fp32, row-major, contiguous, 16-byte aligned DEVICE
+ *     pointers (hipMalloc / torch CUDA tensors), owned by the caller.
+ *   - h independent heads are laid out head-major: K [h][n][d], V [h][n][dv],
+ *     Q [h][m][d], out [h][m][dv], Z [h][m].
+ *   - Supported shapes: d and dv are powers of two in [4, 128]; 0 <= p <= 16;
+ *     h >= 1; the state (about h * D * (1+dv) floats, D = sum_{j<=p} d^j) must fit
+ *     in device memory.  Anything else returns SK_EINVAL (shape) or SK_ENOMEM.
+ *   - Calls are asynchronous on the HIP stream they are given (the handle's
+ *     stream for sketch_* calls); nothing synchronises except sketch_destroy and
+ *     sketch_state.  A kernel fault surfaces as SK_EHIP from a later call.
+ *   - A handle is not thread-safe; use one thread (or external locking) per handle.
+ *   - Results are deterministic: every reduction runs in a fixed order.
+ */
+#ifndef EXPSKETCH_H
+#define EXPSKETCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued call. */
+#define SK_OK         0
+#define SK_EINVAL    -1  /* bad argument: shape, null or misaligned pointer, n < 0 */
+#define SK_ENOMEM    -2  /* device memory for the state or a workspace not available */
+#define SK_EMISMATCH -3  /* merge of sketches with different (d, dv, p, h) */
+#define SK_EHIP      -4  /* a HIP runtime call or kernel launch failed */
+
+typedef struct sk_sketch* sk_handle;  /* opaque; owned by the library */
+
+/*
+ * sketch_create -- an empty sketch of degree p for h heads of key dimension d and
+ * value dimension dv ("O Método Polinomial": the moment summary).
+ *   hip_stream: hipStream_t the handle's calls are issued on (NULL = default).
+ *   out: receives the handle.  The library allocates the state (zeroed) with
+ *        hipMalloc; sketch_destroy frees it.
+ * Errors: SK_EINVAL for unsupported shapes or out == NULL; SK_ENOMEM if the state
+ * does not fit; SK_EHIP if a HIP call fails.  On error *out is set to NULL.
+ */
+int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out);
+
+/* sketch_destroy -- synchronises the handle's stream, frees everything the
+ * handle owns.  NULL is accepted (no-op).  Returns SK_EHIP if a pending kernel
+ * had failed (the memory is still freed). */
+int sketch_destroy(sk_handle s);
+
+/* sketch_set_stream -- issue later calls of this handle on another stream.  The
+ * caller orders the two streams if work is still pending on the old one. */
+int sketch_set_stream(sk_handle s, void* hip_stream);
+
+/* sketch_reset -- back to the empty sketch (all moments zero, count 0). */
+int sketch_reset(sk_handle s);
+
+/*
+ * sketch_update -- ingest n more key/value pairs per head ("Definição do
+ * Problema": the stream; "O Método Polinomial": M_j += sum k^(x)j,
+ * N_j += sum k^(x)j v^T for j = 0..p).
+ *   K: device [h][n][d]; V: device [h][n][dv]; n >= 0 keys per head (n == 0: no-op).
+ * The inputs may be reused or freed once the stream has passed the call.
+ * Errors: SK_EINVAL (NULL/misaligned pointer with n > 0, n < 0), SK_ENOMEM
+ * (split workspace), SK_EHIP.
+ */
+int sketch_update(sk_handle s, const float* K, const float* V, int64_t n);
+
+/*
+ * sketch_merge -- dst += src (Merge-and-Reduce, merge step: moments add, counts
+ * add).  src is unchanged.  Both handles must have equal (d, dv, p, h); the work
+ * runs on dst's stream (the caller orders src's stream before it).
+ * Errors: SK_EINVAL (NULL, dst == src), SK_EMISMATCH, SK_EHIP.
+ */
+int sketch_merge(sk_handle dst, sk_handle src);
+
+/*
+ * sketch_query -- answer m queries per head from the moments:
+ *   Z[h][q]     = Zhat(q) = sum_j <q^(x)j, M_j> / j!      (KDE normaliser estimate)
+ *   out[h][q][:] = ohat(q) = (sum_j <q^(x)j, N_j> / j!) / Zhat(q)
+ * ("O Método Polinomial", query of the truncated expansion).  No clamping: an
+ * empty sketch gives Z = 0 and out = NaN (0/0), as IEEE division does.
+ *   Q: device [h][m][d]; out: device [h][m][dv]; Z: device [h][m]; m >= 0.
+ * Errors: SK_EINVAL, SK_ENOMEM (partials workspace), SK_EHIP.
+ */
+int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z);
+
+/*
+ * exact_attend -- the exact streaming path ("Definição do Problema": keep every
+ * pair):  Z[h][q] = sum_i exp(<q, k_i>),  out[h][q] = sum_i exp(<q,k_i>) v_i / Z.
+ * Computed with a running maximum (online softmax) over key slices and a
+ * fixed-order combine of the slices.  n == 0 gives Z = 0, out = NaN.
+ *   K [h][n][d], V [h][n][dv], Q [h][m][d], out [h][m][dv], Z [h][m]: device.
+ *   hip_stream: hipStream_t to run on (NULL = default stream).
+ * Temporary partials are taken from the stream-ordered allocator
+ * (hipMallocAsync) and released on the same stream.
+ * Errors: SK_EINVAL (shapes, NULL/misaligned pointers, n or m < 0), SK_ENOMEM,
+ * SK_EHIP.
+ */
+int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
+                 const float* Q, int64_t m, float* out, float* Z, void* hip_stream);
+
+/*
+ * sketch_state -- a read-only view of the moments in the canonical layout
+ * [M | N]: per head an array [D][1 + dv], rows stacked by level j = 0..p, level j
+ * holding d^j rows in row-major Kronecker order (row a*d + b of level j is row a
+ * of level j-1 times k[b]); column 0 is M_j, columns 1..dv are N_j; row 0 column
+ * 0 is the count.  The view is materialised on the handle's stream into a
+ * library-owned device buffer [h][D][1+dv], then the stream is synchronised;
+ * it stays valid until the next call on the handle.  Any output pointer may be NULL.
+ * Errors: SK_EINVAL (NULL handle), SK_ENOMEM, SK_EHIP.
+ */
+int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* cols,
+                 int64_t* count);
+
+/*
+ * sketch_export -- the same canonical [M | N] view as sketch_state, written into
+ * caller-owned device memory dst [h][D][1 + dv] (fp32, 16-byte aligned),
+ * asynchronously on the handle's stream.
+ * Errors: SK_EINVAL (NULL handle or dst, misaligned dst), SK_EHIP.
+ */
+int sketch_export(sk_handle s, float* dst);
+
+/* sketch_info -- shape and count of a handle (host values; any pointer may be NULL). */
+int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D,
+                int64_t* count);
+
+/* sk_strerror -- a static string for a status code. */
+const char* sk_strerror(int code);
+
+/* sk_version -- ABI version of this library (major * 100 + minor). */
+int sk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXPSKETCH_H */

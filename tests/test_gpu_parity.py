@@ -1,0 +1,227 @@
+"""GPU parity through the C ABI against the float64 oracle (MI355X only).
+
+Small cases compare every output; they span several tiles and a ragged tail of
+keys, chunks and queries.  Full-size cases run each workload exactly as the
+benchmark does and compare sampled queries, which the oracle answers one by one
+over the whole stream.  Bars: sketch rel <= 2e-4 on Zhat and abs <= 2e-4 on ohat;
+exact rel <= 1e-5 on Z and abs <= 1e-5 on o.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exp_density_sketching_amd as E
+from exp_density_sketching_amd.workload import ingest, run_sketch
+from synthetic import CONFIGS, generate
+from tests.gpu_util import (SK_Z_REL, SK_O_ABS, EX_Z_REL, EX_O_ABS, gpu, host, zrel,
+                            oabs, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_sketch(w, K, V, Q, qidx=None, label=""):
+    Kg, Vg, Qg = gpu(K, V, Q)
+    out, Z, sk = run_sketch(w, Kg, Vg, Qg)
+    out, Z = host(out, Z)
+    worst_z, worst_o = 0.0, 0.0
+    for hd in range(w.h):
+        qi = np.arange(Q.shape[1]) if qidx is None else qidx
+        o_ref, z_ref = oracle.sketch_direct(K[hd], V[hd], Q[hd][qi], w.p)
+        worst_z = max(worst_z, zrel(Z[hd][qi], z_ref))
+        worst_o = max(worst_o, oabs(out[hd][qi], o_ref))
+    say(f"{label} sketch: max rel Zhat err {worst_z:.3e}, max abs ohat err {worst_o:.3e}")
+    assert worst_z <= SK_Z_REL
+    assert worst_o <= SK_O_ABS
+    sk.destroy()
+
+
+def _check_exact(w, K, V, Q, qidx=None, label=""):
+    Kg, Vg, Qg = gpu(K, V, Q)
+    out, Z = E.exact_attend(Kg, Vg, Qg)
+    out, Z = host(out, Z)
+    worst_z, worst_o = 0.0, 0.0
+    for hd in range(w.h):
+        qi = np.arange(Q.shape[1]) if qidx is None else qidx
+        o_ref, z_ref = oracle.exact_attention(K[hd], V[hd], Q[hd][qi])
+        worst_z = max(worst_z, zrel(Z[hd][qi], z_ref))
+        worst_o = max(worst_o, oabs(out[hd][qi], o_ref))
+    say(f"{label} exact: max rel Z err {worst_z:.3e}, max abs o err {worst_o:.3e}")
+    assert worst_z <= EX_Z_REL
+    assert worst_o <= EX_O_ABS
+
+
+# Small versions: every output compared.  Ragged n, chunk and m on purpose.
+SMALL = {
+    1: dict(n=4096, m=64),
+    "1r": dict(n=4097, m=65, chunk=1000),
+    2: dict(n=2 * 4096 + 37, m=200),
+    3: dict(n=8192 + 5, m=300),
+    4: dict(n=5000, m=70, h=3),
+    5: dict(n=3001, m=130),
+}
+
+
+def _small(key):
+    ident = key if isinstance(key, int) else int(str(key)[0])
+    return CONFIGS[ident].scaled(**SMALL[key])
+
+
+@pytest.mark.parametrize("key", list(SMALL))
+def test_sketch_small(key):
+    w = _small(key)
+    K, V, Q = generate(w)
+    _check_sketch(w, K, V, Q, label=f"small {key}")
+
+
+@pytest.mark.parametrize("key", list(SMALL))
+def test_exact_small(key):
+    w = _small(key)
+    K, V, Q = generate(w)
+    _check_exact(w, K, V, Q, label=f"small {key}")
+
+
+@pytest.mark.parametrize("ident,n,h", [(1, 999, 1), (2, 700, 1), (3, 600, 1), (4, 300, 2),
+                                       (5, 150, 1)])
+def test_state_matches_oracle_moments(ident, n, h):
+    """The exported [M | N] equals the oracle's moments entry by entry, within
+    fp32 rounding of the sum of absolute terms (oracle run on |K|, |V|)."""
+    w = CONFIGS[ident].scaled(n=n, m=1, h=h, chunk=256 if ident in (2, 3) else 0,
+                              substreams=2 if ident == 3 else 1)
+    K, V, Q = generate(w)
+    Kg, Vg = gpu(K, V)
+    sk, _ = ingest(w, Kg, Vg)
+    S = host(E.sketch_export(sk))[0]
+    for hd in range(h):
+        ref = oracle.MomentSketch(w.d, w.dv, w.p).update(K[hd], V[hd]).canonical_state()
+        mag = oracle.MomentSketch(w.d, w.dv, w.p).update(
+            np.abs(K[hd].astype(np.float64)), np.abs(V[hd].astype(np.float64))).canonical_state()
+        err = np.abs(S[hd] - ref)
+        assert S[hd].shape == ref.shape
+        assert np.all(err <= 2e-6 * mag + 1e-30), float((err / (mag + 1e-30)).max())
+    ptr, D, cols, cnt = E.sketch_state(sk)
+    assert ptr and D == w.D and cols == 1 + w.dv and cnt == n
+
+
+@pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
+                                    (128, 128, 1), (4, 4, 7), (32, 8, 2)])
+def test_other_shapes(d, dv, p):
+    w = CONFIGS[1].scaled(n=1537, m=129)
+    w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
+    K, V, Q = generate(w)
+    _check_sketch(w, K, V, Q, label=f"d={d} dv={dv} p={p}")
+    _check_exact(w, K, V, Q, label=f"d={d} dv={dv} p={p}")
+
+
+def test_decode_mode_exact():
+    """m = 1..8 queries per head takes the streaming kernel."""
+    for m in (1, 2, 3, 5, 8):
+        w = CONFIGS[4].scaled(n=9001, m=m, h=4)
+        K, V, Q = generate(w)
+        _check_exact(w, K, V, Q, label=f"decode m={m}")
+
+
+def test_empty_and_degenerate():
+    sk = E.sketch_create(8, 4, 3)
+    Q = torch.randn(5, 8, device="cuda")
+    out, Z = E.sketch_query(sk, Q)
+    out, Z = host(out, Z)
+    assert np.all(Z == 0.0) and np.all(np.isnan(out))
+    # n = 0 update is a no-op
+    E.sketch_update(sk, torch.empty(0, 8, device="cuda"), torch.empty(0, 4, device="cuda"))
+    assert sk.count == 0
+    # exact over an empty stream
+    o, z = E.exact_attend(torch.empty(1, 0, 8, device="cuda"),
+                          torch.empty(1, 0, 4, device="cuda"), Q[None])
+    o, z = host(o, z)
+    assert np.all(z == 0.0) and np.all(np.isnan(o))
+    # q = 0: Zhat = Z = n, outputs = mean of the values
+    K = torch.randn(777, 8, device="cuda") * 0.3
+    V = torch.randn(777, 4, device="cuda")
+    E.sketch_update(sk, K, V)
+    q0 = torch.zeros(3, 8, device="cuda")
+    out, Z = host(*E.sketch_query(sk, q0))
+    vbar = V.double().mean(0).cpu().numpy()
+    assert np.all(np.abs(Z - 777) <= 777 * 1e-6)
+    assert oabs(out, np.tile(vbar, (3, 1))) <= 1e-5
+    # reset empties the sketch
+    E.sketch_reset(sk)
+    assert sk.count == 0
+    S = host(E.sketch_export(sk))[0]
+    assert np.all(S == 0.0)
+    sk.destroy()
+
+
+def test_merge_mismatch_and_determinism():
+    a = E.sketch_create(8, 8, 3)
+    b = E.sketch_create(8, 8, 2)
+    with pytest.raises(E.SketchError) as ei:
+        E.sketch_merge(a, b)
+    assert ei.value.code == -3
+    w = CONFIGS[5].scaled(n=20000, m=100)
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = gpu(K, V, Q)
+    outs = []
+    for _ in range(2):
+        o, z, sk = run_sketch(w, Kg, Vg, Qg)
+        outs.append(host(o, z, E.sketch_export(sk)))
+        sk.destroy()
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+    a.destroy()
+    b.destroy()
+
+
+def test_merge_equals_single_stream():
+    w = CONFIGS[2].scaled(n=9000, m=64, chunk=1024)
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = gpu(K, V, Q)
+    whole, _ = ingest(w, Kg, Vg)
+    parts, _ = ingest(w.scaled(substreams=3), Kg, Vg)
+    S1, S2 = host(E.sketch_export(whole), E.sketch_export(parts))
+    mag = np.abs(S1).max()
+    assert np.abs(S1 - S2).max() <= 1e-6 * mag
+    assert parts.count == whole.count == 9000
+
+
+# Full-size workloads, run as the benchmark runs them; sampled queries checked.
+@pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
+def test_full_size_sampled(ident):
+    w = CONFIGS[ident]
+    say(f"full workload {ident}: {w.name} generating inputs")
+    K, V, Q = generate(w)
+    rng = np.random.default_rng(1234 + ident)
+    ns = min(w.m, 96 if w.h == 1 else 8)
+    qidx = np.sort(rng.choice(w.m, size=ns, replace=False))
+    qidx[0] = 0
+    qidx[-1] = w.m - 1
+    _check_sketch(w, K, V, Q, qidx=qidx, label=f"full {ident}")
+    _check_exact(w, K, V, Q, qidx=qidx, label=f"full {ident}")
+
+
+def test_full_size_decode_exact():
+    """Decode shape of the 32-head workload: one query per head over 128K keys."""
+    w = CONFIGS[4].scaled(m=1)
+    K, V, Q = generate(w)
+    _check_exact(w, K, V, Q, label="decode 32x128K")
+
+
+def test_sketch_error_within_bound():
+    """GPU sketch against GPU exact, against the truncation bound (high-temperature
+    workloads, where the bound is informative)."""
+    for ident in (1, 2, 4):
+        w = CONFIGS[ident].scaled(n=16384, m=128, h=min(CONFIGS[ident].h, 2))
+        K, V, Q = generate(w)
+        Kg, Vg, Qg = gpu(K, V, Q)
+        o_s, z_s, sk = run_sketch(w, Kg, Vg, Qg)
+        o_e, z_e = E.exact_attend(Kg, Vg, Qg)
+        o_s, z_s, o_e, z_e = host(o_s, z_s, o_e, z_e)
+        for hd in range(w.h):
+            rho = oracle.measured_radius(K[hd], Q[hd])
+            bound = oracle.kde_relative_bound(w.p, rho)
+            err = np.abs(z_s[hd] - z_e[hd]) / z_e[hd]
+            say(f"workload {ident}: sketch-vs-exact max rel Z err {err.max():.3e} "
+                f"(bound {bound:.3e})")
+            assert np.all(err <= bound + 4 * SK_Z_REL)
+        sk.destroy()
