@@ -25,7 +25,7 @@ namespace {
   } while (0)
 
 constexpr int kMaxP = 16;
-constexpr int kQueryRowsPerTile = 2048;   // feature rows per query tile
+constexpr int kQueryRowsPerTile = 256;    // a_hi rows per query tile
 
 bool is_pow2_in(int x, int lo, int hi) {
   return x >= lo && x <= hi && (x & (x - 1)) == 0;
@@ -73,12 +73,14 @@ int current_device(int* dev) {
 }
 
 size_t update_lds_bytes(int d, int dv) {
-  // Ks + Vs + Lt + Rt with (TM + TN + 2 * pad) <= 384
-  return sizeof(float) * ((size_t)SK_KB * (d + dv) + (size_t)SK_KB * 384);
+  // Ks + Vs (transposed, stride SK_KB + 1) + Lt + Rt with (TM + TN + 2 * pad) <= 384
+  return sizeof(float) * ((size_t)(SK_KB + 1) * (d + dv) + (size_t)SK_KB * 384);
 }
 size_t query_lds_bytes(int d) {
-  return sizeof(float) * ((size_t)d * (SK_TMQ + 1) + (size_t)SK_KB * (SK_TMQ + SK_PAD) +
-                          (size_t)SK_KB * 32);
+  // Qs + max(At + Bt, Ys)
+  const size_t ab = (size_t)SK_KB * (SK_TMQ + SK_PAD) + (size_t)SK_KB * (SK_TNQ + SK_PAD);
+  const size_t ys = (size_t)64 * (SK_TNQ + 1);
+  return sizeof(float) * ((size_t)d * (SK_TMQ + 1) + std::max(ab, ys));
 }
 
 }  // namespace
@@ -97,7 +99,7 @@ struct sk_sketch {
   std::vector<QryTile> qtiles;
   UpdTile* d_utiles = nullptr;
   QryTile* d_qtiles = nullptr;
-  float* d_wts = nullptr;   // 1/j! for j = 0..p+1
+  long long qpb = 0;        // floats of query partials per (head, query tile)
   float* view = nullptr;    // canonical view buffer
   size_t view_bytes = 0;
   DeviceInfo dev;
@@ -147,20 +149,43 @@ void plan_update_level(sk_sketch* s, int j, std::vector<UpdTile>* out) {
     }
 }
 
-void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out) {
-  const long long rows = s->rows[j];
-  for (int e0 = 0; e0 < s->C[j]; e0 += 32)
-    for (long long a0 = 0; a0 < rows; a0 += kQueryRowsPerTile) {
-      QryTile t{};
-      t.xoff = s->xoff[j];
-      t.a0 = a0;
-      t.a1 = std::min(rows, a0 + kQueryRowsPerTile);
-      t.level = j;
-      t.C = s->C[j];
-      t.top = (j == s->p);
-      t.e0 = e0;
-      out->push_back(t);
+// Query tiles of level j: t trailing digits in the columns (the fewest giving at
+// least SK_TNQ columns), 128-column tiles, a_hi ranges of kQueryRowsPerTile.
+void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long* pb) {
+  const int d = s->d, C = s->C[j];
+  int t = j;
+  for (int tt = 0; tt <= j; ++tt) {
+    if (std::pow((double)d, tt) * C >= SK_TNQ) { t = tt; break; }
+  }
+  while (t > SK_MAXDIG) --t;
+  const int sd = j - t;
+  const long long N = (long long)std::llround(std::pow((double)d, t)) * C;
+  const long long Kr = (long long)std::llround(std::pow((double)d, sd));
+  double fj = 1.0;
+  for (int i = 2; i <= j; ++i) fj *= i;
+  for (long long col0 = 0; col0 < N; col0 += SK_TNQ) {
+    const long long last = std::min(N, col0 + SK_TNQ) - 1;
+    for (long long a0 = 0; a0 < Kr; a0 += kQueryRowsPerTile) {
+      QryTile q{};
+      q.xoff = s->xoff[j];
+      q.a0 = a0;
+      q.a1 = std::min(Kr, a0 + kQueryRowsPerTile);
+      q.pofs = *pb;
+      q.level = j;
+      q.C = C;
+      q.top = (j == s->p);
+      q.s = sd;
+      q.t = t;
+      q.N = (int)N;
+      q.col0 = (int)col0;
+      q.alo0 = (int)(col0 / C);
+      q.nalo = (int)(last / C - col0 / C + 1);
+      q.wz = (float)(1.0 / (fj * (j + 1)));
+      q.wn = (float)(1.0 / fj);
+      *pb += (long long)SK_TMQ * C;
+      out->push_back(q);
     }
+  }
 }
 
 int choose_update_splits(const sk_sketch* s, long long n) {
@@ -246,14 +271,9 @@ int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out)
     return SK_EINVAL;
   }
   for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
-  for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles);
 
-  std::vector<float> wts(p + 2);
-  double f = 1.0;
-  for (int j = 0; j <= p + 1; ++j) {
-    if (j > 0) f *= j;
-    wts[j] = (float)(1.0 / f);
-  }
+  for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
+
   const size_t state_bytes = sizeof(float) * (size_t)s->XS * (size_t)h;
   if (hipMalloc(&s->state, state_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -261,14 +281,11 @@ int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out)
     return SK_ENOMEM;
   }
   bool ok = hipMalloc(&s->d_utiles, sizeof(UpdTile) * s->utiles.size()) == hipSuccess &&
-            hipMalloc(&s->d_qtiles, sizeof(QryTile) * s->qtiles.size()) == hipSuccess &&
-            hipMalloc(&s->d_wts, sizeof(float) * wts.size()) == hipSuccess;
+            hipMalloc(&s->d_qtiles, sizeof(QryTile) * s->qtiles.size()) == hipSuccess;
   if (ok)
     ok = hipMemcpy(s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size(),
                    hipMemcpyHostToDevice) == hipSuccess &&
          hipMemcpy(s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size(),
-                   hipMemcpyHostToDevice) == hipSuccess &&
-         hipMemcpy(s->d_wts, wts.data(), sizeof(float) * wts.size(),
                    hipMemcpyHostToDevice) == hipSuccess;
   if (ok) {
     const size_t ul = update_lds_bytes(d, dv), ql = query_lds_bytes(d);
@@ -280,7 +297,7 @@ int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out)
   if (ok) ok = launch_fill_zero(s->state, s->XS * h, s->stream) == SK_OK;
   if (!ok) {
     (void)hipGetLastError();
-    (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles); (void)hipFree(s->d_wts);
+    (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
     delete s;
     return SK_EHIP;
   }
@@ -295,7 +312,6 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->state);
   (void)hipFree(s->d_utiles);
   (void)hipFree(s->d_qtiles);
-  (void)hipFree(s->d_wts);
   (void)hipFree(s->view);
   delete s;
   return rc;
@@ -335,31 +351,32 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const int ntiles = (int)s->utiles.size();
   const size_t lds = update_lds_bytes(s->d, s->dv);
   const long long total = s->XS * s->h;
-  if (nsplit == 1) {
-    hipLaunchKernelGGL(sk_update_kernel, dim3(ntiles, s->h), dim3(SK_WG), lds, s->stream,
-                       K, V, (long long)n, s->d, s->dv, s->logd, s->d_utiles, ntiles,
-                       kps, s->state, s->XS, 0LL, 1);
-    SK_TRY(hipGetLastError());
-  } else {
-    float* parts = nullptr;
-    if (hipMallocAsync((void**)&parts, sizeof(float) * (size_t)total * nsplit, s->stream) !=
-        hipSuccess) {
-      (void)hipGetLastError();
-      return SK_ENOMEM;
-    }
-    hipLaunchKernelGGL(sk_update_kernel, dim3(ntiles * nsplit, s->h), dim3(SK_WG), lds,
-                       s->stream, K, V, (long long)n, s->d, s->dv, s->logd, s->d_utiles,
-                       ntiles, kps, parts, s->XS, total, 0);
-    hipError_t e1 = hipGetLastError();
+  float* parts = nullptr;
+  if (nsplit > 1 &&
+      hipMallocAsync((void**)&parts, sizeof(float) * (size_t)total * nsplit, s->stream) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return SK_ENOMEM;
+  }
+  float* dst = nsplit > 1 ? parts : s->state;
+  const long long sstride = nsplit > 1 ? total : 0;
+  const int acc = nsplit > 1 ? 0 : 1;
+  hipError_t err = hipSuccess;
+  hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)(ntiles * nsplit), s->h), dim3(SK_WG),
+                     lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd, s->d_utiles,
+                     ntiles, kps, dst, s->XS, sstride, acc);
+  err = hipGetLastError();
+  if (nsplit > 1) {
     const long long c4 = total / 4;
     const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
     hipLaunchKernelGGL(sk_split_reduce_kernel, dim3(grid), dim3(256), 0, s->stream,
                        reinterpret_cast<float4*>(s->state),
                        reinterpret_cast<const float4*>(parts), c4, nsplit, c4);
-    hipError_t e2 = hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) err = e;
     (void)hipFreeAsync(parts, s->stream);
-    if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   }
+  if (err != hipSuccess) return SK_EHIP;
   s->count += n;
   return SK_OK;
 }
@@ -385,7 +402,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
   if (nqt * ntiles > 0x7fffffffLL) return SK_EINVAL;
-  const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * ntiles * SK_TMQ * 32;
+  const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
   float* parts = nullptr;
   if (hipMallocAsync((void**)&parts, pbytes, s->stream) != hipSuccess) {
     (void)hipGetLastError();
@@ -393,11 +410,11 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   }
   hipLaunchKernelGGL(sk_query_kernel, dim3((unsigned)(ntiles * nqt), s->h), dim3(SK_WG),
                      query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->logd,
-                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->d_wts, parts);
+                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
   hipError_t e1 = hipGetLastError();
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)m, s->h), dim3(256), 0, s->stream,
-                     parts, s->d_qtiles, ntiles, (int)nqt, (long long)m, s->d, s->dv,
-                     (float)s->count, out, Z);
+                     parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
+                     s->dv, (float)s->count, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
@@ -520,9 +537,8 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
 #undef SK_TIL
   }
   hipError_t e1 = hipGetLastError();
-  const long long tot = (long long)h * m * dv;
-  hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
-                     parts, nsplit, mm, dv, h, out, Z);
+  hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
+                     nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, st);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;

@@ -39,13 +39,22 @@ struct UpdTile {
   int pad_;
 };
 
-// Tile descriptor of the query GEMM  Y[q][e] = sum_a Psi_j[q][a] X_j[a][e]
-// over a range of feature rows a of level j and 32 columns e.
+// Tile descriptor of the query of level j.  The level's Kronecker index is split
+// into s leading digits a_hi (the GEMM's reduction index) and t trailing digits
+// a_lo; the GEMM is
+//     Y[q][(a_lo, e)] = sum_{a_hi in [a0, a1)} q^(x)s[a_hi] * X_j[a_hi][(a_lo, e)]
+// over N = d^t * C columns, one tile owning 128 of them; the epilogue then folds
+// a_lo with the weights q^(x)t[a_lo].
 struct QryTile {
   long long xoff;   // float offset of level j inside one head's state
-  long long a0, a1; // feature-row range [a0, a1) of level j
+  long long a0, a1; // a_hi range
+  long long pofs;   // offset of this tile's [128][C] partial in a query-tile block
   int level;
   int C;            // row width of the level
   int top;
-  int e0;           // first column of the 32-column slice
+  int s, t;
+  int N;            // d^t * C
+  int col0;         // first GEMM column of the tile
+  int alo0, nalo;   // a_lo values the tile's columns touch
+  float wz, wn;     // 1/(j+1)! (weights of M_{j+1}), 1/j! (weights of N_j)
 };

@@ -238,27 +238,47 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
   }
 }
 
-// One thread per (head, query, column); splits folded in order.
+// One workgroup per (head, query).  The slices' maxima are reduced first; then
+// thread (g, slot) sums slot 0 (l) or slot 1 + c (acc[c]) over slices g, g + G,
+// ... with the rescale e^(mu_s - mu*), and the G group sums are added in group
+// order.  Fixed order throughout, so the result does not depend on timing.
 __global__ __launch_bounds__(256)
 void sk_exact_combine(const float* __restrict__ parts, int nsplit, long long m, int dv,
                       int h, float* __restrict__ out, float* __restrict__ Z) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)h * m * dv;
-  if (gid >= total) return;
-  const long long hq = gid / dv;
-  const int c = (int)(gid % dv);
-  const float* P = parts + hq * nsplit * (2 + dv);
-  float ms = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) ms = fmaxf(ms, P[sp * (2 + dv)]);
-  float L = 0.f, A = 0.f;
-  if (ms != -INFINITY) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* r = P + sp * (2 + dv);
-      const float sc = expf(r[0] - ms);
-      L += r[1] * sc;
-      A += r[2 + c] * sc;
+  __shared__ float red[256];
+  __shared__ float lsum;
+  const long long hq = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int rec = 2 + dv;
+  const float* P = parts + hq * (long long)nsplit * rec;
+  float mx = -INFINITY;
+  for (int sp = tid; sp < nsplit; sp += 256) mx = fmaxf(mx, P[(long long)sp * rec]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float ms = red[0];
+  __syncthreads();
+  const int slots = 1 + dv;
+  const int groups = 256 / slots > 0 ? 256 / slots : 1;
+  const int g = tid / slots, slot = tid - g * slots;
+  float acc = 0.f;
+  if (g < groups && ms != -INFINITY) {
+    for (int sp = g; sp < nsplit; sp += groups) {
+      const float* r = P + (long long)sp * rec;
+      acc += r[1 + slot] * expf(r[0] - ms);
     }
   }
-  out[hq * dv + c] = A / L;
-  if (c == 0) Z[hq] = (ms == -INFINITY) ? 0.f : expf(ms) * L;
+  red[tid] = acc;
+  __syncthreads();
+  float sum = 0.f;
+  if (tid < slots) {
+    for (int gg = 0; gg < groups; ++gg) sum += red[gg * slots + tid];
+    if (tid == 0) lsum = sum;
+  }
+  __syncthreads();
+  if (tid == 0) Z[hq] = (ms == -INFINITY) ? 0.f : expf(ms) * lsum;
+  else if (tid < slots) out[hq * dv + (tid - 1)] = sum / lsum;
 }

@@ -5,25 +5,35 @@
 //
 // With the level-fold layout (see sk_update.h), level j contributes
 //     Y_j[q][e] = sum_a q^(x)j[a] * X_j[a][e]
-// and then  Zhat += sum_{e<d} q[e] Y_j[q][e] / (j+1)!   (M_{j+1}, j < p)
-//           Ntilde[c] += Y_j[q][d + c] / j!   (j < p),  Y_p[q][c] / p!  (j = p)
-// plus the count for M_0.  Y_j is a GEMM with the query features on the left;
-// one workgroup owns 128 queries x 32 columns x a range of feature rows a, forms
-// the features q^(x)j[a] in LDS and streams the state rows through LDS into
-// v_mfma_f32_32x32x2_f32.  The epilogue applies the per-column weight and writes
-// a 128 x 32 partial; sk_query_finish sums the partials in a fixed order.
+// then  Zhat += sum_{e<d} q[e] Y_j[q][e] / (j+1)!     (this is M_{j+1}, j < p)
+//       Ntilde[c] += Y_j[q][d + c] / j!  (j < p),   Y_p[q][c] / p!  (j = p)
+// plus the count for M_0.  The feature index a is split into s leading digits
+// a_hi and t trailing digits a_lo, q^(x)j[a] = q^(x)s[a_hi] q^(x)t[a_lo], so
+//     Y_j[q][e] = sum_{a_lo} q^(x)t[a_lo] * sum_{a_hi} q^(x)s[a_hi] X_j[a_hi][(a_lo, e)].
+// The inner sum is a GEMM whose columns (a_lo, e) are rows of X_j read as they lie
+// in memory; t is chosen so that it has at least 128 columns.  One workgroup owns
+// 128 queries x 128 columns x a range of a_hi: per stage of 32 rows it forms the
+// query features q^(x)s in LDS, stages the state rows through LDS (fetched one
+// stage ahead into registers) and runs the same 2x2 v_mfma_f32_32x32x2_f32 register
+// tile per wave as the update.  The epilogue multiplies by q^(x)t[a_lo] (and by
+// q[e]/(j+1)! or 1/j!), folds a_lo through LDS in column order and writes a
+// [128][C] partial; sk_query_finish adds the partials in tile order.
 #pragma once
 
 #include "sk_common.h"
 
 #define SK_TMQ 128
+#define SK_TNQ 128
 
 __global__ __launch_bounds__(SK_WG, 2)
 void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
                      const float* __restrict__ X, long long head_stride,
                      const QryTile* __restrict__ tiles, int ntiles, int nqt,
-                     const float* __restrict__ wts,  // [p+2]: 1/j!
-                     float* __restrict__ parts) {
+                     long long PB, float* __restrict__ parts) {
+  constexpr int LDQ = SK_TMQ + 1;
+  constexpr int LDA = SK_TMQ + SK_PAD;
+  constexpr int LDB = SK_TNQ + SK_PAD;
+  constexpr int LDY = SK_TNQ + 1;
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -32,102 +42,137 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
   const int qt = blockIdx.x / ntiles;
   const long long head = blockIdx.y;
   const QryTile T = tiles[tile_id];
-  const int j = T.level;
+  const int dmask = d - 1;
 
-  const int LDQ = SK_TMQ + 1;
-  const int LDA = SK_TMQ + SK_PAD;
-  const int LDB = 32;
-  float* Qs = lds;                    // [d][LDQ]   transposed query tile
-  float* At = Qs + d * LDQ;           // [SK_KB][LDA] query features
-  float* Bt = At + SK_KB * LDA;       // [SK_KB][LDB] state rows
+  float* Qs = lds;                    // [d][LDQ]       query tile, transposed
+  float* At = Qs + d * LDQ;           // [SK_KB][LDA]   features q^(x)s[a_hi]
+  float* Bt = At + SK_KB * LDA;       // [SK_KB][LDB]   state rows
+  float* Ys = At;                     // [64][LDY]      epilogue (reuses At, Bt)
 
   const long long q0 = (long long)qt * SK_TMQ;
-  const float* Qh = Q + (head * m + q0) * d;
-  const long long qrem = m - q0;
-  for (int i = tid; i < SK_TMQ * d; i += SK_WG) {
-    const int qq = i / d, c = i - qq * d;
-    Qs[c * LDQ + qq] = (qq < qrem) ? Qh[i] : 0.f;
+  {
+    const float* Qh = Q + (head * m + q0) * d;
+    const long long qrem = m - q0;
+    for (int i = tid; i < SK_TMQ * d; i += SK_WG) {
+      const int qq = i / d, c = i - qq * d;
+      Qs[c * LDQ + qq] = (qq < qrem) ? Qh[i] : 0.f;
+    }
   }
 
   const float* Xh = X + head * head_stride + T.xoff;
-  const int C = T.C;
-  const long long arows = 1LL << (logd * j);   // d^j rows in level j
-  const long long a1 = T.a1 < arows ? T.a1 : arows;
-
-  // feature assignment: query qq, rows kk = kp, kp + 2, ...
-  const int qq = tid % SK_TMQ, kp = tid / SK_TMQ;
-  const int dmask = d - 1;
+  const int s = T.s;
+  const int qq = tid % SK_TMQ, kp = tid / SK_TMQ;   // feature thread: query, row phase
+  const int wr0 = (wave >> 1) * 64;                 // wave's queries
+  const int wc0 = (wave & 1) * 64;                  // wave's columns
   const int l32 = lane & 31, lhi = lane >> 5;
-  // state-row copy assignment: row kk = tid / 8, four columns at (tid % 8) * 4
-  const int bk = tid >> 3, bc = (tid & 7) * 4;
-  const bool bcol_ok = (T.e0 + bc) < C;
 
-  floatx16 acc = {0};
-  __syncthreads();
-
-  for (long long ab = T.a0; ab < a1; ab += SK_KB) {
-    // 1. state rows [ab, ab + SK_KB) x columns [e0, e0 + 32) -> LDS
-    {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      const long long a = ab + bk;
-      if (a < a1 && bcol_ok)
-        x = *reinterpret_cast<const float4*>(Xh + a * C + T.e0 + bc);
-      *reinterpret_cast<float4*>(Bt + bk * LDB + bc) = x;
+  float4 breg[4];
+  auto fetch = [&](long long ab) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + r * SK_WG;
+      const int row = i >> 5, c = (i & 31) * 4;
+      const long long a = ab + row;
+      const int col = T.col0 + c;
+      breg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a < T.a1 && col < T.N)
+        breg[r] = *reinterpret_cast<const float4*>(Xh + a * T.N + col);
     }
-    // 2. features q^(x)j[a]: the product of the j digits of a, reusing the
-    //    prefix (leading j-1 digits) while it does not change
-    {
-      long long cur_pre = -1;
-      float pre_val = 0.f;
-      for (int kk = kp; kk < SK_KB; kk += SK_WG / SK_TMQ) {
-        const long long a = ab + kk;
-        float f = 0.f;
-        if (a < a1) {
-          if (j == 0) {
-            f = 1.f;
-          } else {
-            const long long pre = a >> logd;
-            if (pre != cur_pre) {
-              float pv = 1.f;
-              for (int c = 0; c < j - 1; ++c) {
-                const int dig = (int)((pre >> (logd * (j - 2 - c))) & dmask);
-                pv *= Qs[dig * LDQ + qq];
-              }
-              cur_pre = pre;
-              pre_val = pv;
-            }
-            f = pre_val * Qs[(int)(a & dmask) * LDQ + qq];
-          }
+  };
+
+  floatx16 acc00 = {0}, acc01 = {0}, acc10 = {0}, acc11 = {0};
+  __syncthreads();
+  if (T.a0 < T.a1) fetch(T.a0);
+  for (long long ab = T.a0; ab < T.a1; ab += SK_KB) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + r * SK_WG;
+      *reinterpret_cast<float4*>(Bt + (i >> 5) * LDB + (i & 31) * 4) = breg[r];
+    }
+    // features q^(x)s[a_hi] of this thread's query for rows kp, kp + 2, ...
+    float f[SK_KB / 2];
+#pragma unroll
+    for (int u = 0; u < SK_KB / 2; ++u) f[u] = (ab + kp + 2 * u < T.a1) ? 1.f : 0.f;
+#pragma unroll
+    for (int c = 0; c < SK_MAXDIG; ++c) {
+      if (c < s) {
+        const int sh = logd * (s - 1 - c);
+#pragma unroll
+        for (int u = 0; u < SK_KB / 2; ++u) {
+          const int dig = (int)(((ab + kp + 2 * u) >> sh) & dmask);
+          f[u] *= Qs[dig * LDQ + qq];
         }
-        At[kk * LDA + qq] = f;
       }
     }
+#pragma unroll
+    for (int u = 0; u < SK_KB / 2; ++u) At[(kp + 2 * u) * LDA + qq] = f[u];
     __syncthreads();
-    // 3. MFMA: wave w owns queries [32 w, 32 w + 32)
-#pragma unroll 4
+    if (ab + SK_KB < T.a1) fetch(ab + SK_KB);
+    float a0 = At[lhi * LDA + wr0 + l32];
+    float a1 = At[lhi * LDA + wr0 + 32 + l32];
+    float b0 = Bt[lhi * LDB + wc0 + l32];
+    float b1 = Bt[lhi * LDB + wc0 + 32 + l32];
+#pragma unroll
     for (int ks = 0; ks < SK_KB / 2; ++ks) {
-      const int kr = 2 * ks + lhi;
-      const float a = At[kr * LDA + wave * 32 + l32];
-      const float b = Bt[kr * LDB + l32];
-      acc = mfma32x32x2(a, b, acc);
+      float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
+      if (ks + 1 < SK_KB / 2) {
+        const int kr = 2 * (ks + 1) + lhi;
+        na0 = At[kr * LDA + wr0 + l32];
+        na1 = At[kr * LDA + wr0 + 32 + l32];
+        nb0 = Bt[kr * LDB + wc0 + l32];
+        nb1 = Bt[kr * LDB + wc0 + 32 + l32];
+      }
+      acc00 = mfma32x32x2(a0, b0, acc00);
+      acc01 = mfma32x32x2(a0, b1, acc01);
+      acc10 = mfma32x32x2(a1, b0, acc10);
+      acc11 = mfma32x32x2(a1, b1, acc11);
+      a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
     }
     __syncthreads();
   }
 
-  // Epilogue: weight each column, write the 128 x 32 partial of this tile.
-  const int e = T.e0 + l32;
-  const bool zcol = (!T.top) && (e < d);
-  const float wz = wts[j + 1];
-  const float wn = wts[j];
-  float* P = parts + (((head * nqt + qt) * (long long)ntiles) + tile_id) * (SK_TMQ * 32);
+  // Epilogue, 64 queries at a time: weight each column by q^(x)t[a_lo] and by
+  // q[e]/(j+1)! (M_{j+1} part) or 1/j! (N_j part), then fold a_lo.
+  const int C = T.C, t = T.t;
+  float* P = parts + (head * nqt + qt) * PB + T.pofs;   // [SK_TMQ][C]
+  const floatx16* accs[4] = {&acc00, &acc01, &acc10, &acc11};
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    if ((wave >> 1) == half) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int q = wave * 32 + acc_row(r, lane);
-    float v;
-    if (e >= C) v = 0.f;
-    else if (zcol) v = acc[r] * Qs[e * LDQ + q] * wz;
-    else v = acc[r] * wn;
-    P[q * 32 + l32] = v;
+      for (int bi = 0; bi < 4; ++bi) {
+        const int i = bi >> 1, jj = bi & 1;
+        const int cl = wc0 + 32 * jj + l32;
+        const int col = T.col0 + cl;
+        const bool valid = col < T.N;
+        const int alo = col / C;
+        const int e = col - alo * C;
+        const bool zcol = (!T.top) && (e < d);
+        const floatx16 a = *accs[bi];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * i + acc_row(r, lane);   // 0..63 inside this half
+          const int q = wr0 + ql;
+          float w = 0.f;
+          if (valid) {
+            w = zcol ? Qs[e * LDQ + q] * T.wz : T.wn;
+            for (int c = 0; c < t; ++c)
+              w *= Qs[((alo >> (logd * (t - 1 - c))) & dmask) * LDQ + q];
+          }
+          Ys[ql * LDY + cl] = a[r] * w;
+        }
+      }
+    }
+    __syncthreads();
+    const int cmod = T.col0 % C;
+    for (int pi = tid; pi < 64 * C; pi += SK_WG) {
+      const int ql = pi / C, e = pi - ql * C;
+      int cl = e - cmod;
+      if (cl < 0) cl += C;
+      float sum = 0.f;
+      for (; cl < SK_TNQ && T.col0 + cl < T.N; cl += C) sum += Ys[ql * LDY + cl];
+      P[(long long)(64 * half + ql) * C + e] = sum;
+    }
   }
 }
 
@@ -136,22 +181,21 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
 // Ntilde[c].
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
-                     int ntiles, int nqt, long long m, int d, int dv, float count,
-                     float* __restrict__ out, float* __restrict__ Z) {
+                     int ntiles, int nqt, long long PB, long long m, int d, int dv,
+                     float count, float* __restrict__ out, float* __restrict__ Z) {
   __shared__ float zs;
   const long long q = blockIdx.x;
   const long long head = blockIdx.y;
   const int slot = threadIdx.x;
   const int qt = (int)(q / SK_TMQ), qi = (int)(q % SK_TMQ);
-  const float* P = parts + ((head * nqt + qt) * (long long)ntiles) * (SK_TMQ * 32) + qi * 32;
+  const float* P = parts + (head * nqt + qt) * PB;
   float acc = 0.f;
   if (slot == 0) {
     for (int ti = 0; ti < ntiles; ++ti) {
       const QryTile T = tiles[ti];
-      if (T.top || T.e0 >= d) continue;
-      const float* row = P + (long long)ti * (SK_TMQ * 32);
-      const int lim = min(32, min(d, T.C) - T.e0);
-      for (int c = 0; c < lim; ++c) acc += row[c];
+      if (T.top) continue;
+      const float* row = P + T.pofs + (long long)qi * T.C;
+      for (int e = 0; e < d; ++e) acc += row[e];
     }
     acc += count;
     zs = acc;
@@ -160,8 +204,7 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     for (int ti = 0; ti < ntiles; ++ti) {
       const QryTile T = tiles[ti];
       const int e = T.top ? c : d + c;
-      if (e < T.e0 || e >= T.e0 + 32 || e >= T.C) continue;
-      acc += P[(long long)ti * (SK_TMQ * 32) + (e - T.e0)];
+      acc += P[T.pofs + (long long)qi * T.C + e];
     }
   }
   __syncthreads();

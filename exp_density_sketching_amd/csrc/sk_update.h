@@ -27,30 +27,32 @@
 
 #include "sk_common.h"
 
-__global__ __launch_bounds__(SK_WG, 2)
-void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
-                      long long n, int d, int dv, int logd,
-                      const UpdTile* __restrict__ tiles, int ntiles,
-                      long long keys_per_split,
-                      float* __restrict__ out, long long head_stride,
-                      long long split_stride, int accumulate) {
+template <int WC>
+__device__ __forceinline__
+void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
+                    long long n, int d, int dv, int logd, const UpdTile& T,
+                    long long split, long long head, long long keys_per_split,
+                    float* __restrict__ out, long long head_stride,
+                    long long split_stride, int accumulate) {
+  constexpr int TM = SK_WG / WC;      // 256, 128 or 64 rows
+  constexpr int TN = 64 * WC;         // 64, 128 or 256 columns
+  constexpr int LDL = TM + SK_PAD;
+  constexpr int LDR = TN + SK_PAD;
+  constexpr int STEPL = SK_WG / TM, NKL = SK_KB / STEPL;   // keys per thread (L)
+  constexpr int STEPR = SK_WG / TN, NKR = SK_KB / STEPR;   // keys per thread (R)
+  constexpr int CHL = NKL < 16 ? NKL : 16, CHR = NKR < 16 ? NKR : 16;  // keys per pass
+  constexpr int NPF = 4;              // float4 per thread per stage, for d <= 128
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tile_id = blockIdx.x % ntiles;
-  const long long split = blockIdx.x / ntiles;
-  const long long head = blockIdx.y;
-  const UpdTile T = tiles[tile_id];
 
-  const int wc = T.wc;
-  const int TM = SK_WG / wc;          // 256, 128 or 64 rows
-  const int TN = 64 * wc;             // 64, 128 or 256 columns
-  const int LDL = TM + SK_PAD;
-  const int LDR = TN + SK_PAD;
-  float* Ks = lds;                    // [SK_KB][d]
-  float* Vs = Ks + SK_KB * d;         // [SK_KB][dv]
-  float* Lt = Vs + SK_KB * dv;        // [SK_KB][LDL]
+  // K and V of a stage are stored transposed, [component][key] with an odd row
+  // stride, so a thread's keys sit at compile-time offsets from one base.
+  constexpr int LDK = SK_KB + 1;
+  float* Ks = lds;                    // [d][LDK]
+  float* Vs = Ks + d * LDK;           // [dv][LDK]
+  float* Lt = Vs + dv * LDK;          // [SK_KB][LDL]
   float* Rt = Lt + SK_KB * LDL;       // [SK_KB][LDR]
 
   const long long k_begin = split * keys_per_split;
@@ -60,18 +62,19 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   const float* Kh = K + head * n * d;
   const float* Vh = V + head * n * dv;
 
-  // Feature assignment (fixed for the whole key loop).
+  // Feature assignment (fixed for the whole key loop): row rL of the L tile for
+  // keys kpL + STEPL*u, column cR of the R tile for keys kpR + STEPR*u.
   const int s = T.s, t = T.t;
   const int dmask = d - 1;
-  const int rL = tid % TM, kpL = tid / TM, stepL = SK_WG / TM;
+  const int rL = tid % TM, kpL = tid / TM;
   const int gL = T.row0 + rL;
   const bool validL = gL < T.M;
-  int dl[SK_MAXDIG];
+  int dl[SK_MAXDIG];   // LDS offsets of the key components named by the digits
 #pragma unroll
   for (int c = 0; c < SK_MAXDIG; ++c)
-    dl[c] = (c < s) ? ((gL >> (logd * (s - 1 - c))) & dmask) : 0;
+    dl[c] = ((c < s) ? ((gL >> (logd * (s - 1 - c))) & dmask) : 0) * LDK + kpL;
 
-  const int cR = tid % TN, kpR = tid / TN, stepR = SK_WG / TN;
+  const int cR = tid % TN, kpR = tid / TN;
   const int gR = T.col0 + cR;
   const bool validR = gR < T.N;
   const int alo = gR / T.C;             // trailing Kronecker digits of the column
@@ -79,15 +82,13 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   int dr[SK_MAXDIG];
 #pragma unroll
   for (int c = 0; c < SK_MAXDIG; ++c)
-    dr[c] = (c < t) ? ((alo >> (logd * (t - 1 - c))) & dmask) : 0;
+    dr[c] = ((c < t) ? ((alo >> (logd * (t - 1 - c))) & dmask) : 0) * LDK + kpR;
   // u = [k, v] below the top level, u = v at the top level
-  const float* usrc;
-  int ustride;
-  if (!T.top && e < d) { usrc = Ks + e; ustride = d; }
-  else { usrc = Vs + (T.top ? e : e - d); ustride = dv; }
+  const float* usrc = ((!T.top && e < d) ? Ks + e * LDK
+                                         : Vs + (T.top ? e : e - d) * LDK) + kpR;
 
-  const int wr0 = (wave / wc) * 64;
-  const int wc0 = (wave % wc) * 64;
+  const int wr0 = (wave / WC) * 64;
+  const int wc0 = (wave % WC) * 64;
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
@@ -97,53 +98,104 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   const int nV4 = SK_KB * dv / 4;
   const int d4 = d >> 2, dv4 = dv >> 2;
 
-  for (long long kb0 = k_begin; kb0 < k_end; kb0 += SK_KB) {
+  // Next stage's K and V rows are fetched into registers while the MFMAs of the
+  // current stage run; rows past the key range read as zero.
+  float4 kreg[NPF], vreg[NPF];
+  auto fetch = [&](long long kb0) {
     const long long left = k_end - kb0;
     const int nk = left < SK_KB ? (int)left : SK_KB;
-    // 1. K and V rows of this stage -> LDS (rows past the range read as zero)
     const float4* Kg = reinterpret_cast<const float4*>(Kh + kb0 * d);
     const float4* Vg = reinterpret_cast<const float4*>(Vh + kb0 * dv);
-    for (int i = tid; i < nK4; i += SK_WG) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i / d4 < nk) x = Kg[i];
-      reinterpret_cast<float4*>(Ks)[i] = x;
+#pragma unroll
+    for (int r = 0; r < NPF; ++r) {
+      const int i = tid + r * SK_WG;
+      kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < nK4 && i / d4 < nk) kreg[r] = Kg[i];
+      if (i < nV4 && i / dv4 < nk) vreg[r] = Vg[i];
     }
-    for (int i = tid; i < nV4; i += SK_WG) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i / dv4 < nk) x = Vg[i];
-      reinterpret_cast<float4*>(Vs)[i] = x;
+  };
+
+  if (k_begin < k_end) fetch(k_begin);
+  for (long long kb0 = k_begin; kb0 < k_end; kb0 += SK_KB) {
+    // 1. this stage's K and V rows -> LDS, transposed
+#pragma unroll
+    for (int r = 0; r < NPF; ++r) {
+      const int i = tid + r * SK_WG;
+      if (i < nK4) {
+        const int key = i / d4, c = 4 * (i - key * d4);
+        Ks[(c + 0) * LDK + key] = kreg[r].x;
+        Ks[(c + 1) * LDK + key] = kreg[r].y;
+        Ks[(c + 2) * LDK + key] = kreg[r].z;
+        Ks[(c + 3) * LDK + key] = kreg[r].w;
+      }
+      if (i < nV4) {
+        const int key = i / dv4, c = 4 * (i - key * dv4);
+        Vs[(c + 0) * LDK + key] = vreg[r].x;
+        Vs[(c + 1) * LDK + key] = vreg[r].y;
+        Vs[(c + 2) * LDK + key] = vreg[r].z;
+        Vs[(c + 3) * LDK + key] = vreg[r].w;
+      }
     }
     __syncthreads();
-    // 2. feature tiles: L = prod of s key entries, R = prod of t key entries * u[e]
-    for (int kk = kpL; kk < SK_KB; kk += stepL) {
-      const float* kr = Ks + kk * d;
-      float f = validL ? 1.f : 0.f;
+    // 2. feature tiles: L = prod of s key entries, R = u[e] * prod of t entries.
+    //    One digit at a time over all of the thread's keys, so the LDS reads of
+    //    a digit are issued together.
 #pragma unroll
-      for (int c = 0; c < SK_MAXDIG; ++c)
-        if (c < s) f *= kr[dl[c]];
-      Lt[kk * LDL + rL] = f;
+    for (int h0 = 0; h0 < NKL; h0 += CHL) {
+      float f[CHL];
+#pragma unroll
+      for (int u = 0; u < CHL; ++u) f[u] = validL ? 1.f : 0.f;
+#pragma unroll
+      for (int c = 0; c < SK_MAXDIG; ++c) {
+        if (c < s) {
+          const int off = dl[c] + STEPL * h0;
+#pragma unroll
+          for (int u = 0; u < CHL; ++u) f[u] *= Ks[off + STEPL * u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CHL; ++u) Lt[(kpL + STEPL * (h0 + u)) * LDL + rL] = f[u];
     }
-    for (int kk = kpR; kk < SK_KB; kk += stepR) {
-      const float* kr = Ks + kk * d;
-      float f = validR ? usrc[kk * ustride] : 0.f;
 #pragma unroll
-      for (int c = 0; c < SK_MAXDIG; ++c)
-        if (c < t) f *= kr[dr[c]];
-      Rt[kk * LDR + cR] = f;
+    for (int h0 = 0; h0 < NKR; h0 += CHR) {
+      float f[CHR];
+#pragma unroll
+      for (int u = 0; u < CHR; ++u) f[u] = validR ? usrc[STEPR * (h0 + u)] : 0.f;
+#pragma unroll
+      for (int c = 0; c < SK_MAXDIG; ++c) {
+        if (c < t) {
+          const int off = dr[c] + STEPR * h0;
+#pragma unroll
+          for (int u = 0; u < CHR; ++u) f[u] *= Ks[off + STEPR * u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CHR; ++u) Rt[(kpR + STEPR * (h0 + u)) * LDR + cR] = f[u];
     }
     __syncthreads();
-    // 3. fp32 MFMA over the stage: two keys per instruction
-#pragma unroll 4
+    if (kb0 + SK_KB < k_end) fetch(kb0 + SK_KB);
+    // 3. fp32 MFMA over the stage: two keys per instruction, operands of the
+    //    next k-step read while the current ones are in the matrix core
+    float a0 = Lt[lhi * LDL + wr0 + l32];
+    float a1 = Lt[lhi * LDL + wr0 + 32 + l32];
+    float b0 = Rt[lhi * LDR + wc0 + l32];
+    float b1 = Rt[lhi * LDR + wc0 + 32 + l32];
+#pragma unroll
     for (int ks = 0; ks < SK_KB / 2; ++ks) {
-      const int kr = 2 * ks + lhi;
-      const float a0 = Lt[kr * LDL + wr0 + l32];
-      const float a1 = Lt[kr * LDL + wr0 + 32 + l32];
-      const float b0 = Rt[kr * LDR + wc0 + l32];
-      const float b1 = Rt[kr * LDR + wc0 + 32 + l32];
+      float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
+      if (ks + 1 < SK_KB / 2) {
+        const int kr = 2 * (ks + 1) + lhi;
+        na0 = Lt[kr * LDL + wr0 + l32];
+        na1 = Lt[kr * LDL + wr0 + 32 + l32];
+        nb0 = Rt[kr * LDR + wc0 + l32];
+        nb1 = Rt[kr * LDR + wc0 + 32 + l32];
+      }
       acc00 = mfma32x32x2(a0, b0, acc00);
       acc01 = mfma32x32x2(a0, b1, acc01);
       acc10 = mfma32x32x2(a1, b0, acc10);
       acc11 = mfma32x32x2(a1, b1, acc11);
+      a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
     }
     __syncthreads();
   }
@@ -167,4 +219,27 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
       }
     }
   }
+}
+
+// One launch covers every tile of every level; the tile's shape picks the body.
+__global__ __launch_bounds__(SK_WG, 2)
+void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
+                      long long n, int d, int dv, int logd,
+                      const UpdTile* __restrict__ tiles, int ntiles,
+                      long long keys_per_split,
+                      float* __restrict__ out, long long head_stride,
+                      long long split_stride, int accumulate) {
+  const int tile_id = blockIdx.x % ntiles;
+  const long long split = blockIdx.x / ntiles;
+  const long long head = blockIdx.y;
+  const UpdTile T = tiles[tile_id];
+  if (T.wc == 2)
+    sk_update_tile<2>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+                      head_stride, split_stride, accumulate);
+  else if (T.wc == 1)
+    sk_update_tile<1>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+                      head_stride, split_stride, accumulate);
+  else
+    sk_update_tile<4>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+                      head_stride, split_stride, accumulate);
 }
