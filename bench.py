@@ -127,6 +127,8 @@ def main():
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
+    for sk in sketches:          # library events around the update/query kernels
+        E.sketch_timing(sk, True)
     rec = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -138,22 +140,32 @@ def main():
     t_ex = np.mean([c.elapsed_time(d) for _, _, c, d in rec]) / 1e3
     t_step = wall / args.steps
 
-    # dominant kernel: the moment update, timed per call on its stream
+    # dominant kernel: the moment update.  Its launches in the timed steps were
+    # bracketed by HIP events on the library's stream (sketch_timing).
+    upd_ms = [t for sk in sketches for t in E.sketch_kernel_times(sk, "update")]
+    qry_ms = E.sketch_kernel_times(sketches[0], "query")
+    for sk in sketches:
+        E.sketch_timing(sk, False)
+    dur = float(np.mean(upd_ms)) / 1e3
+    chunk = w.chunk or -(-w.n // S)
+    keys_per_call = float(np.mean([min(chunk, w.n // S - c0)
+                                   for c0 in range(0, w.n // S, chunk)]))
+    flop_per_key = 2.0 * w.D * (1 + w.dv)
+    achieved = flop_per_key * keys_per_call * w.h / dur
+    t_qk = float(np.mean(qry_ms)) / 1e3
+
+    # one whole sketch_update call (update kernel + split reduce), per call
     sk = sketches[0]
     E.sketch_reset(sk)
-    chunk = w.chunk or w.n
     per_call = []
-    for c0 in range(0, w.n, chunk):
+    for c0 in range(0, w.n // S, chunk):
         a, b = ev(), ev()
         a.record()
         E.sketch_update(sk, Kg[:, c0:c0 + chunk], Vg[:, c0:c0 + chunk])
         b.record()
-        per_call.append((a, b, min(chunk, w.n - c0)))
+        per_call.append((a, b))
     torch.cuda.synchronize()
-    dur = np.mean([a.elapsed_time(b) for a, b, _ in per_call]) / 1e3
-    keys_per_call = np.mean([k for _, _, k in per_call])
-    flop_per_key = 2.0 * w.D * (1 + w.dv)
-    achieved = flop_per_key * keys_per_call * w.h / dur
+    call_dur = float(np.mean([a.elapsed_time(b) for a, b in per_call])) / 1e3
 
     # exact path in decode mode (one query per head), streaming the whole KV
     dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
@@ -192,15 +204,18 @@ def main():
         "query_ms": t_qry * 1e3,
         "exact_ms": t_ex * 1e3,
         "query_mfma_frac": flop_per_key * w.h * w.m / t_qry / PEAK_FP32_MFMA,
+        "query_kernel_mfma_frac": flop_per_key * w.h * w.m / t_qk / PEAK_FP32_MFMA,
+        "update_call_us": call_dur * 1e6,
+        "update_call_mfma_frac": flop_per_key * keys_per_call * w.h / call_dur / PEAK_FP32_MFMA,
         "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
                          "kv_bytes": kv_bytes,
                          "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
-        "roofline": {"kernel": "sk_update_kernel (+ split reduce)", "bound": "mfma",
+        "roofline": {"kernel": "sk_update_kernel", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
                      "traffic": None,
                      "flop_per_launch": flop_per_key * keys_per_call * w.h,
-                     "launch_us": dur * 1e6},
+                     "launch_us": dur * 1e6, "launches": len(upd_ms)},
     }
     for s_ in sketches:
         s_.destroy()

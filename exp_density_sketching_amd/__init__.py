@@ -10,8 +10,10 @@ Problema" and "Metodologia" (pillar "O Método Polinomial", Merge-and-Reduce).
 
 from ._binding import (LIB_PATH, EXPORTED, Sketch, SketchError, sketch_create,
                        sketch_destroy, sketch_reset, sketch_update, sketch_merge,
-                       sketch_query, sketch_export, sketch_state, exact_attend, raw)
+                       sketch_query, sketch_export, sketch_state, sketch_timing,
+                       sketch_kernel_times, exact_attend, raw)
 
 __all__ = ["LIB_PATH", "EXPORTED", "Sketch", "SketchError", "sketch_create",
            "sketch_destroy", "sketch_reset", "sketch_update", "sketch_merge",
-           "sketch_query", "sketch_export", "sketch_state", "exact_attend", "raw"]
+           "sketch_query", "sketch_export", "sketch_state", "sketch_timing",
+           "sketch_kernel_times", "exact_attend", "raw"]

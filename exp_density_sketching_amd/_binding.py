@@ -18,7 +18,8 @@ SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("sketch_create", "sketch_destroy", "sketch_set_stream", "sketch_reset",
             "sketch_update", "sketch_merge", "sketch_query", "exact_attend",
-            "sketch_state", "sketch_export", "sketch_info", "sk_strerror", "sk_version")
+            "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
+            "sketch_kernel_times", "sk_strerror", "sk_version")
 
 
 class SketchError(RuntimeError):
@@ -56,6 +57,9 @@ def _lib():
             "sketch_info": (c_int, [vp, ctypes.POINTER(c_int), ctypes.POINTER(c_int),
                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int),
                                     ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
+            "sketch_timing": (c_int, [vp, c_int]),
+            "sketch_kernel_times": (c_int, [vp, c_int, ctypes.POINTER(ctypes.c_float), c_int,
+                                            ctypes.POINTER(c_int)]),
             "sk_strerror": (ctypes.c_char_p, [c_int]),
             "sk_version": (c_int, []),
         }
@@ -197,6 +201,21 @@ def sketch_state(s):
     _check(_lib().sketch_state(s._handle(), ctypes.byref(ptr), ctypes.byref(D),
                                ctypes.byref(cols), ctypes.byref(cnt)), "sketch_state")
     return ptr.value, D.value, cols.value, cnt.value
+
+
+def sketch_timing(s, enable=True):
+    _check(_lib().sketch_timing(s._h, 1 if enable else 0), "sketch_timing")
+
+
+def sketch_kernel_times(s, kind):
+    """Milliseconds of each recorded kernel of `kind` ("update" or "query")."""
+    k = {"update": 0, "query": 1}[kind]
+    cap = 256
+    buf = (ctypes.c_float * cap)()
+    cnt = ctypes.c_int()
+    _check(_lib().sketch_kernel_times(s._h, k, buf, cap, ctypes.byref(cnt)),
+           "sketch_kernel_times")
+    return [buf[i] for i in range(min(cnt.value, cap))]
 
 
 def exact_attend(K, V, Q, out=None, Z=None):

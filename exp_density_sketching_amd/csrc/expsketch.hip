@@ -101,11 +101,23 @@ struct sk_sketch {
   QryTile* d_qtiles = nullptr;
   long long qpb = 0;        // floats of query partials per (head, query tile)
   float* view = nullptr;    // canonical view buffer
+  bool timing = false;      // kernel timing (sketch_timing)
+  std::vector<hipEvent_t> tev[2][2];   // [kind][start, stop], created on first use
+  int trec[2] = {0, 0};     // pairs recorded per kind
   size_t view_bytes = 0;
   DeviceInfo dev;
 };
 
 namespace {
+
+constexpr int kTimingPairs = 256;
+
+// Records the start (stop = false) or stop event of the current pair of `kind`.
+void timing_mark(sk_sketch* s, int kind, bool stop) {
+  if (!s->timing || s->trec[kind] >= (int)s->tev[kind][0].size()) return;
+  (void)hipEventRecord(s->tev[kind][stop ? 1 : 0][s->trec[kind]], s->stream);
+  if (stop) ++s->trec[kind];
+}
 
 // Level split and tile shape of the update GEMM for one level: fewest tiles.
 void plan_update_level(sk_sketch* s, int j, std::vector<UpdTile>* out) {
@@ -313,6 +325,9 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->d_utiles);
   (void)hipFree(s->d_qtiles);
   (void)hipFree(s->view);
+  for (int k = 0; k < 2; ++k)
+    for (int w = 0; w < 2; ++w)
+      for (hipEvent_t e : s->tev[k][w]) (void)hipEventDestroy(e);
   delete s;
   return rc;
 }
@@ -362,10 +377,12 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const long long sstride = nsplit > 1 ? total : 0;
   const int acc = nsplit > 1 ? 0 : 1;
   hipError_t err = hipSuccess;
+  timing_mark(s, 0, false);
   hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)(ntiles * nsplit), s->h), dim3(SK_WG),
                      lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd, s->d_utiles,
                      ntiles, kps, dst, s->XS, sstride, acc);
   err = hipGetLastError();
+  timing_mark(s, 0, true);
   if (nsplit > 1) {
     const long long c4 = total / 4;
     const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
@@ -408,16 +425,46 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     (void)hipGetLastError();
     return SK_ENOMEM;
   }
+  timing_mark(s, 1, false);
   hipLaunchKernelGGL(sk_query_kernel, dim3((unsigned)(ntiles * nqt), s->h), dim3(SK_WG),
                      query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->logd,
                      s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
   hipError_t e1 = hipGetLastError();
+  timing_mark(s, 1, true);
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)m, s->h), dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
                      s->dv, (float)s->count, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
+  return SK_OK;
+}
+
+int sketch_timing(sk_handle s, int enable) {
+  if (s == nullptr) return SK_EINVAL;
+  if (enable && s->tev[0][0].empty()) {
+    for (int k = 0; k < 2; ++k)
+      for (int w = 0; w < 2; ++w) {
+        s->tev[k][w].resize(kTimingPairs);
+        for (int i = 0; i < kTimingPairs; ++i) SK_TRY(hipEventCreate(&s->tev[k][w][i]));
+      }
+  }
+  s->timing = enable != 0;
+  s->trec[0] = s->trec[1] = 0;
+  return SK_OK;
+}
+
+int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count) {
+  if (s == nullptr || kind < 0 || kind > 1 || cap < 0 || (ms == nullptr && cap > 0))
+    return SK_EINVAL;
+  const int nrec = s->trec[kind];
+  if (count) *count = nrec;
+  if (nrec > 0) {
+    SK_TRY(hipEventSynchronize(s->tev[kind][1][nrec - 1]));
+    for (int i = 0; i < nrec && i < cap; ++i)
+      SK_TRY(hipEventElapsedTime(&ms[i], s->tev[kind][0][i], s->tev[kind][1][i]));
+  }
+  s->trec[kind] = 0;
   return SK_OK;
 }
 

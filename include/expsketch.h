@@ -143,6 +143,22 @@ int sketch_export(sk_handle s, float* dst);
 int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D,
                 int64_t* count);
 
+/*
+ * sketch_timing -- kernel timing with HIP events on the handle's stream (for
+ * measurement).  While enabled, each sketch_update records a pair of
+ * library-owned events around its moment-update kernel (kind 0) and each
+ * sketch_query around its contraction kernel (kind 1), up to 256 pairs per kind;
+ * later calls are not recorded until the pairs are collected.  enable != 0
+ * starts (and clears) recording, 0 stops it.
+ * sketch_kernel_times -- waits for the last recorded event of `kind`, writes the
+ * elapsed milliseconds of up to `cap` recorded pairs into ms (host array), sets
+ * *count to the number recorded, and clears them.
+ * Errors: SK_EINVAL (NULL handle, kind not 0/1, cap < 0, ms NULL with cap > 0),
+ * SK_EHIP.
+ */
+int sketch_timing(sk_handle s, int enable);
+int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count);
+
 /* sk_strerror -- a static string for a status code. */
 const char* sk_strerror(int code);
 

@@ -225,3 +225,24 @@ def test_sketch_error_within_bound():
                 f"(bound {bound:.3e})")
             assert np.all(err <= bound + 4 * SK_Z_REL)
         sk.destroy()
+
+
+def test_kernel_timing_events():
+    """sketch_timing records one event pair per update/query kernel launch."""
+    w = CONFIGS[2].scaled(n=3 * 4096, m=200)
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = gpu(K, V, Q)
+    sk = E.sketch_create(w.d, w.dv, w.p)
+    E.sketch_timing(sk, True)
+    for c0 in range(0, w.n, 4096):
+        E.sketch_update(sk, Kg[:, c0:c0 + 4096], Vg[:, c0:c0 + 4096])
+    E.sketch_query(sk, Qg)
+    ups = E.sketch_kernel_times(sk, "update")
+    qs = E.sketch_kernel_times(sk, "query")
+    assert len(ups) == 3 and all(t > 0 for t in ups)
+    assert len(qs) == 1 and qs[0] > 0
+    assert E.sketch_kernel_times(sk, "update") == []
+    E.sketch_timing(sk, False)
+    E.sketch_update(sk, Kg[:, :4096], Vg[:, :4096])
+    assert E.sketch_kernel_times(sk, "update") == []
+    sk.destroy()
