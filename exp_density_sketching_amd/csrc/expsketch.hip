@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -201,6 +202,12 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
 }
 
 int choose_update_splits(const sk_sketch* s, long long n) {
+  // EXPSKETCH_UPDATE_SPLITS=<k> fixes the number of key splits (tuning aid).
+  static const int forced = [] {
+    const char* v = std::getenv("EXPSKETCH_UPDATE_SPLITS");
+    return v ? std::max(0, std::atoi(v)) : 0;
+  }();
+  if (forced > 0) return (int)std::max(1LL, std::min<long long>(forced, (n + SK_KB - 1) / SK_KB));
   const long long base = (long long)s->utiles.size() * s->h;
   const long long slots = 2LL * std::max(1, s->dev.num_cu);
   const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
@@ -530,9 +537,16 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   const int bmax = std::max(d, dv);
   const bool decode = m <= 8;
   const long long nqt = decode ? 1 : (m + 255) / 256;
-  const long long target = 8LL * di.num_cu;
+  // EXPSKETCH_EXACT_MINKEYS=<k> sets the fewest keys per slice (tuning aid).
+  static const long long min_keys_env = [] {
+    const char* v = std::getenv("EXPSKETCH_EXACT_MINKEYS");
+    return v ? std::max(0LL, std::atoll(v)) : 0LL;
+  }();
+  // Decode streams K/V once: about two long slices per CU keep HBM busiest.
+  // The batched kernel is compute-bound: more, shorter slices.
+  const long long target = (decode ? 2LL : 8LL) * di.num_cu;
   long long ns = (target + h * nqt - 1) / (h * nqt);
-  const long long min_keys = decode ? 1024 : 512;
+  const long long min_keys = min_keys_env > 0 ? min_keys_env : decode ? 4096 : 512;
   ns = std::max(1LL, std::min(ns, (n + min_keys - 1) / min_keys));
   long long kps = n > 0 ? (n + ns - 1) / ns : 0;
   kps = (kps + 31) / 32 * 32;

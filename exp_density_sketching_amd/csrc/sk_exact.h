@@ -20,7 +20,14 @@
 
 #include "sk_common.h"
 
-#define SK_EX_U 4
+#ifndef SK_EX_U
+#define SK_EX_U 8          // keys per group in flight per step (decode)
+#endif
+
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+  const floatx4v v = __builtin_nontemporal_load(reinterpret_cast<const floatx4v*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
@@ -78,8 +85,9 @@ void sk_exact_decode(const float* __restrict__ K, const float* __restrict__ V,
       ok[u] = key < k_end;
       k4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       v4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok[u] && kin) k4[u] = *reinterpret_cast<const float4*>(Kh + key * d + c4);
-      if (ok[u] && vin) v4[u] = *reinterpret_cast<const float4*>(Vh + key * dv + c4);
+      // streamed once: non-temporal loads
+      if (ok[u] && kin) k4[u] = ld_stream(Kh + key * d + c4);
+      if (ok[u] && vin) v4[u] = ld_stream(Vh + key * dv + c4);
     }
 #pragma unroll
     for (int i = 0; i < MQ; ++i) {
