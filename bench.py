@@ -33,7 +33,48 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--counters", action="store_true",
+                    help="short fixed sequence for rocprofv3 --pmc passes: a 1 GiB "
+                         "device copy, one pass of the update calls, 3 decode passes")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {
+    "sk_update_kernel": ["sk_update.h", "sk_common.h"],
+    "sk_exact_decode": ["sk_exact.h", "sk_common.h"],
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "exp_density_sketching_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic__{kernel}__{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, K, V, Q, budget):
@@ -80,6 +121,35 @@ def cpu_baseline(w, K, V, Q, budget):
     }
 
 
+def counters_pass(w, E, torch, generate):
+    """Fixed sequence for counter passes: copy of known size, update, decode."""
+    from exp_density_sketching_amd.workload import ingest
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    K, V, Q = generate(w)
+    Kg = torch.from_numpy(K).cuda()
+    Vg = torch.from_numpy(V).cuda()
+    S = max(1, w.substreams)
+    sketches = [E.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
+    ingest(w, Kg, Vg, sketches)
+    q1 = torch.from_numpy(Q[:, :1].copy()).cuda()
+    for _ in range(3):
+        E.exact_attend(Kg, Vg, q1)
+    torch.cuda.synchronize()
+    for sk in sketches:
+        sk.destroy()
+    print(json.dumps({"counters_pass": w.name, "copy_bytes": nbytes, "copies": 3,
+                      "update_sources": source_hash("sk_update_kernel"),
+                      "decode_sources": source_hash("sk_exact_decode"),
+                      "kv_bytes": 4 * w.h * w.n * (w.d + w.dv)}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -96,6 +166,8 @@ def main():
 
     w = CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.counters:
+        return counters_pass(w, E, torch, generate)
     K, V, Q = generate(w)
     Kg = torch.from_numpy(K).cuda()
     Vg = torch.from_numpy(V).cuda()
@@ -213,7 +285,7 @@ def main():
         "roofline": {"kernel": "sk_update_kernel", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
-                     "traffic": None,
+                     "traffic": committed_traffic("sk_update_kernel", w.name),
                      "flop_per_launch": flop_per_key * keys_per_call * w.h,
                      "launch_us": dur * 1e6, "launches": len(upd_ms)},
     }

@@ -26,7 +26,15 @@ namespace {
   } while (0)
 
 constexpr int kMaxP = 16;
-constexpr int kQueryRowsPerTile = 256;    // a_hi rows per query tile
+// a_hi rows per query tile (EXPSKETCH_QUERY_ROWS overrides, tuning aid)
+long long query_rows_per_tile() {
+  static const long long v = [] {
+    const char* e = std::getenv("EXPSKETCH_QUERY_ROWS");
+    const long long r = e ? std::atoll(e) : 0;
+    return r >= SK_KB ? r / SK_KB * SK_KB : 256LL;
+  }();
+  return v;
+}
 
 bool is_pow2_in(int x, int lo, int hi) {
   return x >= lo && x <= hi && (x & (x - 1)) == 0;
@@ -163,7 +171,7 @@ void plan_update_level(sk_sketch* s, int j, std::vector<UpdTile>* out) {
 }
 
 // Query tiles of level j: t trailing digits in the columns (the fewest giving at
-// least SK_TNQ columns), 128-column tiles, a_hi ranges of kQueryRowsPerTile.
+// least SK_TNQ columns), 128-column tiles, a_hi ranges of query_rows_per_tile().
 void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long* pb) {
   const int d = s->d, C = s->C[j];
   int t = j;
@@ -178,11 +186,11 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
   for (int i = 2; i <= j; ++i) fj *= i;
   for (long long col0 = 0; col0 < N; col0 += SK_TNQ) {
     const long long last = std::min(N, col0 + SK_TNQ) - 1;
-    for (long long a0 = 0; a0 < Kr; a0 += kQueryRowsPerTile) {
+    for (long long a0 = 0; a0 < Kr; a0 += query_rows_per_tile()) {
       QryTile q{};
       q.xoff = s->xoff[j];
       q.a0 = a0;
-      q.a1 = std::min(Kr, a0 + kQueryRowsPerTile);
+      q.a1 = std::min(Kr, a0 + query_rows_per_tile());
       q.pofs = *pb;
       q.level = j;
       q.C = C;
@@ -371,6 +379,7 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
   const int nsplit = (int)((n + kps - 1) / kps);
   const int ntiles = (int)s->utiles.size();
+  if ((long long)ntiles * nsplit * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t lds = update_lds_bytes(s->d, s->dv);
   const long long total = s->XS * s->h;
   float* parts = nullptr;
@@ -385,9 +394,9 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const int acc = nsplit > 1 ? 0 : 1;
   hipError_t err = hipSuccess;
   timing_mark(s, 0, false);
-  hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)(ntiles * nsplit), s->h), dim3(SK_WG),
-                     lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd, s->d_utiles,
-                     ntiles, kps, dst, s->XS, sstride, acc);
+  hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
+                     dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
+                     s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc);
   err = hipGetLastError();
   timing_mark(s, 0, true);
   if (nsplit > 1) {
@@ -425,7 +434,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
   const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
-  if (nqt * ntiles > 0x7fffffffLL) return SK_EINVAL;
+  if (nqt * ntiles * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
   float* parts = nullptr;
   if (hipMallocAsync((void**)&parts, pbytes, s->stream) != hipSuccess) {
@@ -433,9 +442,9 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     return SK_ENOMEM;
   }
   timing_mark(s, 1, false);
-  hipLaunchKernelGGL(sk_query_kernel, dim3((unsigned)(ntiles * nqt), s->h), dim3(SK_WG),
+  hipLaunchKernelGGL(sk_query_kernel, dim3((unsigned)(ntiles * nqt * s->h)), dim3(SK_WG),
                      query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->logd,
-                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
+                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->h, s->qpb, parts);
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 1, true);
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)m, s->h), dim3(256), 0, s->stream,

@@ -23,6 +23,17 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Map dispatch index p to a logical index so that every XCD works through one
+// contiguous range of logical indices: neighbours in logical order (tiles that
+// read the same keys, or the same state rows) then share an L2.
+#define SK_NXCD 8
+__device__ __forceinline__ long long xcd_remap(long long p, long long total) {
+  const long long x = p % SK_NXCD, i = p / SK_NXCD;
+  const long long q = total / SK_NXCD, rem = total % SK_NXCD;
+  return (x < rem) ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+}
+
 // Tile descriptor of the moment update: one (level, row tile, column tile) of the
 // level's GEMM  X_j[a_hi][(a_lo, e)] += sum_keys L[a_hi](k) * R[(a_lo, e)](k, v)
 // with L = k^(x)s (s leading digits) and R = k^(x)t (x) u, u = [k, v] below the

@@ -28,7 +28,7 @@
 __global__ __launch_bounds__(SK_WG, 2)
 void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
                      const float* __restrict__ X, long long head_stride,
-                     const QryTile* __restrict__ tiles, int ntiles, int nqt,
+                     const QryTile* __restrict__ tiles, int ntiles, int nqt, int nhead,
                      long long PB, float* __restrict__ parts) {
   constexpr int LDQ = SK_TMQ + 1;
   constexpr int LDA = SK_TMQ + SK_PAD;
@@ -38,9 +38,13 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tile_id = blockIdx.x % ntiles;
-  const int qt = blockIdx.x / ntiles;
-  const long long head = blockIdx.y;
+  // 1-D grid over (tile, query tile, head), tile fastest: tiles of different
+  // levels differ in length, so they are dealt round-robin over the XCDs
+  const long long lg = blockIdx.x;
+  const int tile_id = (int)(lg % ntiles);
+  const int qt = (int)((lg / ntiles) % nqt);
+  const long long head = lg / ((long long)nqt * ntiles);
+  (void)nhead;
   const QryTile T = tiles[tile_id];
   const int dmask = d - 1;
 
@@ -176,39 +180,60 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
   }
 }
 
-// Sum the partials of every tile in tile order, add the count, divide.
-// One workgroup per (query, head); thread 0 forms Zhat, thread 1 + c forms
-// Ntilde[c].
+// Sum the partials of every tile, add the count, divide.  One workgroup per
+// (query, head); thread 0 forms Zhat, thread 1 + c forms Ntilde[c].  The tile
+// table is staged in LDS so that the partial loads do not wait on descriptor
+// loads; each thread keeps four running sums (tiles i, i+4, ... in each) and adds
+// them in a fixed order at the end.
+#define SK_QFIN_LDS 1024
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
                      int ntiles, int nqt, long long PB, long long m, int d, int dv,
                      float count, float* __restrict__ out, float* __restrict__ Z) {
+  __shared__ long long tp[SK_QFIN_LDS];
+  __shared__ int tc[SK_QFIN_LDS];
+  __shared__ int tt[SK_QFIN_LDS];
   __shared__ float zs;
   const long long q = blockIdx.x;
   const long long head = blockIdx.y;
   const int slot = threadIdx.x;
   const int qt = (int)(q / SK_TMQ), qi = (int)(q % SK_TMQ);
   const float* P = parts + (head * nqt + qt) * PB;
-  float acc = 0.f;
-  if (slot == 0) {
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const QryTile T = tiles[ti];
-      if (T.top) continue;
-      const float* row = P + T.pofs + (long long)qi * T.C;
-      for (int e = 0; e < d; ++e) acc += row[e];
-    }
-    acc += count;
-    zs = acc;
-  } else if (slot <= dv) {
-    const int c = slot - 1;
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const QryTile T = tiles[ti];
-      const int e = T.top ? c : d + c;
-      acc += P[T.pofs + (long long)qi * T.C + e];
+  const bool staged = ntiles <= SK_QFIN_LDS;
+  if (staged) {
+    for (int i = slot; i < ntiles; i += 256) {
+      const QryTile T = tiles[i];
+      tp[i] = T.pofs + (long long)qi * T.C;
+      tc[i] = T.C;
+      tt[i] = T.top;
     }
   }
   __syncthreads();
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (slot == 0) {
+    for (int ti = 0; ti < ntiles; ++ti) {
+      long long base;
+      int top;
+      if (staged) { base = tp[ti]; top = tt[ti]; }
+      else { base = tiles[ti].pofs + (long long)qi * tiles[ti].C; top = tiles[ti].top; }
+      if (top) continue;
+      const float* row = P + base;
+      for (int e = 0; e < d; ++e) acc[e & 3] += row[e];
+    }
+  } else if (slot <= dv) {
+    const int c = slot - 1;
+    for (int ti = 0; ti < ntiles; ++ti) {
+      long long base;
+      int top;
+      if (staged) { base = tp[ti]; top = tt[ti]; }
+      else { base = tiles[ti].pofs + (long long)qi * tiles[ti].C; top = tiles[ti].top; }
+      acc[ti & 3] += P[base + (top ? c : d + c)];
+    }
+  }
+  const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (slot == 0) zs = sum + count;
+  __syncthreads();
   const float zh = zs;
   if (slot == 0) Z[head * m + q] = zh;
-  else if (slot <= dv) out[(head * m + q) * dv + (slot - 1)] = acc / zh;
+  else if (slot <= dv) out[(head * m + q) * dv + (slot - 1)] = sum / zh;
 }

@@ -226,12 +226,15 @@ __global__ __launch_bounds__(SK_WG, 2)
 void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                       long long n, int d, int dv, int logd,
                       const UpdTile* __restrict__ tiles, int ntiles,
-                      long long keys_per_split,
+                      long long keys_per_split, int nsplit, int nhead,
                       float* __restrict__ out, long long head_stride,
                       long long split_stride, int accumulate) {
-  const int tile_id = blockIdx.x % ntiles;
-  const long long split = blockIdx.x / ntiles;
-  const long long head = blockIdx.y;
+  // 1-D grid over (tile, split, head), tile fastest, remapped per XCD
+  const long long total = (long long)ntiles * nsplit * nhead;
+  const long long lg = xcd_remap(blockIdx.x, total);
+  const int tile_id = (int)(lg % ntiles);
+  const long long split = (lg / ntiles) % nsplit;
+  const long long head = lg / ((long long)ntiles * nsplit);
   const UpdTile T = tiles[tile_id];
   if (T.wc == 2)
     sk_update_tile<2>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
