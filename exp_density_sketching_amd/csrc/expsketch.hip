@@ -447,7 +447,8 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
                      s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->h, s->qpb, parts);
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 1, true);
-  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)m, s->h), dim3(256), 0, s->stream,
+  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / SK_QFG) * s->h)),
+                     dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
                      s->dv, (float)s->count, out, Z);
   hipError_t e2 = hipGetLastError();
@@ -551,12 +552,22 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     const char* v = std::getenv("EXPSKETCH_EXACT_MINKEYS");
     return v ? std::max(0LL, std::atoll(v)) : 0LL;
   }();
-  // Decode streams K/V once: about two long slices per CU keep HBM busiest.
-  // The batched kernel is compute-bound: more, shorter slices.
-  const long long target = (decode ? 2LL : 8LL) * di.num_cu;
-  long long ns = (target + h * nqt - 1) / (h * nqt);
-  const long long min_keys = min_keys_env > 0 ? min_keys_env : decode ? 4096 : 512;
-  ns = std::max(1LL, std::min(ns, (n + min_keys - 1) / min_keys));
+  // Decode streams K/V once: about two long (>= 4096-key) slices per CU keep HBM
+  // busiest, but never fewer slices than one per CU while slices stay >= 512
+  // keys.  The batched kernel is compute-bound: more, shorter slices.
+  const long long hq = h * nqt;
+  long long ns;
+  if (decode) {
+    const long long lk = min_keys_env > 0 ? min_keys_env : 4096;
+    const long long nn = n;
+    const long long ns_long = std::min((2LL * di.num_cu + hq - 1) / hq, (nn + lk - 1) / lk);
+    const long long ns_fill = std::min(((long long)di.num_cu + hq - 1) / hq, (nn + 511) / 512);
+    ns = std::max(ns_long, ns_fill);
+  } else {
+    const long long lk = min_keys_env > 0 ? min_keys_env : 512;
+    ns = std::min((8LL * di.num_cu + hq - 1) / hq, ((long long)n + lk - 1) / lk);
+  }
+  ns = std::max(1LL, ns);
   long long kps = n > 0 ? (n + ns - 1) / ns : 0;
   kps = (kps + 31) / 32 * 32;
   const int nsplit = kps > 0 ? (int)((n + kps - 1) / kps) : 1;

@@ -180,12 +180,13 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
   }
 }
 
-// Sum the partials of every tile, add the count, divide.  One workgroup per
-// (query, head); thread 0 forms Zhat, thread 1 + c forms Ntilde[c].  The tile
-// table is staged in LDS so that the partial loads do not wait on descriptor
-// loads; each thread keeps four running sums (tiles i, i+4, ... in each) and adds
-// them in a fixed order at the end.
+// Sum the partials of every tile in tile order, add the count, divide.  One
+// workgroup per (head, query tile, group of SK_QFG queries), the tile table staged
+// in LDS once.  Threads first form Zhat of each query (four running sums over the
+// tiles' M columns, added in a fixed order), then one (query, c) pair each forms
+// Ntilde[c] and ohat = Ntilde / Zhat.
 #define SK_QFIN_LDS 1024
+#define SK_QFG 16
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
                      int ntiles, int nqt, long long PB, long long m, int d, int dv,
@@ -193,47 +194,51 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
   __shared__ long long tp[SK_QFIN_LDS];
   __shared__ int tc[SK_QFIN_LDS];
   __shared__ int tt[SK_QFIN_LDS];
-  __shared__ float zs;
-  const long long q = blockIdx.x;
-  const long long head = blockIdx.y;
-  const int slot = threadIdx.x;
-  const int qt = (int)(q / SK_TMQ), qi = (int)(q % SK_TMQ);
+  __shared__ float zq[SK_QFG];
+  const int tid = threadIdx.x;
+  constexpr int NGRP = SK_TMQ / SK_QFG;
+  const int grpq = blockIdx.x % NGRP;
+  const int qt = (blockIdx.x / NGRP) % nqt;
+  const long long head = blockIdx.x / ((long long)NGRP * nqt);
   const float* P = parts + (head * nqt + qt) * PB;
+  const long long qbase = (long long)qt * SK_TMQ + grpq * SK_QFG;   // first query
+  const int qi0 = grpq * SK_QFG;                                    // inside the tile
   const bool staged = ntiles <= SK_QFIN_LDS;
   if (staged) {
-    for (int i = slot; i < ntiles; i += 256) {
+    for (int i = tid; i < ntiles; i += 256) {
       const QryTile T = tiles[i];
-      tp[i] = T.pofs + (long long)qi * T.C;
+      tp[i] = T.pofs;
       tc[i] = T.C;
       tt[i] = T.top;
     }
   }
   __syncthreads();
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (slot == 0) {
+  auto tinfo = [&](int ti, long long* pofs, int* C, int* top) {
+    if (staged) { *pofs = tp[ti]; *C = tc[ti]; *top = tt[ti]; }
+    else { const QryTile T = tiles[ti]; *pofs = T.pofs; *C = T.C; *top = T.top; }
+  };
+  if (tid < SK_QFG) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int ti = 0; ti < ntiles; ++ti) {
-      long long base;
-      int top;
-      if (staged) { base = tp[ti]; top = tt[ti]; }
-      else { base = tiles[ti].pofs + (long long)qi * tiles[ti].C; top = tiles[ti].top; }
+      long long pofs; int C, top;
+      tinfo(ti, &pofs, &C, &top);
       if (top) continue;
-      const float* row = P + base;
+      const float* row = P + pofs + (long long)(qi0 + tid) * C;
       for (int e = 0; e < d; ++e) acc[e & 3] += row[e];
     }
-  } else if (slot <= dv) {
-    const int c = slot - 1;
-    for (int ti = 0; ti < ntiles; ++ti) {
-      long long base;
-      int top;
-      if (staged) { base = tp[ti]; top = tt[ti]; }
-      else { base = tiles[ti].pofs + (long long)qi * tiles[ti].C; top = tiles[ti].top; }
-      acc[ti & 3] += P[base + (top ? c : d + c)];
-    }
+    zq[tid] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + count;
   }
-  const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  if (slot == 0) zs = sum + count;
   __syncthreads();
-  const float zh = zs;
-  if (slot == 0) Z[head * m + q] = zh;
-  else if (slot <= dv) out[(head * m + q) * dv + (slot - 1)] = sum / zh;
+  for (int pi = tid; pi < SK_QFG * dv; pi += 256) {
+    const int ql = pi / dv, c = pi - ql * dv;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ti = 0; ti < ntiles; ++ti) {
+      long long pofs; int C, top;
+      tinfo(ti, &pofs, &C, &top);
+      acc[ti & 3] += P[pofs + (long long)(qi0 + ql) * C + (top ? c : d + c)];
+    }
+    const long long q = qbase + ql;
+    if (q < m) out[(head * m + q) * dv + c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / zq[ql];
+  }
+  if (tid < SK_QFG && qbase + tid < m) Z[head * m + qbase + tid] = zq[tid];
 }
