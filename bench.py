@@ -122,7 +122,7 @@ def cpu_baseline(w, K, V, Q, budget):
 
 
 def counters_pass(w, E, torch, generate):
-    """Fixed sequence for counter passes: copy of known size, update, decode."""
+    """Fixed sequence for counter passes: copy of known size, update, query, decode."""
     from exp_density_sketching_amd.workload import ingest
     nbytes = 1 << 30
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -137,6 +137,9 @@ def counters_pass(w, E, torch, generate):
     S = max(1, w.substreams)
     sketches = [E.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
     ingest(w, Kg, Vg, sketches)
+    Qg = torch.from_numpy(Q).cuda()
+    for _ in range(3):
+        E.sketch_query(sketches[0], Qg)
     q1 = torch.from_numpy(Q[:, :1].copy()).cuda()
     for _ in range(3):
         E.exact_attend(Kg, Vg, q1)

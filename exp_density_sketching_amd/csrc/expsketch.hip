@@ -31,7 +31,7 @@ long long query_rows_per_tile() {
   static const long long v = [] {
     const char* e = std::getenv("EXPSKETCH_QUERY_ROWS");
     const long long r = e ? std::atoll(e) : 0;
-    return r >= SK_KB ? r / SK_KB * SK_KB : 256LL;
+    return r >= SK_KB ? r / SK_KB * SK_KB : 512LL;
   }();
   return v;
 }
@@ -90,6 +90,21 @@ size_t query_lds_bytes(int d) {
   const size_t ab = (size_t)SK_KB * (SK_TMQ + SK_PAD) + (size_t)SK_KB * (SK_TNQ + SK_PAD);
   const size_t ys = (size_t)64 * (SK_TNQ + 1);
   return sizeof(float) * ((size_t)d * (SK_TMQ + 1) + std::max(ab, ys));
+}
+
+// The query kernel is instantiated per log2(d) (d = 4 .. 128).
+using QueryKernel = void (*)(const float*, long long, const float*, long long,
+                             const QryTile*, int, int, long long, float*);
+QueryKernel query_kernel_for(int logd) {
+  switch (logd) {
+    case 2: return sk_query_kernel<2>;
+    case 3: return sk_query_kernel<3>;
+    case 4: return sk_query_kernel<4>;
+    case 5: return sk_query_kernel<5>;
+    case 6: return sk_query_kernel<6>;
+    case 7: return sk_query_kernel<7>;
+    default: return nullptr;
+  }
 }
 
 }  // namespace
@@ -318,7 +333,7 @@ int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out)
     const size_t ul = update_lds_bytes(d, dv), ql = query_lds_bytes(d);
     ok = hipFuncSetAttribute((const void*)sk_update_kernel,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
-         hipFuncSetAttribute((const void*)sk_query_kernel,
+         hipFuncSetAttribute((const void*)query_kernel_for(s->logd),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
   }
   if (ok) ok = launch_fill_zero(s->state, s->XS * h, s->stream) == SK_OK;
@@ -434,7 +449,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
   const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
-  if (nqt * ntiles * s->h > 0x7fffffffLL) return SK_EINVAL;
+  if (nqt * std::max<long long>(ntiles, SK_TMQ) * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
   float* parts = nullptr;
   if (hipMallocAsync((void**)&parts, pbytes, s->stream) != hipSuccess) {
@@ -442,15 +457,18 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     return SK_ENOMEM;
   }
   timing_mark(s, 1, false);
-  hipLaunchKernelGGL(sk_query_kernel, dim3((unsigned)(ntiles * nqt * s->h)), dim3(SK_WG),
-                     query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->logd,
-                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->h, s->qpb, parts);
+  hipLaunchKernelGGL(query_kernel_for(s->logd), dim3((unsigned)(ntiles * nqt * s->h)),
+                     dim3(SK_WG), query_lds_bytes(s->d), s->stream, Q, (long long)m,
+                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 1, true);
-  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / SK_QFG) * s->h)),
+  // queries per finishing workgroup: a power of two with qg * (d + dv) <= 256
+  int qg = 1;
+  while (qg < SK_TMQ && 2 * qg * (s->d + s->dv) <= 256) qg *= 2;
+  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / qg) * s->h)),
                      dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
-                     s->dv, (float)s->count, out, Z);
+                     s->dv, qg, (float)s->count, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;

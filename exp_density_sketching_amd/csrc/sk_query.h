@@ -25,15 +25,21 @@
 #define SK_TMQ 128
 #define SK_TNQ 128
 
+template <int LOGD>
 __global__ __launch_bounds__(SK_WG, 2)
-void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
+void sk_query_kernel(const float* __restrict__ Q, long long m,
                      const float* __restrict__ X, long long head_stride,
-                     const QryTile* __restrict__ tiles, int ntiles, int nqt, int nhead,
+                     const QryTile* __restrict__ tiles, int ntiles, int nqt,
                      long long PB, float* __restrict__ parts) {
+  constexpr int d = 1 << LOGD;
+  constexpr int dmask = d - 1;
   constexpr int LDQ = SK_TMQ + 1;
   constexpr int LDA = SK_TMQ + SK_PAD;
   constexpr int LDB = SK_TNQ + SK_PAD;
   constexpr int LDY = SK_TNQ + 1;
+  // digits of a row index that overlap its lowest four bits
+  constexpr int NV = (4 + LOGD - 1) / LOGD;
+  static_assert(NV <= 2, "d >= 4");
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -44,9 +50,7 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
   const int tile_id = (int)(lg % ntiles);
   const int qt = (int)((lg / ntiles) % nqt);
   const long long head = lg / ((long long)nqt * ntiles);
-  (void)nhead;
   const QryTile T = tiles[tile_id];
-  const int dmask = d - 1;
 
   float* Qs = lds;                    // [d][LDQ]       query tile, transposed
   float* At = Qs + d * LDQ;           // [SK_KB][LDA]   features q^(x)s[a_hi]
@@ -65,7 +69,14 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
 
   const float* Xh = X + head * head_stride + T.xoff;
   const int s = T.s;
-  const int qq = tid % SK_TMQ, kp = tid / SK_TMQ;   // feature thread: query, row phase
+  // Feature thread: query qq, rows 16 kp + u (u < 16) of every 32-row stage.  A
+  // stage starts at a multiple of 32, so row ab + 16 kp + u has the bits of ab,
+  // kp and u in disjoint places: its digits above bit 3 are the same for all 16
+  // rows of the thread (one product per stage), and only the (at most two)
+  // digits overlapping bits 0..3 change with u, by compile-time amounts.
+  const int qq = tid % SK_TMQ;
+  const int kp = __builtin_amdgcn_readfirstlane(tid / SK_TMQ);
+  const float* Qq = Qs + qq;
   const int wr0 = (wave >> 1) * 64;                 // wave's queries
   const int wc0 = (wave & 1) * 64;                  // wave's columns
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -93,23 +104,32 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
       const int i = tid + r * SK_WG;
       *reinterpret_cast<float4*>(Bt + (i >> 5) * LDB + (i & 31) * 4) = breg[r];
     }
-    // features q^(x)s[a_hi] of this thread's query for rows kp, kp + 2, ...
-    float f[SK_KB / 2];
+    // features q^(x)s[a_hi] of this thread's query for rows ab + 16 kp + u
+    {
+      const long long rb = ab + 16 * kp;            // first row of the thread
+      float hpre = 1.f;
 #pragma unroll
-    for (int u = 0; u < SK_KB / 2; ++u) f[u] = (ab + kp + 2 * u < T.a1) ? 1.f : 0.f;
+      for (int i = NV; i < SK_MAXDIG; ++i)
+        if (i < s) hpre *= Qq[(int)((rb >> (LOGD * i)) & dmask) * LDQ];
+      const long long rem = T.a1 - rb;              // rows of the thread still in range
+      const int nvs = s < NV ? s : NV;
+      const float* Q0 = Qq + (int)(rb & dmask) * LDQ;
+      const float* Q1 = Qq + (int)((rb >> LOGD) & dmask) * LDQ;
+      float f[16];
+      if (nvs == 0) {
 #pragma unroll
-    for (int c = 0; c < SK_MAXDIG; ++c) {
-      if (c < s) {
-        const int sh = logd * (s - 1 - c);
+        for (int u = 0; u < 16; ++u) f[u] = hpre;
+      } else if (nvs == 1) {
 #pragma unroll
-        for (int u = 0; u < SK_KB / 2; ++u) {
-          const int dig = (int)(((ab + kp + 2 * u) >> sh) & dmask);
-          f[u] *= Qs[dig * LDQ + qq];
-        }
+        for (int u = 0; u < 16; ++u) f[u] = hpre * Q0[(u & dmask) * LDQ];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          f[u] = hpre * Q0[(u & dmask) * LDQ] * Q1[((u >> LOGD) & dmask) * LDQ];
       }
-    }
 #pragma unroll
-    for (int u = 0; u < SK_KB / 2; ++u) At[(kp + 2 * u) * LDA + qq] = f[u];
+      for (int u = 0; u < 16; ++u) At[(16 * kp + u) * LDA + qq] = (u < rem) ? f[u] : 0.f;
+    }
     __syncthreads();
     if (ab + SK_KB < T.a1) fetch(ab + SK_KB);
     float a0 = At[lhi * LDA + wr0 + l32];
@@ -161,7 +181,7 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
           if (valid) {
             w = zcol ? Qs[e * LDQ + q] * T.wz : T.wn;
             for (int c = 0; c < t; ++c)
-              w *= Qs[((alo >> (logd * (t - 1 - c))) & dmask) * LDQ + q];
+              w *= Qs[((alo >> (LOGD * (t - 1 - c))) & dmask) * LDQ + q];
           }
           Ys[ql * LDY + cl] = a[r] * w;
         }
@@ -181,28 +201,31 @@ void sk_query_kernel(const float* __restrict__ Q, long long m, int d, int logd,
 }
 
 // Sum the partials of every tile in tile order, add the count, divide.  One
-// workgroup per (head, query tile, group of SK_QFG queries), the tile table staged
-// in LDS once.  Threads first form Zhat of each query (four running sums over the
-// tiles' M columns, added in a fixed order), then one (query, c) pair each forms
-// Ntilde[c] and ohat = Ntilde / Zhat.
+// workgroup per (head, query tile, group of qg queries), qg * (d + dv) <= 256, the
+// tile table staged in LDS once.  Thread (query, col) adds column col of its query
+// over the tiles in tile order (four running sums, tile index mod 4): a column
+// col < d of a lower level holds a share of Zhat, col >= d one of Ntilde[col - d]
+// (top-level tiles hold only the Ntilde columns, at col - d).  Zhat is then the
+// count plus the Zhat columns of the query, added in column order.
 #define SK_QFIN_LDS 1024
-#define SK_QFG 16
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
-                     int ntiles, int nqt, long long PB, long long m, int d, int dv,
+                     int ntiles, int nqt, long long PB, long long m, int d, int dv, int qg,
                      float count, float* __restrict__ out, float* __restrict__ Z) {
   __shared__ long long tp[SK_QFIN_LDS];
   __shared__ int tc[SK_QFIN_LDS];
   __shared__ int tt[SK_QFIN_LDS];
-  __shared__ float zq[SK_QFG];
+  __shared__ float cs[256];
+  __shared__ float zq[256];
   const int tid = threadIdx.x;
-  constexpr int NGRP = SK_TMQ / SK_QFG;
-  const int grpq = blockIdx.x % NGRP;
-  const int qt = (blockIdx.x / NGRP) % nqt;
-  const long long head = blockIdx.x / ((long long)NGRP * nqt);
+  const int cols = d + dv;
+  const int ngrp = SK_TMQ / qg;
+  const int grpq = blockIdx.x % ngrp;
+  const int qt = (blockIdx.x / ngrp) % nqt;
+  const long long head = blockIdx.x / ((long long)ngrp * nqt);
   const float* P = parts + (head * nqt + qt) * PB;
-  const long long qbase = (long long)qt * SK_TMQ + grpq * SK_QFG;   // first query
-  const int qi0 = grpq * SK_QFG;                                    // inside the tile
+  const int qi0 = grpq * qg;                                        // inside the tile
+  const long long qbase = (long long)qt * SK_TMQ + qi0;             // first query
   const bool staged = ntiles <= SK_QFIN_LDS;
   if (staged) {
     for (int i = tid; i < ntiles; i += 256) {
@@ -213,32 +236,41 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     }
   }
   __syncthreads();
-  auto tinfo = [&](int ti, long long* pofs, int* C, int* top) {
-    if (staged) { *pofs = tp[ti]; *C = tc[ti]; *top = tt[ti]; }
-    else { const QryTile T = tiles[ti]; *pofs = T.pofs; *C = T.C; *top = T.top; }
+  const bool act = tid < qg * cols;
+  const int ql = act ? tid / cols : 0;
+  const int col = tid - ql * cols;
+  const long long qoff = qi0 + ql;
+  // one term: the partial of tile ti for (query, col), zero if the tile has no such column
+  auto term = [&](int ti) -> float {
+    long long pofs; int C, top;
+    if (staged) { pofs = tp[ti]; C = tc[ti]; top = tt[ti]; }
+    else { const QryTile T = tiles[ti]; pofs = T.pofs; C = T.C; top = T.top; }
+    const int c = top ? col - d : col;
+    return (c >= 0) ? P[pofs + qoff * C + c] : 0.f;
   };
-  if (tid < SK_QFG) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ti = 0; ti < ntiles; ++ti) {
-      long long pofs; int C, top;
-      tinfo(ti, &pofs, &C, &top);
-      if (top) continue;
-      const float* row = P + pofs + (long long)(qi0 + tid) * C;
-      for (int e = 0; e < d; ++e) acc[e & 3] += row[e];
+  if (act) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int ti = 0;
+    for (; ti + 4 <= ntiles; ti += 4) {
+      const float v0 = term(ti), v1 = term(ti + 1), v2 = term(ti + 2), v3 = term(ti + 3);
+      a0 += v0; a1 += v1; a2 += v2; a3 += v3;
     }
-    zq[tid] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + count;
+    if (ti < ntiles) a0 += term(ti);
+    if (ti + 1 < ntiles) a1 += term(ti + 1);
+    if (ti + 2 < ntiles) a2 += term(ti + 2);
+    cs[tid] = (a0 + a1) + (a2 + a3);
   }
   __syncthreads();
-  for (int pi = tid; pi < SK_QFG * dv; pi += 256) {
-    const int ql = pi / dv, c = pi - ql * dv;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ti = 0; ti < ntiles; ++ti) {
-      long long pofs; int C, top;
-      tinfo(ti, &pofs, &C, &top);
-      acc[ti & 3] += P[pofs + (long long)(qi0 + ql) * C + (top ? c : d + c)];
+  if (tid < qg) {
+    const float* row = cs + tid * cols;
+    float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
+    for (int e = 0; e < d; e += 4) {
+      z0 += row[e]; z1 += row[e + 1]; z2 += row[e + 2]; z3 += row[e + 3];
     }
-    const long long q = qbase + ql;
-    if (q < m) out[(head * m + q) * dv + c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / zq[ql];
+    zq[tid] = ((z0 + z1) + (z2 + z3)) + count;
   }
-  if (tid < SK_QFG && qbase + tid < m) Z[head * m + qbase + tid] = zq[tid];
+  __syncthreads();
+  const long long q = qbase + ql;
+  if (act && col >= d && q < m) out[(head * m + q) * dv + (col - d)] = cs[tid] / zq[ql];
+  if (tid < qg && qbase + tid < m) Z[head * m + qbase + tid] = zq[tid];
 }
