@@ -25,6 +25,10 @@ repository's design notes):
 * Same section, closing paragraph on Merge-and-Reduce: summaries of sub-streams
   are merged.  Moments are sums, so the merge is an addition.
   -> ``sketch.MomentSketch.merge``.
+* ``sym``: the same moments kept once per multiset of tensor indices (the moment
+  tensors are symmetric), with the query weight q^alpha / alpha!.  The pages
+  leave the storage open; this is the symmetric-tensor reading.
+  -> ``sym.SymMomentSketch``.
 * ``bounds``: the Lagrange form of the Taylor remainder, carried through the sums
   (derived here; the pages state only asymptotic space bounds).
 
@@ -35,9 +39,11 @@ docstrings there).  No function of this package is "parity unpinned".
 
 from .exact import exact_attention
 from .sketch import taylor_exp, sketch_direct, MomentSketch, feature_map
+from .sym import SymMomentSketch, multisets, alpha_factorial, sym_features
 from .bounds import (taylor_term_bound, kde_relative_bound, attention_abs_bound,
                      measured_radius)
 
 __all__ = ["exact_attention", "taylor_exp", "sketch_direct", "MomentSketch",
-           "feature_map", "taylor_term_bound", "kde_relative_bound",
+           "feature_map", "SymMomentSketch", "multisets", "alpha_factorial",
+           "sym_features", "taylor_term_bound", "kde_relative_bound",
            "attention_abs_bound", "measured_radius"]

@@ -274,3 +274,104 @@ def pin_taylor_gamma(impl):
         refn = np.array([math.fsum(c * x ** j for j, c in enumerate(coef)) for x in xn])
         err = max(err, absmax(impl.taylor_exp(xn, p), refn) / max(1.0, np.abs(refn).max()))
     return err
+
+
+# Multiset storage (oracle.sym) ------------------------------------------------------
+
+def _sorted_tuples(d, j, lo=0):
+    """Sorted index tuples of size j over lo..d-1 in lexicographic order, by
+    recursion (independent of itertools)."""
+    if j == 0:
+        return [()]
+    out = []
+    for a in range(lo, d):
+        out.extend((a,) + rest for rest in _sorted_tuples(d, j - 1, a))
+    return out
+
+
+def pin_sym_counts(impl, d, p):
+    """S1: row counts are C(d + j - 1, j) per level and C(d + p, p) in all; the
+    tuples are sorted, distinct and in lexicographic order; the multinomial
+    theorem sum_alpha j!/alpha! = d^j holds for the alpha! the module computes."""
+    err = 0.0
+    total = 0
+    for j in range(p + 1):
+        t = impl.multisets(d, j)
+        total += t.shape[0]
+        err = max(err, abs(t.shape[0] - math.comb(d + j - 1, j)))
+        ref = _sorted_tuples(d, j)
+        err = max(err, 0.0 if [tuple(r) for r in t] == ref else 1.0)
+        mult = math.factorial(j) / impl.alpha_factorial(t)
+        err = max(err, abs(float(mult.sum()) - d ** j) / d ** j)
+    err = max(err, abs(total - math.comb(d + p, p)))
+    sk = impl.SymMomentSketch(d, 2, p)
+    err = max(err, abs(sk.rows - math.comb(d + p, p)))
+    return err
+
+
+def pin_sym_bruteforce(impl, d, p, n=9, m=3, dv=2, seed=21):
+    """S2: stored entries and query answers against pure-Python sums over every
+    index tuple of every level (math.factorial, itertools.product)."""
+    import itertools as it
+    K, V, Q = _small(seed + 7 * d + p, n, m, d, dv)
+    sk = impl.SymMomentSketch(d, dv, p).update(K, V, chunk=4)
+    # stored entries, in the independently generated row order
+    S = sk.canonical_state()
+    ref_rows = []
+    for j in range(p + 1):
+        for alpha in _sorted_tuples(d, j):
+            w = [math.prod(float(K[i][a]) for a in alpha) for i in range(n)]
+            ref_rows.append([math.fsum(w)] +
+                            [math.fsum(w[i] * float(V[i][c]) for i in range(n))
+                             for c in range(dv)])
+    ref = np.array(ref_rows)
+    err = float(np.max(np.abs(S - ref) / np.maximum(np.abs(ref), 1.0)))
+    # answers: sum over all index tuples, 1/j!
+    Zb = np.zeros(m)
+    Nb = np.zeros((m, dv))
+    for qi in range(m):
+        for i in range(n):
+            w = 0.0
+            for j in range(p + 1):
+                w += math.fsum(math.prod(float(Q[qi][a]) * float(K[i][a]) for a in idx)
+                               for idx in it.product(range(d), repeat=j)) / math.factorial(j)
+            Zb[qi] += w
+            Nb[qi] += w * V[i]
+    o, Z = sk.query(Q)
+    err = max(err, relmax(Z, Zb), absmax(o, Nb / Zb[:, None]))
+    return err
+
+
+def pin_sym_equals_direct(impl, K, V, Q, p, chunk=64):
+    """S3: the multiset route answers as the plain definition sum_i T_p(<q, k_i>)."""
+    d, dv = K.shape[1], V.shape[1]
+    sk = impl.SymMomentSketch(d, dv, p).update(K, V, chunk=chunk)
+    o, Z = sk.query(Q)
+    od, Zd = impl.sketch_direct(K, V, Q, p)
+    return max(relmax(Z, Zd), absmax(o, od))
+
+
+def pin_sym_expand(impl, d, p, n=17, dv=3, seed=23):
+    """S4: the stored entries, spread back to every index tuple, equal the
+    Kronecker-layout moments built here with np.kron."""
+    K, V, _ = _small(seed + d + p, n, 1, d, dv)
+    sk = impl.SymMomentSketch(d, dv, p).update(K, V, chunk=5)
+    full = sk.expand_full()
+    blocks = []
+    for j in range(p + 1):
+        F = np.stack([kron_power(K[i], j) for i in range(n)])
+        blocks.append(np.concatenate([F.sum(axis=0)[:, None], F.T @ V], axis=1))
+    ref = np.concatenate(blocks, axis=0)
+    return float(np.max(np.abs(full - ref) / np.maximum(np.abs(ref), 1.0)))
+
+
+def pin_sym_merge(impl, p=3, d=3, dv=2, seed=24):
+    """S5: merge(sketch(A), sketch(B)) == sketch(A u B)."""
+    K, V, Q = _small(seed, 40, 5, d, dv)
+    a = impl.SymMomentSketch(d, dv, p).update(K[:15], V[:15])
+    b = impl.SymMomentSketch(d, dv, p).update(K[15:], V[15:])
+    ab = impl.SymMomentSketch(d, dv, p).update(K, V)
+    a.merge(b)
+    S1, S2 = a.canonical_state(), ab.canonical_state()
+    err = float(np.max(np.abs(S1 - S2) / np.maximum(np.abs(S2), 1.0)))
+    return max(err, abs(a.count - ab.count))

@@ -151,3 +151,102 @@ def test_unmutated_passes_all_pins():
 def test_mutant_is_caught(name):
     with np.errstate(all="ignore"):
         assert _all_pins(MUTANTS[name]) > 1e-6, f"mutant {name} survived every pin"
+
+
+# Multiset storage mutants ------------------------------------------------------------
+
+from oracle import sym as osym
+
+
+def _sym_impl(**over):
+    base = dict(SymMomentSketch=oracle.SymMomentSketch, multisets=oracle.multisets,
+                alpha_factorial=oracle.alpha_factorial, sketch_direct=oracle.sketch_direct)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+class SymJFactorial(oracle.SymMomentSketch):
+    """Weights every entry of level j by 1/j! instead of 1/alpha!."""
+
+    def __init__(self, d, dv, p):
+        super().__init__(d, dv, p)
+        self.weights = [np.full(len(t), 1.0 / math.factorial(j))
+                        for j, t in enumerate(self.tuples)]
+
+
+class SymDroppedTop(oracle.SymMomentSketch):
+    """Answers without the degree-p level."""
+
+    def query(self, Q):
+        Q = np.asarray(Q, dtype=np.float64)
+        Z = np.zeros(Q.shape[0])
+        Nt = np.zeros((Q.shape[0], self.dv))
+        for j, F in enumerate(osym.sym_features(Q, self.p)[:-1]):
+            Fw = F * self.weights[j][None, :]
+            Z += Fw @ self.M[j]
+            Nt += Fw @ self.N[j]
+        return Nt / Z[:, None], Z
+
+
+class SymReversedRows(oracle.SymMomentSketch):
+    """Lists each level's rows in reverse lexicographic order."""
+
+    def canonical_state(self):
+        import numpy as _np
+        return _np.concatenate(
+            [_np.concatenate([self.M[j][::-1, None], self.N[j][::-1]], axis=1)
+             for j in range(self.p + 1)], axis=0)
+
+
+def _no_replacement(d, j):
+    import itertools
+    rows = list(itertools.combinations(range(d), j))
+    return np.array(rows, dtype=np.int64).reshape(len(rows), j)
+
+
+def _alpha_fact_counts_distinct(tuples):
+    """Takes alpha! as (number of distinct indices)!."""
+    return np.array([float(math.factorial(len(set(r)))) for r in tuples])
+
+
+class SymLastChunkOnly(oracle.SymMomentSketch):
+    def update(self, K, V, chunk=256):
+        K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64)
+        for c0 in range(0, K.shape[0], chunk):
+            for j, F in enumerate(osym.sym_features(K[c0:c0 + chunk], self.p)):
+                self.M[j] = F.sum(axis=0)
+                self.N[j] = F.T @ V[c0:c0 + chunk]
+        self.count += K.shape[0]
+        return self
+
+
+def _sym_pins(impl):
+    errs = [pins.pin_sym_counts(impl, 3, 4), pins.pin_sym_counts(impl, 4, 3),
+            pins.pin_sym_bruteforce(impl, 3, 3), pins.pin_sym_bruteforce(impl, 2, 4),
+            pins.pin_sym_expand(impl, 3, 3), pins.pin_sym_merge(impl)]
+    K, V, Q = pins._small(99, 60, 6, 4, 3)
+    errs.append(pins.pin_sym_equals_direct(impl, K, V, Q, 3, chunk=16))
+    return max(errs)
+
+
+@pytest.mark.parametrize("impl", [
+    _sym_impl(SymMomentSketch=SymJFactorial),
+    _sym_impl(SymMomentSketch=SymDroppedTop),
+    _sym_impl(SymMomentSketch=SymReversedRows),
+    _sym_impl(multisets=_no_replacement),
+    _sym_impl(alpha_factorial=_alpha_fact_counts_distinct),
+    _sym_impl(SymMomentSketch=SymLastChunkOnly),
+], ids=["j_factorial", "dropped_top", "reversed_rows", "no_replacement",
+        "alpha_fact_distinct", "last_chunk_only"])
+def test_sym_mutant_caught(impl):
+    with np.errstate(all="ignore"):
+        try:
+            err = _sym_pins(impl)
+        except (AssertionError, KeyError, ValueError, IndexError):
+            return
+    assert not err < 1e-9, "mutant survived every multiset pin"
+
+
+def test_sym_pins_pass_on_oracle():
+    assert _sym_pins(_sym_impl()) < 1e-11
