@@ -8,12 +8,13 @@ Estritos para Atenção em Streaming" (gist.science, pt), sections "Definição 
 Problema" and "Metodologia" (pillar "O Método Polinomial", Merge-and-Reduce).
 """
 
-from ._binding import (LIB_PATH, EXPORTED, Sketch, SketchError, sketch_create,
-                       sketch_destroy, sketch_reset, sketch_update, sketch_merge,
+from ._binding import (LIB_PATH, EXPORTED, LAYOUTS, Sketch, SketchError, sketch_create,
+                       sketch_layout, sketch_destroy, sketch_reset, sketch_update, sketch_merge,
                        sketch_query, sketch_export, sketch_state, sketch_timing,
                        sketch_kernel_times, exact_attend, raw)
 
-__all__ = ["LIB_PATH", "EXPORTED", "Sketch", "SketchError", "sketch_create",
+__all__ = ["LIB_PATH", "EXPORTED", "LAYOUTS", "Sketch", "SketchError", "sketch_create",
+           "sketch_layout",
            "sketch_destroy", "sketch_reset", "sketch_update", "sketch_merge",
            "sketch_query", "sketch_export", "sketch_state", "sketch_timing",
            "sketch_kernel_times", "exact_attend", "raw"]

@@ -15,8 +15,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libexpsketch.so")
 
 SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
+LAYOUTS = {"full": 0, "sym": 1}
 
-EXPORTED = ("sketch_create", "sketch_destroy", "sketch_set_stream", "sketch_reset",
+EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy", "sketch_set_stream", "sketch_reset",
             "sketch_update", "sketch_merge", "sketch_query", "exact_attend",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
@@ -43,6 +44,9 @@ def _lib():
         c_int, c_i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         sig = {
             "sketch_create": (c_int, [c_int, c_int, c_int, c_int, vp, ctypes.POINTER(vp)]),
+            "sketch_create_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, vp,
+                                         ctypes.POINTER(vp)]),
+            "sketch_layout": (c_int, [vp, ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
             "sketch_destroy": (c_int, [vp]),
             "sketch_set_stream": (c_int, [vp, vp]),
             "sketch_reset": (c_int, [vp]),
@@ -100,15 +104,24 @@ def _heads(t, name):
 
 
 class Sketch:
-    """A handle of the C library (sketch_create ... sketch_destroy)."""
+    """A handle of the C library (sketch_create_ex ... sketch_destroy).
 
-    def __init__(self, d, dv, p, h=1):
+    layout "full" keeps every Kronecker index tuple (D = sum_j d^j rows); "sym"
+    keeps one entry per multiset of indices (C(d + p, p) rows, same answers)."""
+
+    def __init__(self, d, dv, p, h=1, layout="full"):
         lib = _lib()
+        if layout not in LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
         handle = ctypes.c_void_p()
-        _check(lib.sketch_create(d, dv, p, h, _stream(), ctypes.byref(handle)),
-               "sketch_create")
+        _check(lib.sketch_create_ex(d, dv, p, h, LAYOUTS[layout], _stream(),
+                                    ctypes.byref(handle)), "sketch_create_ex")
         self._h = handle
         self.d, self.dv, self.p, self.h = d, dv, p, h
+        self.layout = layout
+        rows = ctypes.c_int64()
+        _check(lib.sketch_layout(handle, None, ctypes.byref(rows)), "sketch_layout")
+        self.rows = rows.value
 
     def _handle(self):
         if self._h is None:
@@ -139,8 +152,17 @@ class Sketch:
         return c.value
 
 
-def sketch_create(d, dv, p, h=1):
-    return Sketch(d, dv, p, h)
+def sketch_create(d, dv, p, h=1, layout="full"):
+    return Sketch(d, dv, p, h, layout)
+
+
+def sketch_layout(s):
+    """(layout name, rows of the canonical view)."""
+    lay = ctypes.c_int()
+    rows = ctypes.c_int64()
+    _check(_lib().sketch_layout(s._handle(), ctypes.byref(lay), ctypes.byref(rows)),
+           "sketch_layout")
+    return {v: k for k, v in LAYOUTS.items()}[lay.value], rows.value
 
 
 def sketch_destroy(s):
@@ -184,10 +206,13 @@ def sketch_query(s, Q, out=None, Z=None):
 
 
 def sketch_export(s, dst=None, device=None):
-    """Canonical [M | N] view into a new (or given) tensor [h, D, 1 + dv]."""
+    """Canonical [M | N] view into a new (or given) tensor [h, rows, 1 + dv]
+    (rows = D for the full layout, C(d + p, p) for the multiset layout)."""
     if dst is None:
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-        dst = torch.empty((s.h, s.D, 1 + s.dv), dtype=torch.float32, device=dev)
+        dst = torch.empty((s.h, s.rows, 1 + s.dv), dtype=torch.float32, device=dev)
+    elif tuple(dst.shape) != (s.h, s.rows, 1 + s.dv):
+        raise ValueError(f"dst must be [{s.h}, {s.rows}, {1 + s.dv}]")
     _check(_lib().sketch_export(s._handle(), _dev(dst, "dst", 3)), "sketch_export")
     return dst
 

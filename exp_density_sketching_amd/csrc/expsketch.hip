@@ -16,6 +16,7 @@
 #include "sk_elementwise.h"
 #include "sk_exact.h"
 #include "sk_query.h"
+#include "sk_sym.h"
 #include "sk_update.h"
 
 namespace {
@@ -92,6 +93,27 @@ size_t query_lds_bytes(int d) {
   return sizeof(float) * ((size_t)d * (SK_TMQ + 1) + std::max(ab, ys));
 }
 
+size_t sym_update_lds_bytes(int d, int dv) {
+  // Ks (+ ones and zeros rows) + Vs, prefix products, slot codes
+  return sizeof(float) * ((size_t)(d + 2 + dv) * (SY_KB + 1) + (size_t)SY_KB * SY_LDP) +
+         sizeof(unsigned long long) * SY_NS;
+}
+size_t sym_query_lds_bytes(int d) {
+  // Qs + At + Bt (widest column tile, 128 columns: row stride 144) + row codes
+  return sizeof(float) * ((size_t)d * (SY_TQ + 1) + (size_t)SY_QKB * (SY_TQ + 16) +
+                          (size_t)SY_QKB * 144) +
+         sizeof(unsigned long long) * SY_QKB;
+}
+// state rows per range of the multiset query (EXPSKETCH_SYM_QUERY_ROWS overrides)
+int sym_query_rows() {
+  static const int v = [] {
+    const char* e = std::getenv("EXPSKETCH_SYM_QUERY_ROWS");
+    const int r = e ? std::atoi(e) : 0;
+    return r >= SY_QKB ? r / SY_QKB * SY_QKB : 128;
+  }();
+  return v;
+}
+
 // The query kernel is instantiated per log2(d) (d = 4 .. 128).
 using QueryKernel = void (*)(const float*, long long, const float*, long long,
                              const QryTile*, int, int, long long, float*);
@@ -130,6 +152,15 @@ struct sk_sketch {
   int trec[2] = {0, 0};     // pairs recorded per kind
   size_t view_bytes = 0;
   DeviceInfo dev;
+  // multiset layout (SK_LAYOUT_SYM)
+  int layout = SK_LAYOUT_FULL;
+  long long Dsym = 0, Rlo = 0, Rtop = 0;   // canonical rows; lower and top block rows
+  void* symbuf = nullptr;                  // device tables (one allocation)
+  SymTables tb{};
+  std::vector<SymUpdTile> sutiles;
+  std::vector<SymQryTile> sqtiles;
+  SymUpdTile* d_sutiles = nullptr;
+  SymQryTile* d_sqtiles = nullptr;
 };
 
 namespace {
@@ -224,6 +255,161 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
   }
 }
 
+// Multiset layout: canonical tables, update row tiles (with their prefix slots)
+// and query row ranges.  Level j is generated from level j - 1 in order: for each
+// multiset beta of size j - 1, beta + {e} for e from the largest index of beta
+// (0 for the empty multiset) to d - 1.  That is lexicographic order of the sorted
+// tuples, and it gives the prefix, the multiplicity of the largest index and
+// 1/alpha! = (1/beta!) / (multiplicity of e in beta + 1) on the way.
+struct SymHost {
+  std::vector<unsigned long long> code;
+  std::vector<int> prefix, last, lmul, rslot, slots;
+  std::vector<float> winv;
+};
+
+void sym_tables(int d, int p, SymHost* t, long long* Rlo) {
+  std::vector<double> wv;
+  t->code.push_back(0ull);
+  t->prefix.push_back(-1);
+  t->last.push_back(d);
+  t->lmul.push_back(0);
+  wv.push_back(1.0);
+  long long b0 = 0, b1 = 1;
+  *Rlo = p > 0 ? 1 : 0;
+  for (int j = 1; j <= p; ++j) {
+    for (long long b = b0; b < b1; ++b) {
+      const int lb = (j == 1) ? 0 : t->last[b];
+      for (int e = lb; e < d; ++e) {
+        const int mult = (j > 1 && e == t->last[b]) ? t->lmul[b] : 0;
+        const unsigned long long base = t->code[b] & 0x00ffffffffffffffull;
+        t->code.push_back(base | ((unsigned long long)e << (8 * (j - 1))) |
+                          ((unsigned long long)j << 56));
+        t->prefix.push_back((int)b);
+        t->last.push_back(e);
+        t->lmul.push_back(mult + 1);
+        wv.push_back(wv[b] / (double)(mult + 1));
+      }
+    }
+    b0 = b1;
+    b1 = (long long)t->code.size();
+    if (j < p) *Rlo = b1;
+  }
+  t->winv.assign(wv.begin(), wv.end());
+  t->rslot.assign(t->code.size(), 0);
+}
+
+// Update tiles of one block: row tiles of at most TM rows and SY_NS prefix slots
+// (rows with one prefix are consecutive), each cut into column tiles.
+void plan_sym_update_block(sk_sketch* s, SymHost* t, long long xoff, int rc0, int nrows,
+                           int C, int top) {
+  const int cb = C <= 16 ? 1 : (C <= 32 ? 2 : 4);
+  const int TM = 64 * (16 / cb), TN = 16 * cb;
+  int r = 0;
+  while (r < nrows) {
+    const int row0 = r, slot0 = (int)t->slots.size();
+    int ns = 0, cnt = 0, lastpid = 0;
+    while (r < nrows && cnt < TM) {
+      const int cid = rc0 + r;
+      const int pid = t->prefix[cid];
+      if (ns == 0 || pid != lastpid) {
+        if (ns == SY_NS) break;
+        t->slots.push_back(pid);
+        ++ns;
+        lastpid = pid;
+      }
+      t->rslot[cid] = ns - 1;
+      ++r;
+      ++cnt;
+    }
+    for (int col0 = 0; col0 < C; col0 += TN) {
+      SymUpdTile u{};
+      u.xoff = xoff;
+      u.rc0 = rc0;
+      u.row0 = row0;
+      u.nrows = cnt;
+      u.col0 = col0;
+      u.C = C;
+      u.top = top;
+      u.slot0 = slot0;
+      u.nslots = ns;
+      u.cb = cb;
+      s->sutiles.push_back(u);
+    }
+  }
+}
+
+// Query ranges of one block: one [SY_TQ][C] partial per range of sym_query_rows()
+// rows, filled by the range's column tiles.
+void plan_sym_query_block(sk_sketch* s, long long xoff, int rc0, int nrows, int C, int top) {
+  const int cb = C <= 16 ? 1 : (C <= 32 ? 2 : (C <= 64 ? 4 : 8));
+  const int TN = 16 * cb;
+  for (int r0 = 0; r0 < nrows; r0 += sym_query_rows()) {
+    QryTile f{};
+    f.pofs = s->qpb;
+    f.C = C;
+    f.top = top;
+    s->qtiles.push_back(f);
+    for (int col0 = 0; col0 < C; col0 += TN) {
+      SymQryTile q{};
+      q.xoff = xoff;
+      q.pofs = s->qpb;
+      q.rc0 = rc0;
+      q.row0 = r0;
+      q.nrows = std::min(sym_query_rows(), nrows - r0);
+      q.col0 = col0;
+      q.C = C;
+      q.top = top;
+      q.cb = cb;
+      s->sqtiles.push_back(q);
+    }
+    s->qpb += (long long)SY_TQ * C;
+  }
+}
+
+// Builds the multiset layout's plans and device tables of a new handle.
+int build_sym(sk_sketch* s) {
+  SymHost t;
+  sym_tables(s->d, s->p, &t, &s->Rlo);
+  s->Dsym = (long long)t.code.size();
+  s->Rtop = s->Dsym - s->Rlo;
+  const int Cl = s->d + s->dv;
+  s->XS = s->Rlo * Cl + s->Rtop * s->dv;
+  if (s->Rlo > 0) plan_sym_update_block(s, &t, 0, 0, (int)s->Rlo, Cl, 0);
+  plan_sym_update_block(s, &t, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
+  if (s->Rlo > 0) plan_sym_query_block(s, 0, 0, (int)s->Rlo, Cl, 0);
+  plan_sym_query_block(s, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
+  // one device allocation: code | prefix | last | lmul | rslot | winv | slots
+  const size_t n = (size_t)s->Dsym, ns = t.slots.size();
+  const size_t bytes = 8 * n + 4 * (5 * n + ns) + 64;
+  if (hipMalloc(&s->symbuf, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return SK_ENOMEM;
+  }
+  char* base = static_cast<char*>(s->symbuf);
+  size_t off = 0;
+  auto put = [&](const void* src, size_t sz) -> void* {
+    void* dst = base + off;
+    off += (sz + 7) / 8 * 8;
+    if (sz > 0 && hipMemcpy(dst, src, sz, hipMemcpyHostToDevice) != hipSuccess) return nullptr;
+    return dst;
+  };
+  s->tb.code = static_cast<const unsigned long long*>(put(t.code.data(), 8 * n));
+  s->tb.prefix = static_cast<const int*>(put(t.prefix.data(), 4 * n));
+  s->tb.last = static_cast<const int*>(put(t.last.data(), 4 * n));
+  s->tb.lmul = static_cast<const int*>(put(t.lmul.data(), 4 * n));
+  s->tb.rslot = static_cast<const int*>(put(t.rslot.data(), 4 * n));
+  s->tb.winv = static_cast<const float*>(put(t.winv.data(), 4 * n));
+  s->tb.slots = static_cast<const int*>(put(t.slots.data(), 4 * ns));
+  if (!s->tb.code || !s->tb.prefix || !s->tb.last || !s->tb.lmul || !s->tb.rslot ||
+      !s->tb.winv || !s->tb.slots)
+    return SK_EHIP;
+  return SK_OK;
+}
+
+int update_tile_count(const sk_sketch* s) {
+  return (int)(s->layout == SK_LAYOUT_SYM ? s->sutiles.size() : s->utiles.size());
+}
+
 int choose_update_splits(const sk_sketch* s, long long n) {
   // EXPSKETCH_UPDATE_SPLITS=<k> fixes the number of key splits (tuning aid).
   static const int forced = [] {
@@ -231,9 +417,11 @@ int choose_update_splits(const sk_sketch* s, long long n) {
     return v ? std::max(0, std::atoi(v)) : 0;
   }();
   if (forced > 0) return (int)std::max(1LL, std::min<long long>(forced, (n + SK_KB - 1) / SK_KB));
-  const long long base = (long long)s->utiles.size() * s->h;
+  const long long base = (long long)update_tile_count(s) * s->h;
   const long long slots = 2LL * std::max(1, s->dev.num_cu);
-  const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
+  // at least 256 keys (multiset layout: 128) per split
+  const long long minkeys = s->layout == SK_LAYOUT_SYM ? 128 : 256;
+  const long long max_ns = std::max(1LL, std::min(64LL, n / minkeys));
   int best = 1;
   double best_score = -1.0;
   for (long long ns = 1; ns <= max_ns; ++ns) {
@@ -263,7 +451,7 @@ int launch_fill_zero(float* p, long long count, hipStream_t st) {
 
 extern "C" {
 
-int sk_version(void) { return 100; }
+int sk_version(void) { return 101; }
 
 const char* sk_strerror(int code) {
   switch (code) {
@@ -276,22 +464,32 @@ const char* sk_strerror(int code) {
   }
 }
 
-int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out) {
+int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
+                     sk_handle* out) {
   if (out == nullptr) return SK_EINVAL;
   *out = nullptr;
   if (!is_pow2_in(d, 4, 128) || !is_pow2_in(dv, 4, 128) || p < 0 || p > kMaxP || h < 1)
     return SK_EINVAL;
+  if (layout != SK_LAYOUT_FULL && layout != SK_LAYOUT_SYM) return SK_EINVAL;
+  if (layout == SK_LAYOUT_SYM && p > SY_MAXP) return SK_EINVAL;
   // sizes, with overflow checks in floating point first
-  double XSd = 0.0;
+  double XSd = 0.0, rowsd = 0.0;
   for (int j = 0; j <= p; ++j) {
-    const double r = std::pow((double)d, j);
+    double r = std::pow((double)d, j);
+    if (layout == SK_LAYOUT_SYM) {            // C(d + j - 1, j)
+      r = 1.0;
+      for (int i = 1; i <= j; ++i) r = r * (double)(d + i - 1) / (double)i;
+    }
     XSd += r * (double)(j < p ? d + dv : dv);
+    rowsd += r;
   }
   if (XSd * (double)h * 4.0 > 1.0e15) return SK_ENOMEM;
+  if (layout == SK_LAYOUT_SYM && rowsd > 2.0e8) return SK_ENOMEM;   // int row ids, tables
 
   sk_sketch* s = new (std::nothrow) sk_sketch();
   if (s == nullptr) return SK_ENOMEM;
   s->d = d; s->dv = dv; s->p = p; s->h = h; s->logd = ilog2(d);
+  s->layout = layout;
   s->stream = reinterpret_cast<hipStream_t>(hip_stream);
   int rc = current_device(&s->device);
   if (rc == SK_OK) rc = device_info(s->device, &s->dev);
@@ -307,43 +505,73 @@ int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out)
   }
   s->D = D;
   s->XS = off;   // a multiple of 4: every term is
-  if (update_lds_bytes(d, dv) > (size_t)s->dev.max_lds ||
-      query_lds_bytes(d) > (size_t)s->dev.max_lds) {
+  const bool sym = layout == SK_LAYOUT_SYM;
+  const size_t ul = sym ? sym_update_lds_bytes(d, dv) : update_lds_bytes(d, dv);
+  const size_t ql = sym ? sym_query_lds_bytes(d) : query_lds_bytes(d);
+  if (ul > (size_t)s->dev.max_lds || ql > (size_t)s->dev.max_lds) {
     delete s;
     return SK_EINVAL;
   }
-  for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
-
-  for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
+  if (sym) {
+    rc = build_sym(s);   // sets XS, the sym tiles, the finishing records and tables
+    if (rc != SK_OK) {
+      (void)hipFree(s->symbuf);
+      delete s;
+      return rc;
+    }
+  } else {
+    for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
+    for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
+  }
 
   const size_t state_bytes = sizeof(float) * (size_t)s->XS * (size_t)h;
   if (hipMalloc(&s->state, state_bytes) != hipSuccess) {
     (void)hipGetLastError();
+    (void)hipFree(s->symbuf);
     delete s;
     return SK_ENOMEM;
   }
-  bool ok = hipMalloc(&s->d_utiles, sizeof(UpdTile) * s->utiles.size()) == hipSuccess &&
-            hipMalloc(&s->d_qtiles, sizeof(QryTile) * s->qtiles.size()) == hipSuccess;
-  if (ok)
-    ok = hipMemcpy(s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size(),
-                   hipMemcpyHostToDevice) == hipSuccess &&
-         hipMemcpy(s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size(),
-                   hipMemcpyHostToDevice) == hipSuccess;
-  if (ok) {
-    const size_t ul = update_lds_bytes(d, dv), ql = query_lds_bytes(d);
-    ok = hipFuncSetAttribute((const void*)sk_update_kernel,
+  auto upload = [](void** dst, const void* src, size_t bytes) {
+    if (bytes == 0) return true;
+    return hipMalloc(dst, bytes) == hipSuccess &&
+           hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice) == hipSuccess;
+  };
+  bool ok = upload((void**)&s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size());
+  if (ok && sym)
+    ok = upload((void**)&s->d_sutiles, s->sutiles.data(),
+                sizeof(SymUpdTile) * s->sutiles.size()) &&
+         upload((void**)&s->d_sqtiles, s->sqtiles.data(),
+                sizeof(SymQryTile) * s->sqtiles.size()) &&
+         hipFuncSetAttribute((const void*)sk_sym_update_kernel,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
+         hipFuncSetAttribute((const void*)sk_sym_query_kernel,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
+  if (ok && !sym)
+    ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
+         hipFuncSetAttribute((const void*)sk_update_kernel,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
          hipFuncSetAttribute((const void*)query_kernel_for(s->logd),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
-  }
   if (ok) ok = launch_fill_zero(s->state, s->XS * h, s->stream) == SK_OK;
   if (!ok) {
     (void)hipGetLastError();
     (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
+    (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
     delete s;
     return SK_EHIP;
   }
   *out = s;
+  return SK_OK;
+}
+
+int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out) {
+  return sketch_create_ex(d, dv, p, h, SK_LAYOUT_FULL, hip_stream, out);
+}
+
+int sketch_layout(sk_handle s, int* layout, int64_t* rows) {
+  if (s == nullptr) return SK_EINVAL;
+  if (layout) *layout = s->layout;
+  if (rows) *rows = s->layout == SK_LAYOUT_SYM ? s->Dsym : s->D;
   return SK_OK;
 }
 
@@ -354,6 +582,9 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->state);
   (void)hipFree(s->d_utiles);
   (void)hipFree(s->d_qtiles);
+  (void)hipFree(s->d_sutiles);
+  (void)hipFree(s->d_sqtiles);
+  (void)hipFree(s->symbuf);
   (void)hipFree(s->view);
   for (int k = 0; k < 2; ++k)
     for (int w = 0; w < 2; ++w)
@@ -393,9 +624,10 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   long long kps = (n + ns - 1) / ns;
   kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
   const int nsplit = (int)((n + kps - 1) / kps);
-  const int ntiles = (int)s->utiles.size();
+  const bool sym = s->layout == SK_LAYOUT_SYM;
+  const int ntiles = update_tile_count(s);
   if ((long long)ntiles * nsplit * s->h > 0x7fffffffLL) return SK_EINVAL;
-  const size_t lds = update_lds_bytes(s->d, s->dv);
+  const size_t lds = sym ? sym_update_lds_bytes(s->d, s->dv) : update_lds_bytes(s->d, s->dv);
   const long long total = s->XS * s->h;
   float* parts = nullptr;
   if (nsplit > 1 &&
@@ -409,9 +641,15 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const int acc = nsplit > 1 ? 0 : 1;
   hipError_t err = hipSuccess;
   timing_mark(s, 0, false);
-  hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
-                     dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
-                     s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc);
+  if (sym)
+    hipLaunchKernelGGL(sk_sym_update_kernel,
+                       dim3((unsigned)((long long)ntiles * nsplit * s->h)), dim3(SK_WG), lds,
+                       s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles, ntiles,
+                       s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc);
+  else
+    hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
+                       dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
+                       s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc);
   err = hipGetLastError();
   timing_mark(s, 0, true);
   if (nsplit > 1) {
@@ -431,7 +669,8 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
 
 int sketch_merge(sk_handle dst, sk_handle src) {
   if (dst == nullptr || src == nullptr || dst == src) return SK_EINVAL;
-  if (dst->d != src->d || dst->dv != src->dv || dst->p != src->p || dst->h != src->h)
+  if (dst->d != src->d || dst->dv != src->dv || dst->p != src->p || dst->h != src->h ||
+      dst->layout != src->layout)
     return SK_EMISMATCH;
   const long long c4 = dst->XS * dst->h / 4;
   const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
@@ -449,7 +688,9 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
   const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
-  if (nqt * std::max<long long>(ntiles, SK_TMQ) * s->h > 0x7fffffffLL) return SK_EINVAL;
+  const long long nlaunch = std::max<long long>(
+      SK_TMQ, std::max<long long>(ntiles, (long long)s->sqtiles.size()));
+  if (nqt * nlaunch * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
   float* parts = nullptr;
   if (hipMallocAsync((void**)&parts, pbytes, s->stream) != hipSuccess) {
@@ -457,9 +698,16 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     return SK_ENOMEM;
   }
   timing_mark(s, 1, false);
-  hipLaunchKernelGGL(query_kernel_for(s->logd), dim3((unsigned)(ntiles * nqt * s->h)),
-                     dim3(SK_WG), query_lds_bytes(s->d), s->stream, Q, (long long)m,
-                     s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
+  if (s->layout == SK_LAYOUT_SYM) {
+    const long long nst = (long long)s->sqtiles.size();
+    hipLaunchKernelGGL(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
+                       sym_query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->state,
+                       s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, s->qpb, parts);
+  } else {
+    hipLaunchKernelGGL(query_kernel_for(s->logd), dim3((unsigned)(ntiles * nqt * s->h)),
+                       dim3(SK_WG), query_lds_bytes(s->d), s->stream, Q, (long long)m,
+                       s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
+  }
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 1, true);
   // queries per finishing workgroup: a power of two with qg * (d + dv) <= 256
@@ -505,6 +753,14 @@ int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count) {
 
 int sketch_export(sk_handle s, float* dst) {
   if (s == nullptr || dst == nullptr || !aligned16(dst)) return SK_EINVAL;
+  if (s->layout == SK_LAYOUT_SYM) {
+    const long long total = s->Dsym * (1 + s->dv) * s->h;
+    const int grid = (int)std::min<long long>((total + 255) / 256, 16384);
+    hipLaunchKernelGGL(sk_sym_export_kernel, dim3(grid), dim3(256), 0, s->stream, s->state,
+                       s->XS, s->tb, s->Dsym, s->Rlo, s->d, s->dv, (float)s->count, dst, total);
+    SK_TRY(hipGetLastError());
+    return SK_OK;
+  }
   const long long total = s->D * (1 + s->dv) * s->h;
   LevelTable lt{};
   lt.p = s->p;
@@ -526,7 +782,8 @@ int sketch_export(sk_handle s, float* dst) {
 int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* cols,
                  int64_t* count) {
   if (s == nullptr) return SK_EINVAL;
-  const size_t bytes = sizeof(float) * (size_t)(s->D * (1 + s->dv) * s->h);
+  const long long vrows = s->layout == SK_LAYOUT_SYM ? s->Dsym : s->D;
+  const size_t bytes = sizeof(float) * (size_t)(vrows * (1 + s->dv) * s->h);
   if (s->view_bytes < bytes) {
     SK_TRY(hipStreamSynchronize(s->stream));
     (void)hipFree(s->view);
@@ -542,7 +799,7 @@ int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* col
   if (rc != SK_OK) return rc;
   SK_TRY(hipStreamSynchronize(s->stream));
   if (dev_state) *dev_state = s->view;
-  if (rows_D) *rows_D = s->D;
+  if (rows_D) *rows_D = vrows;
   if (cols) *cols = 1 + s->dv;
   if (count) *count = s->count;
   return SK_OK;

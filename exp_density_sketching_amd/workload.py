@@ -11,16 +11,17 @@ Estritos para Atenção em Streaming", "Metodologia", closing paragraph).
 from . import _binding as B
 
 
-def ingest(w, K, V, sketches=None):
+def ingest(w, K, V, sketches=None, layout="full"):
     """Ingest K [h, n, d], V [h, n, dv] per the workload's protocol.
 
-    ``sketches``: optional list of S pre-created (and reset) Sketch handles.
-    Returns the sketch holding the whole stream (sketch 0).
+    ``sketches``: optional list of S pre-created (and reset) Sketch handles;
+    otherwise S new ones of the given storage ``layout`` ("full" or "sym").
+    Returns the sketch holding the whole stream (sketch 0) and the list.
     """
     S = max(1, w.substreams)
     n = K.shape[1]
     if sketches is None:
-        sketches = [B.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
+        sketches = [B.sketch_create(w.d, w.dv, w.p, w.h, layout) for _ in range(S)]
     bounds = [n * i // S for i in range(S + 1)]
     for i in range(S):
         lo, hi = bounds[i], bounds[i + 1]
@@ -33,8 +34,8 @@ def ingest(w, K, V, sketches=None):
     return sketches[0], sketches
 
 
-def run_sketch(w, K, V, Q):
+def run_sketch(w, K, V, Q, layout="full"):
     """Whole sketch path of a workload: (ohat [h, m, dv], Zhat [h, m], sketch)."""
-    sk, _ = ingest(w, K, V)
+    sk, _ = ingest(w, K, V, layout=layout)
     out, Z = B.sketch_query(sk, Q)
     return out, Z, sk

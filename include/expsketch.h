@@ -23,7 +23,8 @@
  *     pointers (hipMalloc / torch CUDA tensors), owned by the caller.
  *   - h independent heads are laid out head-major: K [h][n][d], V [h][n][dv],
  *     Q [h][m][d], out [h][m][dv], Z [h][m].
- *   - Supported shapes: d and dv are powers of two in [4, 128]; 0 <= p <= 16;
+ *   - Supported shapes: d and dv are powers of two in [4, 128]; 0 <= p <= 16
+ *     (p <= 7 in the multiset layout);
  *     h >= 1; the state (about h * D * (1+dv) floats, D = sum_{j<=p} d^j) must fit
  *     in device memory.  Anything else returns SK_EINVAL (shape) or SK_ENOMEM.
  *   - Calls are asynchronous on the HIP stream they are given (the handle's
@@ -50,6 +51,10 @@ extern "C" {
 
 typedef struct sk_sketch* sk_handle;  /* opaque; owned by the library */
 
+/* Storage layouts of the moments (sketch_create_ex). */
+#define SK_LAYOUT_FULL 0  /* every tensor index tuple: D = sum_{j<=p} d^j rows */
+#define SK_LAYOUT_SYM  1  /* one row per multiset of indices: C(d + p, p) rows */
+
 /*
  * sketch_create -- an empty sketch of degree p for h heads of key dimension d and
  * value dimension dv ("O Método Polinomial": the moment summary).
@@ -60,6 +65,33 @@ typedef struct sk_sketch* sk_handle;  /* opaque; owned by the library */
  * does not fit; SK_EHIP if a HIP call fails.  On error *out is set to NULL.
  */
 int sketch_create(int d, int dv, int p, int h, void* hip_stream, sk_handle* out);
+
+/*
+ * sketch_create_ex -- sketch_create with a choice of storage layout.
+ *   layout == SK_LAYOUT_FULL: as sketch_create.
+ *   layout == SK_LAYOUT_SYM: the moment tensors are symmetric in their j indices
+ *     (M_j[a_1..a_j] depends only on the multiset {a_1..a_j}), so one entry per
+ *     multiset alpha is kept: M^s[alpha] = sum_i k_i^alpha, N^s[alpha] =
+ *     sum_i k_i^alpha v_i, k^alpha = prod_l k[a_l].  Each entry stands for
+ *     j!/alpha! index tuples (alpha! = product of the factorials of the
+ *     multiplicities), so the answers are the same values as the full layout's:
+ *         Zhat(q) = sum_alpha q^alpha M^s[alpha] / alpha!,  Ntilde likewise.
+ *     C(d + p, p) rows instead of sum_j d^j ("O Método Polinomial": the pages
+ *     keep the low-degree moments and leave their storage open).  Requires
+ *     p <= 7.
+ * Errors: as sketch_create; SK_EINVAL also for an unknown layout or p > 7 with
+ * SK_LAYOUT_SYM.
+ */
+int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
+                     sk_handle* out);
+
+/*
+ * sketch_layout -- the handle's layout (SK_LAYOUT_FULL or SK_LAYOUT_SYM) and the
+ * number of rows of its canonical view (sketch_state, sketch_export): D for the
+ * full layout, C(d + p, p) for the multiset layout.  Either pointer may be NULL.
+ * Errors: SK_EINVAL (NULL handle).
+ */
+int sketch_layout(sk_handle s, int* layout, int64_t* rows);
 
 /* sketch_destroy -- synchronises the handle's stream, frees everything the
  * handle owns.  NULL is accepted (no-op).  Returns SK_EHIP if a pending kernel
@@ -86,7 +118,8 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n);
 
 /*
  * sketch_merge -- dst += src (Merge-and-Reduce, merge step: moments add, counts
- * add).  src is unchanged.  Both handles must have equal (d, dv, p, h); the work
+ * add).  src is unchanged.  Both handles must have equal (d, dv, p, h) and the
+ * same layout; the work
  * runs on dst's stream (the caller orders src's stream before it).
  * Errors: SK_EINVAL (NULL, dst == src), SK_EMISMATCH, SK_EHIP.
  */
@@ -123,9 +156,14 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
  * [M | N]: per head an array [D][1 + dv], rows stacked by level j = 0..p, level j
  * holding d^j rows in row-major Kronecker order (row a*d + b of level j is row a
  * of level j-1 times k[b]); column 0 is M_j, columns 1..dv are N_j; row 0 column
- * 0 is the count.  The view is materialised on the handle's stream into a
- * library-owned device buffer [h][D][1+dv], then the stream is synchronised;
- * it stays valid until the next call on the handle.  Any output pointer may be NULL.
+ * 0 is the count.  For a handle of layout SK_LAYOUT_SYM the view is the
+ * multiset entries instead: rows_D = C(d + p, p) rows, the multisets of size
+ * j = 0..p stacked by size, each size in lexicographic order of the sorted index
+ * tuples (a_1 <= ... <= a_j); column 0 is M^s, columns 1..dv are N^s (raw
+ * moments, without the 1/alpha! query weights).  The view is materialised on the
+ * handle's stream into a library-owned device buffer [h][rows_D][1+dv], then the
+ * stream is synchronised; it stays valid until the next call on the handle.  Any
+ * output pointer may be NULL.
  * Errors: SK_EINVAL (NULL handle), SK_ENOMEM, SK_EHIP.
  */
 int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* cols,
@@ -133,7 +171,8 @@ int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* col
 
 /*
  * sketch_export -- the same canonical [M | N] view as sketch_state, written into
- * caller-owned device memory dst [h][D][1 + dv] (fp32, 16-byte aligned),
+ * caller-owned device memory dst [h][rows][1 + dv] (rows from sketch_layout;
+ * fp32, 16-byte aligned),
  * asynchronously on the handle's stream.
  * Errors: SK_EINVAL (NULL handle or dst, misaligned dst), SK_EHIP.
  */

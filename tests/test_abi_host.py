@@ -73,6 +73,18 @@ def test_create_rejects_null_out_and_huge_state():
     assert out.value is None
 
 
+def test_create_ex_checks_the_layout():
+    lib = _lib()
+    out = ctypes.c_void_p(1234)
+    assert lib.sketch_create_ex(4, 4, 2, 1, 2, None, ctypes.byref(out)) == -1   # layout
+    assert out.value is None
+    assert lib.sketch_create_ex(4, 4, 8, 1, 1, None, ctypes.byref(out)) == -1   # p > 7
+    assert lib.sketch_create_ex(4, 4, 2, 1, -1, None, ctypes.byref(out)) == -1
+    # C(135, 7) ~ 1.6e11 multiset rows: refused before any allocation
+    assert lib.sketch_create_ex(128, 128, 7, 1, 1, None, ctypes.byref(out)) == -2
+    assert out.value is None
+
+
 def test_null_handles_are_rejected():
     lib = _lib()
     assert lib.sketch_destroy(None) == 0
@@ -84,6 +96,7 @@ def test_null_handles_are_rejected():
     assert lib.sketch_state(None, None, None, None, None) == -1
     assert lib.sketch_info(None, None, None, None, None, None, None) == -1
     assert lib.sketch_set_stream(None, None) == -1
+    assert lib.sketch_layout(None, None, None) == -1
 
 
 def test_exact_rejects_bad_arguments():

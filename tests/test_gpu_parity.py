@@ -21,9 +21,9 @@ from tests.gpu_util import (SK_Z_REL, SK_O_ABS, EX_Z_REL, EX_O_ABS, gpu, host, z
 pytestmark = pytest.mark.gpu
 
 
-def _check_sketch(w, K, V, Q, qidx=None, label=""):
+def _check_sketch(w, K, V, Q, qidx=None, label="", layout="full"):
     Kg, Vg, Qg = gpu(K, V, Q)
-    out, Z, sk = run_sketch(w, Kg, Vg, Qg)
+    out, Z, sk = run_sketch(w, Kg, Vg, Qg, layout=layout)
     out, Z = host(out, Z)
     worst_z, worst_o = 0.0, 0.0
     for hd in range(w.h):
@@ -31,7 +31,8 @@ def _check_sketch(w, K, V, Q, qidx=None, label=""):
         o_ref, z_ref = oracle.sketch_direct(K[hd], V[hd], Q[hd][qi], w.p)
         worst_z = max(worst_z, zrel(Z[hd][qi], z_ref))
         worst_o = max(worst_o, oabs(out[hd][qi], o_ref))
-    say(f"{label} sketch: max rel Zhat err {worst_z:.3e}, max abs ohat err {worst_o:.3e}")
+    say(f"{label} sketch ({layout}): max rel Zhat err {worst_z:.3e}, "
+        f"max abs ohat err {worst_o:.3e}")
     assert worst_z <= SK_Z_REL
     assert worst_o <= SK_O_ABS
     sk.destroy()
