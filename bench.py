@@ -14,6 +14,7 @@ oracle timed on a bounded sample on the host cores.
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -33,6 +34,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--layout", choices=["full", "sym"], default="full",
+                    help="storage layout of the sketches in the --counters sequence")
     ap.add_argument("--counters", action="store_true",
                     help="short fixed sequence for rocprofv3 --pmc passes: a 1 GiB "
                          "device copy, one pass of the update calls, 3 decode passes")
@@ -121,7 +124,7 @@ def cpu_baseline(w, K, V, Q, budget):
     }
 
 
-def counters_pass(w, E, torch, generate):
+def counters_pass(w, E, torch, generate, layout="full"):
     """Fixed sequence for counter passes: copy of known size, update, query, decode."""
     from exp_density_sketching_amd.workload import ingest
     nbytes = 1 << 30
@@ -135,7 +138,7 @@ def counters_pass(w, E, torch, generate):
     Kg = torch.from_numpy(K).cuda()
     Vg = torch.from_numpy(V).cuda()
     S = max(1, w.substreams)
-    sketches = [E.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
+    sketches = [E.sketch_create(w.d, w.dv, w.p, w.h, layout) for _ in range(S)]
     ingest(w, Kg, Vg, sketches)
     Qg = torch.from_numpy(Q).cuda()
     for _ in range(3):
@@ -146,7 +149,8 @@ def counters_pass(w, E, torch, generate):
     torch.cuda.synchronize()
     for sk in sketches:
         sk.destroy()
-    print(json.dumps({"counters_pass": w.name, "copy_bytes": nbytes, "copies": 3,
+    print(json.dumps({"counters_pass": w.name, "layout": layout, "copy_bytes": nbytes,
+                      "copies": 3,
                       "update_sources": source_hash("sk_update_kernel"),
                       "decode_sources": source_hash("sk_exact_decode"),
                       "kv_bytes": 4 * w.h * w.n * (w.d + w.dv)}), flush=True)
@@ -170,7 +174,7 @@ def main():
     w = CONFIGS[args.workload]
     torch.cuda.set_device(0)
     if args.counters:
-        return counters_pass(w, E, torch, generate)
+        return counters_pass(w, E, torch, generate, args.layout)
     K, V, Q = generate(w)
     Kg = torch.from_numpy(K).cuda()
     Vg = torch.from_numpy(V).cuda()
@@ -180,54 +184,63 @@ def main():
     out_e = torch.empty_like(out_s)
     z_e = torch.empty_like(z_s)
     S = max(1, w.substreams)
-    sketches = [E.sketch_create(w.d, w.dv, w.p, w.h) for _ in range(S)]
     ev = lambda: torch.cuda.Event(enable_timing=True)
     n_calls = sum(-(-(w.n * (i + 1) // S - w.n * i // S) // (w.chunk or w.n))
                   for i in range(S))
-
-    def step(rec):
-        for sk in sketches:
-            E.sketch_reset(sk)
-        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
-        e0.record()
-        ingest(w, Kg, Vg, sketches)
-        e1.record()
-        E.sketch_query(sketches[0], Qg, out_s, z_s)
-        e2.record()
-        E.exact_attend(Kg, Vg, Qg, out_e, z_e)
-        e3.record()
-        rec.append((e0, e1, e2, e3))
-
-    warm = []
-    for _ in range(args.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-    for sk in sketches:          # library events around the update/query kernels
-        E.sketch_timing(sk, True)
-    rec = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(rec)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_upd = np.mean([a.elapsed_time(b) for a, b, _, _ in rec]) / 1e3
-    t_qry = np.mean([b.elapsed_time(c) for _, b, c, _ in rec]) / 1e3
-    t_ex = np.mean([c.elapsed_time(d) for _, _, c, d in rec]) / 1e3
-    t_step = wall / args.steps
-
-    # dominant kernel: the moment update.  Its launches in the timed steps were
-    # bracketed by HIP events on the library's stream (sketch_timing).
-    upd_ms = [t for sk in sketches for t in E.sketch_kernel_times(sk, "update")]
-    qry_ms = E.sketch_kernel_times(sketches[0], "query")
-    for sk in sketches:
-        E.sketch_timing(sk, False)
-    dur = float(np.mean(upd_ms)) / 1e3
     chunk = w.chunk or -(-w.n // S)
     keys_per_call = float(np.mean([min(chunk, w.n // S - c0)
                                    for c0 in range(0, w.n // S, chunk)]))
+
+    def measure(layout):
+        """Warm-up and timed steps with sketches of the given storage layout."""
+        sketches = [E.sketch_create(w.d, w.dv, w.p, w.h, layout) for _ in range(S)]
+
+        def step(rec):
+            for sk in sketches:
+                E.sketch_reset(sk)
+            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+            e0.record()
+            ingest(w, Kg, Vg, sketches)
+            e1.record()
+            E.sketch_query(sketches[0], Qg, out_s, z_s)
+            e2.record()
+            E.exact_attend(Kg, Vg, Qg, out_e, z_e)
+            e3.record()
+            rec.append((e0, e1, e2, e3))
+
+        warm = []
+        for _ in range(args.warmup):
+            step(warm)
+        torch.cuda.synchronize()
+        for sk in sketches:          # library events around the update/query kernels
+            E.sketch_timing(sk, True)
+        rec = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(rec)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        r = {"sketches": sketches, "t_step": wall / args.steps,
+             "t_upd": np.mean([a.elapsed_time(b) for a, b, _, _ in rec]) / 1e3,
+             "t_qry": np.mean([b.elapsed_time(c) for _, b, c, _ in rec]) / 1e3,
+             "t_ex": np.mean([c.elapsed_time(d) for _, _, c, d in rec]) / 1e3}
+        # the update and query kernels' launches in the timed steps, bracketed by
+        # HIP events on the library's stream (sketch_timing)
+        upd_ms = [t for sk in sketches for t in E.sketch_kernel_times(sk, "update")]
+        qry_ms = E.sketch_kernel_times(sketches[0], "query")
+        for sk in sketches:
+            E.sketch_timing(sk, False)
+        r["dur"] = float(np.mean(upd_ms)) / 1e3
+        r["launches"] = len(upd_ms)
+        r["t_qk"] = float(np.mean(qry_ms)) / 1e3
+        return r
+
+    full = measure("full")
+    sketches = full["sketches"]
+    t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
+    dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
     achieved = flop_per_key * keys_per_call * w.h / dur
-    t_qk = float(np.mean(qry_ms)) / 1e3
 
     # one whole sketch_update call (update kernel + split reduce), per call
     sk = sketches[0]
@@ -290,10 +303,34 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
                      "traffic": committed_traffic("sk_update_kernel", w.name),
                      "flop_per_launch": flop_per_key * keys_per_call * w.h,
-                     "launch_us": dur * 1e6, "launches": len(upd_ms)},
+                     "launch_us": dur * 1e6, "launches": full["launches"]},
     }
     for s_ in sketches:
         s_.destroy()
+    # the same step with multiset storage of the moments (identical answers,
+    # C(d + p, p) rows instead of D); priced at its own algorithmic work
+    sym = measure("sym")
+    for s_ in sym["sketches"]:
+        s_.destroy()
+    rows = math.comb(w.d + w.p, w.p)
+    sflop = 2.0 * rows * (1 + w.dv)
+    s_ach = sflop * keys_per_call * w.h / sym["dur"]
+    line["sym_layout"] = {
+        "value": w.h * (w.n + w.m) / sym["t_step"],
+        "ms_per_step": sym["t_step"] * 1e3,
+        "rows": rows,
+        "keys_per_s": w.h * w.n / sym["t_upd"],
+        "queries_per_s": w.h * w.m / sym["t_qry"],
+        "update_ms": sym["t_upd"] * 1e3,
+        "query_ms": sym["t_qry"] * 1e3,
+        "exact_ms": sym["t_ex"] * 1e3,
+        "query_kernel_mfma_frac": sflop * w.h * w.m / sym["t_qk"] / PEAK_FP32_MFMA,
+        "roofline": {"kernel": "sk_sym_update_kernel", "bound": "mfma",
+                     "achieved": s_ach / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
+                     "unit": "TFLOP/s", "frac": s_ach / PEAK_FP32_MFMA,
+                     "flop_per_launch": sflop * keys_per_call * w.h,
+                     "launch_us": sym["dur"] * 1e6, "launches": sym["launches"]},
+    }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, K, V, Q, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -94,15 +94,24 @@ size_t query_lds_bytes(int d) {
 }
 
 size_t sym_update_lds_bytes(int d, int dv) {
-  // Ks (+ ones and zeros rows) + Vs, prefix products, slot codes
-  return sizeof(float) * ((size_t)(d + 2 + dv) * (SY_KB + 1) + (size_t)SY_KB * SY_LDP) +
-         sizeof(unsigned long long) * SY_NS;
+  // Ks (+ ones and zeros rows) + Vs, prefix products
+  return sizeof(float) * ((size_t)(d + 2 + dv) * SY_LDK + (size_t)SY_KB * SY_LDP);
 }
 size_t sym_query_lds_bytes(int d) {
   // Qs + At + Bt (widest column tile, 128 columns: row stride 144) + row codes
   return sizeof(float) * ((size_t)d * (SY_TQ + 1) + (size_t)SY_QKB * (SY_TQ + 16) +
                           (size_t)SY_QKB * 144) +
          sizeof(unsigned long long) * SY_QKB;
+}
+// row blocks of 16 per wave of the multiset update: 1, 2 or 4, tiles of 64 * rb
+// rows (EXPSKETCH_SYM_RB overrides the default 4; tuning aid)
+int sym_update_rb() {
+  static const int v = [] {
+    const char* e = std::getenv("EXPSKETCH_SYM_RB");
+    const int r = e ? std::atoi(e) : 4;
+    return (r == 1 || r == 2 || r == 4) ? r : 4;
+  }();
+  return v;
 }
 // state rows per range of the multiset query (EXPSKETCH_SYM_QUERY_ROWS overrides)
 int sym_query_rows() {
@@ -112,6 +121,23 @@ int sym_query_rows() {
     return r >= SY_QKB ? r / SY_QKB * SY_QKB : 128;
   }();
   return v;
+}
+
+// The multiset update kernel is instantiated per tile shape (rb, cb).
+using SymUpdateKernel = void (*)(const float*, const float*, long long, int, int,
+                                 const SymUpdTile*, int, SymTables, long long, int, int,
+                                 float*, long long, long long, int);
+SymUpdateKernel sym_update_kernel_for(int rb, int cb) {
+  switch (rb * 8 + cb) {
+    case 4 * 8 + 1: return sk_sym_update_kernel<4, 1>;
+    case 4 * 8 + 2: return sk_sym_update_kernel<4, 2>;
+    case 4 * 8 + 4: return sk_sym_update_kernel<4, 4>;
+    case 2 * 8 + 1: return sk_sym_update_kernel<2, 1>;
+    case 2 * 8 + 2: return sk_sym_update_kernel<2, 2>;
+    case 2 * 8 + 4: return sk_sym_update_kernel<2, 4>;
+    case 1 * 8 + 4: return sk_sym_update_kernel<1, 4>;
+    default: return nullptr;
+  }
 }
 
 // The query kernel is instantiated per log2(d) (d = 4 .. 128).
@@ -157,7 +183,8 @@ struct sk_sketch {
   long long Dsym = 0, Rlo = 0, Rtop = 0;   // canonical rows; lower and top block rows
   void* symbuf = nullptr;                  // device tables (one allocation)
   SymTables tb{};
-  std::vector<SymUpdTile> sutiles;
+  std::vector<SymUpdTile> sutiles;         // grouped by tile shape
+  std::vector<int> sgroup;                 // first tile of each shape group, + end
   std::vector<SymQryTile> sqtiles;
   SymUpdTile* d_sutiles = nullptr;
   SymQryTile* d_sqtiles = nullptr;
@@ -298,12 +325,18 @@ void sym_tables(int d, int p, SymHost* t, long long* Rlo) {
   t->rslot.assign(t->code.size(), 0);
 }
 
+// Column blocks of 16 per wave of the multiset update.  One shape serves both
+// blocks of a sketch (one launch per update call): the top block's width dv sets
+// it, and the wider lower block (d + dv) takes more column tiles.
+int sym_update_cb(int dv) { return dv <= 16 ? 1 : (dv <= 32 ? 2 : 4); }
+
 // Update tiles of one block: row tiles of at most TM rows and SY_NS prefix slots
 // (rows with one prefix are consecutive), each cut into column tiles.
 void plan_sym_update_block(sk_sketch* s, SymHost* t, long long xoff, int rc0, int nrows,
                            int C, int top) {
-  const int cb = C <= 16 ? 1 : (C <= 32 ? 2 : 4);
-  const int TM = 64 * (16 / cb), TN = 16 * cb;
+  const int cb = sym_update_cb(s->dv);
+  const int rb = sym_update_rb();
+  const int TM = 64 * rb, TN = 16 * cb;   // TM <= SY_NS: a tile never runs out of slots
   int r = 0;
   while (r < nrows) {
     const int row0 = r, slot0 = (int)t->slots.size();
@@ -333,6 +366,7 @@ void plan_sym_update_block(sk_sketch* s, SymHost* t, long long xoff, int rc0, in
       u.slot0 = slot0;
       u.nslots = ns;
       u.cb = cb;
+      u.rb = (rb == 1 && cb != 4) ? 2 : rb;   // (1, 1) and (1, 2) are not instantiated
       s->sutiles.push_back(u);
     }
   }
@@ -376,6 +410,16 @@ int build_sym(sk_sketch* s) {
   s->XS = s->Rlo * Cl + s->Rtop * s->dv;
   if (s->Rlo > 0) plan_sym_update_block(s, &t, 0, 0, (int)s->Rlo, Cl, 0);
   plan_sym_update_block(s, &t, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
+  // group the update tiles by shape (one launch per shape), order kept inside
+  std::stable_sort(s->sutiles.begin(), s->sutiles.end(),
+                   [](const SymUpdTile& a, const SymUpdTile& b) {
+                     return a.rb * 8 + a.cb < b.rb * 8 + b.cb;
+                   });
+  for (size_t i = 0; i < s->sutiles.size(); ++i)
+    if (i == 0 || s->sutiles[i].rb * 8 + s->sutiles[i].cb !=
+                      s->sutiles[i - 1].rb * 8 + s->sutiles[i - 1].cb)
+      s->sgroup.push_back((int)i);
+  s->sgroup.push_back((int)s->sutiles.size());
   if (s->Rlo > 0) plan_sym_query_block(s, 0, 0, (int)s->Rlo, Cl, 0);
   plan_sym_query_block(s, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
   // one device allocation: code | prefix | last | lmul | rslot | winv | slots
@@ -418,10 +462,20 @@ int choose_update_splits(const sk_sketch* s, long long n) {
   }();
   if (forced > 0) return (int)std::max(1LL, std::min<long long>(forced, (n + SK_KB - 1) / SK_KB));
   const long long base = (long long)update_tile_count(s) * s->h;
-  const long long slots = 2LL * std::max(1, s->dev.num_cu);
+  const bool sym = s->layout == SK_LAYOUT_SYM;
+  // workgroups resident per CU: two for the full layout's kernel; for the
+  // multiset kernel its wave bound (four, two for the 16-block shape) and LDS
+  long long per_cu = 2;
+  if (sym) {
+    const int cb = sym_update_cb(s->dv);
+    per_cu = (sym_update_rb() * cb >= 16) ? 2 : 4;
+    const long long fit = (long long)s->dev.max_lds / (long long)sym_update_lds_bytes(s->d, s->dv);
+    per_cu = std::max(1LL, std::min(per_cu, fit));
+  }
+  const long long slots = per_cu * std::max(1, s->dev.num_cu);
   // at least 256 keys (multiset layout: 128) per split
-  const long long minkeys = s->layout == SK_LAYOUT_SYM ? 128 : 256;
-  const long long max_ns = std::max(1LL, std::min(64LL, n / minkeys));
+  const long long minkeys = sym ? 128 : 256;
+  const long long max_ns = std::max(1LL, std::min(sym ? 128LL : 64LL, n / minkeys));
   int best = 1;
   double best_score = -1.0;
   for (long long ns = 1; ns <= max_ns; ++ns) {
@@ -542,10 +596,13 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
                 sizeof(SymUpdTile) * s->sutiles.size()) &&
          upload((void**)&s->d_sqtiles, s->sqtiles.data(),
                 sizeof(SymQryTile) * s->sqtiles.size()) &&
-         hipFuncSetAttribute((const void*)sk_sym_update_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
          hipFuncSetAttribute((const void*)sk_sym_query_kernel,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
+  for (size_t g = 0; ok && sym && g + 1 < s->sgroup.size(); ++g) {
+    const SymUpdTile& t0 = s->sutiles[s->sgroup[g]];
+    ok = hipFuncSetAttribute((const void*)sym_update_kernel_for(t0.rb, t0.cb),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess;
+  }
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
          hipFuncSetAttribute((const void*)sk_update_kernel,
@@ -641,16 +698,23 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const int acc = nsplit > 1 ? 0 : 1;
   hipError_t err = hipSuccess;
   timing_mark(s, 0, false);
-  if (sym)
-    hipLaunchKernelGGL(sk_sym_update_kernel,
-                       dim3((unsigned)((long long)ntiles * nsplit * s->h)), dim3(SK_WG), lds,
-                       s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles, ntiles,
-                       s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc);
-  else
+  if (sym) {
+    for (size_t g = 0; g + 1 < s->sgroup.size(); ++g) {
+      const int t0 = s->sgroup[g], nt = s->sgroup[g + 1] - t0;
+      const SymUpdTile& sh = s->sutiles[t0];
+      hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb),
+                         dim3((unsigned)((long long)nt * nsplit * s->h)), dim3(SK_WG), lds,
+                         s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles + t0, nt,
+                         s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) err = e;
+    }
+  } else {
     hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
                        dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
                        s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc);
-  err = hipGetLastError();
+    err = hipGetLastError();
+  }
   timing_mark(s, 0, true);
   if (nsplit > 1) {
     const long long c4 = total / 4;

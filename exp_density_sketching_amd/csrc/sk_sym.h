@@ -41,6 +41,12 @@ __device__ __forceinline__ floatx4v mfma16x16x4(float a, float b, floatx4v c) {
 }
 
 #define SY_KB 32                 // keys per update stage
+#ifndef SY_LDK
+// row stride of the transposed key/value stage: the A operand reads rows
+// last(row) for 16 rows and 4 keys at once; stride 34 puts them on distinct banks
+// (32 banks per half-wave)
+#define SY_LDK 34
+#endif
 #define SY_NS 256                // prefix slots per update row tile
 #define SY_LDP (SY_NS + 16)      // row stride of the prefix products (bank spread)
 #define SY_TQ 128                // queries per query tile
@@ -66,8 +72,8 @@ struct SymUpdTile {
   int col0, C;       // first column; the block's width (d + dv, or dv at the top)
   int top;           // 1 for the top block (u = v)
   int slot0, nslots; // the tile's prefix slots in SymTables::slots
-  int cb;            // column blocks of 16 per wave: 1, 2 or 4 (tile 64*16/cb x 16*cb)
-  int pad_;
+  int cb;            // column blocks of 16 per wave: 1, 2 or 4
+  int rb;            // row blocks of 16 per wave: 1, 2 or 4 (tile 64*rb x 16*cb)
 };
 
 // One (row range, column tile) of a block's query GEMM
@@ -89,29 +95,32 @@ struct SymQryTile {
 
 // ---------------------------------------------------------------------------
 // Update: one workgroup = 4 waves stacked along the rows, each wave 16*RB rows x
-// 16*CB columns (RB * CB = 16 accumulator blocks).  Per stage of SY_KB keys:
+// 16*CB columns (RB * CB <= 16 accumulator blocks), so a tile is 64*RB rows and
+// at most SY_NS = 256 prefix slots.  Per stage of SY_KB keys:
 //   1. the stage's K and V rows -> LDS, transposed ([component][key]), with two
 //      extra key rows: all ones (the empty prefix and the empty multiset) and all
 //      zeros (rows and columns outside the block);
-//   2. prefix products P[key][slot] = k^prefix for the tile's prefix slots;
+//   2. prefix products P[key][slot] = k^prefix: thread t owns slot t for the
+//      whole tile, with the LDS offsets of its prefix's indices in registers, and
+//      reads the stage's keys at compile-time offsets from them;
 //   3. per k-step of 4 keys, each lane forms its A operand P[key][slot(row)] *
 //      k[last(row)] in a register and reads its B operand u[key][col] from LDS.
 // ---------------------------------------------------------------------------
-template <int CB>
+template <int RB, int CB>
 __device__ __forceinline__
 void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V,
                         long long n, int d, int dv, const SymUpdTile& T, const SymTables& tb,
                         long long split, long long head, long long keys_per_split,
                         float* __restrict__ out, long long head_stride,
                         long long split_stride, int accumulate) {
-  constexpr int RB = 16 / CB;
-  constexpr int LDK = SY_KB + 1;
+  static_assert(RB * CB <= 16 && 64 * RB <= SY_NS, "tile shape");
+  constexpr int LDK = SY_LDK;
   constexpr int NPF = 4;              // float4 per thread per stage, for d, dv <= 128
+  constexpr int PK = 8;               // keys per pass of the prefix products
   extern __shared__ float lds[];
   float* Ks = lds;                                  // [d + 2][LDK]
   float* Vs = Ks + (d + 2) * LDK;                   // [dv][LDK]
   float* P = Vs + dv * LDK;                         // [SY_KB][SY_LDP]
-  unsigned long long* Sc = reinterpret_cast<unsigned long long*>(P + SY_KB * SY_LDP);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
@@ -126,10 +135,22 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
     Ks[d * LDK + i] = 1.f;
     Ks[(d + 1) * LDK + i] = 0.f;
   }
-  const int nslots = T.nslots;
-  for (int i = tid; i < nslots; i += SK_WG) {
-    const int id = tb.slots[T.slot0 + i];
-    Sc[i] = id < 0 ? 0ull : tb.code[id];
+  // this thread's prefix slot (fixed for the tile; with few slots, up to four
+  // threads share a slot and take different chunks of PK keys): the slot's
+  // indices as LDS row offsets
+  const int ns = T.nslots;
+  const int G = ns <= 64 ? 4 : (ns <= 128 ? 2 : 1);
+  const bool pown = tid < G * ns;
+  const int pslot = pown ? tid % ns : 0;
+  const int pc0 = pown ? tid / ns : SY_KB / PK;
+  int pcnt = 0;
+  int pdo[SY_MAXP - 1];
+  {
+    const int id = pown ? tb.slots[T.slot0 + pslot] : -1;
+    const unsigned long long c = id < 0 ? 0ull : tb.code[id];
+    pcnt = (int)(c >> 56);
+#pragma unroll
+    for (int q = 0; q < SY_MAXP - 1; ++q) pdo[q] = (int)((c >> (8 * q)) & 0xffu) * LDK;
   }
 
   // A operand: row 16 rb + li of the wave's rows, key 4 ks + lk of the k-step
@@ -202,14 +223,22 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
       }
     }
     __syncthreads();
-    // prefix products of the stage: consecutive threads take consecutive slots
-    for (int i = tid; i < nslots * SY_KB; i += SK_WG) {
-      const int key = i / nslots, sl = i - key * nslots;
-      const unsigned long long c = Sc[sl];
-      const int cnt = (int)(c >> 56);
-      float pr = 1.f;
-      for (int q = 0; q < cnt; ++q) pr *= Ks[(int)((c >> (8 * q)) & 0xffu) * LDK + key];
-      P[key * SY_LDP + sl] = pr;
+    for (int kc = pc0; kc < SY_KB / PK; kc += G) {
+      const int k0 = kc * PK;
+      float f[PK];
+#pragma unroll
+      for (int u = 0; u < PK; ++u) f[u] = 1.f;
+#pragma unroll
+      for (int q = 0; q < SY_MAXP - 1; ++q) {
+        if (q < pcnt) {
+          const float* src = Ks + pdo[q] + k0;
+#pragma unroll
+          for (int u = 0; u < PK; ++u) f[u] *= src[u];
+        }
+      }
+      float* dst = P + k0 * SY_LDP + pslot;
+#pragma unroll
+      for (int u = 0; u < PK; ++u) dst[u * SY_LDP] = f[u];
     }
     __syncthreads();
     if (kb0 + SY_KB < k_end) fetch(kb0 + SY_KB);
@@ -247,10 +276,14 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
   }
 }
 
-// Every (tile, key split, head) of one update call in one launch; the 1-D grid
-// is remapped so that each XCD takes a contiguous range (tiles that read the
-// same keys share an L2).
-__global__ __launch_bounds__(SK_WG, 2)
+// All (tile, key split, head) of one tile shape (RB, CB) in one launch; the 1-D
+// grid is remapped so that each XCD takes a contiguous range (tiles that read
+// the same keys share an L2).  One kernel per shape keeps each shape's register
+// count its own: at most 128 VGPRs, four waves per SIMD, so the stages of other
+// workgroups cover the latency of a workgroup's barriers (two waves for the
+// 16-block shape, whose accumulators alone take 64 registers).
+template <int RB, int CB>
+__global__ __launch_bounds__(SK_WG, (RB * CB >= 16) ? 2 : 4)
 void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                           long long n, int d, int dv,
                           const SymUpdTile* __restrict__ tiles, int ntiles, SymTables tb,
@@ -263,20 +296,8 @@ void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__
   const long long split = (lg / ntiles) % nsplit;
   const long long head = lg / ((long long)ntiles * nsplit);
   const SymUpdTile T = tiles[tile];
-  switch (T.cb) {
-    case 1:
-      sk_sym_update_tile<1>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
-                            head_stride, split_stride, accumulate);
-      break;
-    case 2:
-      sk_sym_update_tile<2>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
-                            head_stride, split_stride, accumulate);
-      break;
-    default:
-      sk_sym_update_tile<4>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
-                            head_stride, split_stride, accumulate);
-      break;
-  }
+  sk_sym_update_tile<RB, CB>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
+                             head_stride, split_stride, accumulate);
 }
 
 // ---------------------------------------------------------------------------
