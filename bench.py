@@ -124,6 +124,54 @@ def cpu_baseline(w, K, V, Q, budget):
     }
 
 
+def state_floats(w, layout):
+    """Floats of one head's stored moments (the layout's blocks)."""
+    if layout == "full":
+        return (w.D - 1) + w.D * w.dv
+    top = math.comb(w.d + w.p - 1, w.p)
+    lower = math.comb(w.d + w.p, w.p) - top
+    return lower * (w.d + w.dv) + top * w.dv
+
+
+def decode_steps(w, E, torch, Kg, Vg, Qg, steps, exact_us):
+    """sketch_step on a sketch holding the whole stream: one key/value appended
+    and one query answered per head and step.  Algorithmic traffic: one read and
+    one write of the stored moments per step."""
+    import numpy as np
+    res = {}
+    for layout in ("full", "sym"):
+        sk = E.sketch_create(w.d, w.dv, w.p, w.h, layout)
+        E.sketch_update(sk, Kg, Vg)
+        ks = [Kg[:, i].contiguous() for i in range(steps)]
+        vs = [Vg[:, i].contiguous() for i in range(steps)]
+        qs = [Qg[:, i % w.m].contiguous() for i in range(steps)]
+        out = torch.empty((w.h, w.dv), device="cuda")
+        z = torch.empty((w.h,), device="cuda")
+        for i in range(3):
+            E.sketch_step(sk, ks[i], vs[i], qs[i], out, z)
+        torch.cuda.synchronize()
+        E.sketch_timing(sk, True)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            E.sketch_step(sk, ks[i], vs[i], qs[i], out, z)
+        b.record()
+        torch.cuda.synchronize()
+        kern = E.sketch_kernel_times(sk, "step")
+        E.sketch_timing(sk, False)
+        sk.destroy()
+        t = a.elapsed_time(b) / 1e3 / steps
+        tk = float(np.mean(kern)) / 1e3
+        nbytes = 2.0 * 4 * w.h * state_floats(w, layout)
+        res[layout] = {"us_per_step": t * 1e6, "kernel_us": tk * 1e6,
+                       "state_bytes": nbytes / 2, "kernel_GBps": nbytes / tk / 1e9,
+                       "speedup_vs_exact_decode": exact_us / (t * 1e6)}
+    res["steps"] = steps
+    res["resident"] = "cache (state <= 256 MB)"
+    return res
+
+
 def counters_pass(w, E, torch, generate, layout="full"):
     """Fixed sequence for counter passes: copy of known size, update, query, decode."""
     from exp_density_sketching_amd.workload import ingest
@@ -331,6 +379,8 @@ def main():
                      "flop_per_launch": sflop * keys_per_call * w.h,
                      "launch_us": sym["dur"] * 1e6, "launches": sym["launches"]},
     }
+    line["decode_step"] = decode_steps(w, E, torch, Kg, Vg, Qg, args.decode_steps,
+                                       line["exact_decode"]["us_per_step"])
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, K, V, Q, args.cpu_seconds)
     print(json.dumps(line), flush=True)

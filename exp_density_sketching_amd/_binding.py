@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_PKG, "libexpsketch.so")
 SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
 LAYOUTS = {"full": 0, "sym": 1}
 
-EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy", "sketch_set_stream", "sketch_reset",
-            "sketch_update", "sketch_merge", "sketch_query", "exact_attend",
+EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy",
+            "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
+            "sketch_query", "sketch_step", "exact_attend",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
 
@@ -53,6 +54,7 @@ def _lib():
             "sketch_update": (c_int, [vp, vp, vp, c_i64]),
             "sketch_merge": (c_int, [vp, vp]),
             "sketch_query": (c_int, [vp, vp, c_i64, vp, vp]),
+            "sketch_step": (c_int, [vp, vp, vp, vp, vp, vp]),
             "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
                                      vp, vp]),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
@@ -205,6 +207,26 @@ def sketch_query(s, Q, out=None, Z=None):
     return (out[0], Z[0]) if squeeze else (out, Z)
 
 
+def sketch_step(s, k, v, q, out=None, Z=None):
+    """One decode step per head: append (k, v), answer q over the stream with it.
+
+    k [h, d], v [h, dv], q [h, d] (or 1-d for one head) -> (out [h, dv], Z [h])."""
+    squeeze = k.dim() == 1
+    if squeeze:
+        k, v, q = k.unsqueeze(0), v.unsqueeze(0), q.unsqueeze(0)
+    if tuple(k.shape) != (s.h, s.d) or tuple(v.shape) != (s.h, s.dv) or \
+            tuple(q.shape) != (s.h, s.d):
+        raise ValueError(f"k {tuple(k.shape)}, v {tuple(v.shape)}, q {tuple(q.shape)} do "
+                         f"not match h={s.h}, d={s.d}, dv={s.dv}")
+    if out is None:
+        out = torch.empty((s.h, s.dv), dtype=torch.float32, device=k.device)
+    if Z is None:
+        Z = torch.empty((s.h,), dtype=torch.float32, device=k.device)
+    _check(_lib().sketch_step(s._handle(), _dev(k, "k", 2), _dev(v, "v", 2), _dev(q, "q", 2),
+                              _dev(out, "out", 2), _dev(Z, "Z", 1)), "sketch_step")
+    return (out[0], Z[0]) if squeeze else (out, Z)
+
+
 def sketch_export(s, dst=None, device=None):
     """Canonical [M | N] view into a new (or given) tensor [h, rows, 1 + dv]
     (rows = D for the full layout, C(d + p, p) for the multiset layout)."""
@@ -233,8 +255,8 @@ def sketch_timing(s, enable=True):
 
 
 def sketch_kernel_times(s, kind):
-    """Milliseconds of each recorded kernel of `kind` ("update" or "query")."""
-    k = {"update": 0, "query": 1}[kind]
+    """Milliseconds of each recorded kernel of `kind` ("update", "query", "step")."""
+    k = {"update": 0, "query": 1, "step": 2}[kind]
     cap = 256
     buf = (ctypes.c_float * cap)()
     cnt = ctypes.c_int()

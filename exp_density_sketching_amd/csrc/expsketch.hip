@@ -16,6 +16,7 @@
 #include "sk_elementwise.h"
 #include "sk_exact.h"
 #include "sk_query.h"
+#include "sk_step.h"
 #include "sk_sym.h"
 #include "sk_update.h"
 
@@ -174,8 +175,8 @@ struct sk_sketch {
   long long qpb = 0;        // floats of query partials per (head, query tile)
   float* view = nullptr;    // canonical view buffer
   bool timing = false;      // kernel timing (sketch_timing)
-  std::vector<hipEvent_t> tev[2][2];   // [kind][start, stop], created on first use
-  int trec[2] = {0, 0};     // pairs recorded per kind
+  std::vector<hipEvent_t> tev[3][2];   // [kind][start, stop], created on first use
+  int trec[3] = {0, 0, 0};  // pairs recorded per kind
   size_t view_bytes = 0;
   DeviceInfo dev;
   // multiset layout (SK_LAYOUT_SYM)
@@ -188,6 +189,10 @@ struct sk_sketch {
   std::vector<SymQryTile> sqtiles;
   SymUpdTile* d_sutiles = nullptr;
   SymQryTile* d_sqtiles = nullptr;
+  // decode steps (sketch_step): row-range tiles of the whole state, partials
+  std::vector<StepTile> stiles;
+  StepTile* d_stiles = nullptr;
+  float* sparts = nullptr;                 // [h][tiles][1 + dv]
 };
 
 namespace {
@@ -450,6 +455,39 @@ int build_sym(sk_sketch* s) {
   return SK_OK;
 }
 
+// Decode-step tiles: every block of the state cut into row ranges of at most
+// ST_FLOATS floats (and ST_ROWS rows).
+void plan_step_block(sk_sketch* s, long long xoff, long long rows, int C, int top, int level,
+                     int rc0, int j) {
+  const long long rpt = std::max(1LL, std::min<long long>(ST_ROWS, ST_FLOATS / C));
+  double fj = 1.0;
+  for (int i = 2; i <= j; ++i) fj *= i;
+  for (long long r0 = 0; r0 < rows; r0 += rpt) {
+    StepTile t{};
+    t.xoff = xoff;
+    t.row0 = r0;
+    t.nrows = (int)std::min(rpt, rows - r0);
+    t.C = C;
+    t.top = top;
+    t.level = level;
+    t.rc0 = rc0;
+    t.wn = (float)(1.0 / fj);
+    t.wz = (float)(1.0 / (j + 1));
+    s->stiles.push_back(t);
+  }
+}
+
+void plan_step(sk_sketch* s) {
+  if (s->layout == SK_LAYOUT_SYM) {
+    const int Cl = s->d + s->dv;
+    if (s->Rlo > 0) plan_step_block(s, 0, s->Rlo, Cl, 0, -1, 0, 0);
+    plan_step_block(s, s->Rlo * Cl, s->Rtop, s->dv, 1, -1, (int)s->Rlo, 0);
+  } else {
+    for (int j = 0; j <= s->p; ++j)
+      plan_step_block(s, s->xoff[j], s->rows[j], s->C[j], j == s->p, j, 0, j);
+  }
+}
+
 int update_tile_count(const sk_sketch* s) {
   return (int)(s->layout == SK_LAYOUT_SYM ? s->sutiles.size() : s->utiles.size());
 }
@@ -578,6 +616,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
   }
 
+  plan_step(s);
   const size_t state_bytes = sizeof(float) * (size_t)s->XS * (size_t)h;
   if (hipMalloc(&s->state, state_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -590,7 +629,11 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     return hipMalloc(dst, bytes) == hipSuccess &&
            hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice) == hipSuccess;
   };
-  bool ok = upload((void**)&s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size());
+  bool ok = upload((void**)&s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size()) &&
+            upload((void**)&s->d_stiles, s->stiles.data(),
+                   sizeof(StepTile) * s->stiles.size()) &&
+            hipMalloc(&s->sparts, sizeof(float) * (size_t)h * s->stiles.size() * (1 + dv)) ==
+                hipSuccess;
   if (ok && sym)
     ok = upload((void**)&s->d_sutiles, s->sutiles.data(),
                 sizeof(SymUpdTile) * s->sutiles.size()) &&
@@ -614,6 +657,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     (void)hipGetLastError();
     (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
     (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
+    (void)hipFree(s->d_stiles); (void)hipFree(s->sparts);
     delete s;
     return SK_EHIP;
   }
@@ -642,8 +686,10 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->d_sutiles);
   (void)hipFree(s->d_sqtiles);
   (void)hipFree(s->symbuf);
+  (void)hipFree(s->d_stiles);
+  (void)hipFree(s->sparts);
   (void)hipFree(s->view);
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < 3; ++k)
     for (int w = 0; w < 2; ++w)
       for (hipEvent_t e : s->tev[k][w]) (void)hipEventDestroy(e);
   delete s;
@@ -787,22 +833,43 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   return SK_OK;
 }
 
+int sketch_step(sk_handle s, const float* k, const float* v, const float* q, float* out,
+                float* Z) {
+  if (s == nullptr || k == nullptr || v == nullptr || q == nullptr || out == nullptr ||
+      Z == nullptr)
+    return SK_EINVAL;
+  const int nt = (int)s->stiles.size();
+  if ((long long)nt * s->h > 0x7fffffffLL) return SK_EINVAL;
+  timing_mark(s, 2, false);
+  hipLaunchKernelGGL(sk_step_kernel, dim3((unsigned)((long long)nt * s->h)), dim3(256), 0,
+                     s->stream, s->state, s->XS, s->d_stiles, nt, s->d, s->dv, s->logd, k, v,
+                     q, s->tb, s->sparts);
+  hipError_t e1 = hipGetLastError();
+  timing_mark(s, 2, true);
+  hipLaunchKernelGGL(sk_step_finish, dim3((unsigned)s->h), dim3(256), 0, s->stream, s->sparts,
+                     nt, s->dv, (float)(s->count + 1), out, Z);
+  hipError_t e2 = hipGetLastError();
+  if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
+  s->count += 1;
+  return SK_OK;
+}
+
 int sketch_timing(sk_handle s, int enable) {
   if (s == nullptr) return SK_EINVAL;
   if (enable && s->tev[0][0].empty()) {
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 3; ++k)
       for (int w = 0; w < 2; ++w) {
         s->tev[k][w].resize(kTimingPairs);
         for (int i = 0; i < kTimingPairs; ++i) SK_TRY(hipEventCreate(&s->tev[k][w][i]));
       }
   }
   s->timing = enable != 0;
-  s->trec[0] = s->trec[1] = 0;
+  s->trec[0] = s->trec[1] = s->trec[2] = 0;
   return SK_OK;
 }
 
 int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count) {
-  if (s == nullptr || kind < 0 || kind > 1 || cap < 0 || (ms == nullptr && cap > 0))
+  if (s == nullptr || kind < 0 || kind > 2 || cap < 0 || (ms == nullptr && cap > 0))
     return SK_EINVAL;
   const int nrec = s->trec[kind];
   if (count) *count = nrec;

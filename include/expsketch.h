@@ -137,6 +137,24 @@ int sketch_merge(sk_handle dst, sk_handle src);
 int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z);
 
 /*
+ * sketch_step -- one streaming decode step per head: append the pair (k, v) to
+ * the stream, then answer the query q over the stream including it
+ * ("Definição do Problema": the stream answered query by query; "O Método
+ * Polinomial": the same moments and answers as sketch_update with n = 1
+ * followed by sketch_query with m = 1).  One pass over the state adds the
+ * rank-one term of the new key to every stored entry and forms the query's
+ * weighted sums of the updated entries; a second, small kernel adds them in a
+ * fixed order and divides.  Nothing is allocated: the per-tile partials live in
+ * a buffer the handle owns (sized at create), so calls on one handle must not
+ * overlap.
+ *   k: device [h][d]; v: device [h][dv]; q: device [h][d];
+ *   out: device [h][dv] (ohat); Z: device [h] (Zhat).  count grows by 1.
+ * Errors: SK_EINVAL (NULL handle or pointer), SK_EHIP.
+ */
+int sketch_step(sk_handle s, const float* k, const float* v, const float* q, float* out,
+                float* Z);
+
+/*
  * exact_attend -- the exact streaming path ("Definição do Problema": keep every
  * pair):  Z[h][q] = sum_i exp(<q, k_i>),  out[h][q] = sum_i exp(<q,k_i>) v_i / Z.
  * Computed with a running maximum (online softmax) over key slices and a
@@ -185,14 +203,15 @@ int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D,
 /*
  * sketch_timing -- kernel timing with HIP events on the handle's stream (for
  * measurement).  While enabled, each sketch_update records a pair of
- * library-owned events around its moment-update kernel (kind 0) and each
- * sketch_query around its contraction kernel (kind 1), up to 256 pairs per kind;
+ * library-owned events around its moment-update kernel(s) (kind 0), each
+ * sketch_query around its contraction kernel (kind 1) and each sketch_step around
+ * its fused update-and-answer kernel (kind 2), up to 256 pairs per kind;
  * later calls are not recorded until the pairs are collected.  enable != 0
  * starts (and clears) recording, 0 stops it.
  * sketch_kernel_times -- waits for the last recorded event of `kind`, writes the
  * elapsed milliseconds of up to `cap` recorded pairs into ms (host array), sets
  * *count to the number recorded, and clears them.
- * Errors: SK_EINVAL (NULL handle, kind not 0/1, cap < 0, ms NULL with cap > 0),
+ * Errors: SK_EINVAL (NULL handle, kind not 0/1/2, cap < 0, ms NULL with cap > 0),
  * SK_EHIP.
  */
 int sketch_timing(sk_handle s, int enable);
