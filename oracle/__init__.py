@@ -25,6 +25,11 @@ repository's design notes):
 * Same section, closing paragraph on Merge-and-Reduce: summaries of sub-streams
   are merged.  Moments are sums, so the merge is an addition.
   -> ``sketch.MomentSketch.merge``.
+* Same section, pillar "Particionamento de Espaço e Recentramento" (shift a
+  dense cluster to the origin): with one fixed centre c,
+  exp<q,k> = e^{<q,c>} exp<q, k - c>, so the sketch of the shifted keys k - c
+  answers with an extra factor e^{<q,c>} on Zhat (it cancels in ohat).
+  -> ``sketch.sketch_direct_centered``.
 * ``sym``: the same moments kept once per multiset of tensor indices (the moment
   tensors are symmetric), with the query weight q^alpha / alpha!.  The pages
   leave the storage open; this is the symmetric-tensor reading.
@@ -38,12 +43,14 @@ docstrings there).  No function of this package is "parity unpinned".
 """
 
 from .exact import exact_attention
-from .sketch import taylor_exp, sketch_direct, MomentSketch, feature_map
+from .sketch import (taylor_exp, sketch_direct, sketch_direct_centered, MomentSketch,
+                     feature_map)
 from .sym import SymMomentSketch, multisets, alpha_factorial, sym_features
 from .bounds import (taylor_term_bound, kde_relative_bound, attention_abs_bound,
                      measured_radius)
 
-__all__ = ["exact_attention", "taylor_exp", "sketch_direct", "MomentSketch",
+__all__ = ["exact_attention", "taylor_exp", "sketch_direct", "sketch_direct_centered",
+           "MomentSketch",
            "feature_map", "SymMomentSketch", "multisets", "alpha_factorial",
            "sym_features", "taylor_term_bound", "kde_relative_bound",
            "attention_abs_bound", "measured_radius"]

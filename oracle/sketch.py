@@ -140,3 +140,24 @@ class MomentSketch:
         return np.concatenate(
             [np.concatenate([self.M[j][:, None], self.N[j]], axis=1)
              for j in range(self.p + 1)], axis=0)
+
+
+def sketch_direct_centered(K, V, Q, p, c):
+    """The sketch recentred at a fixed centre c, by its plain definition.
+
+    Source: "Metodologia", pillar "Particionamento de Espaço e Recentramento"
+    (French page: "Partition de l'Espace et Recentrage"): a dense cluster is
+    shifted to the origin, which shrinks the radius the expansion has to cover.
+    Reading taken for one fixed centre (the recursive Partition is not built):
+
+        Zhat_c(q) = e^{<q,c>} sum_i T_p(<q, k_i - c>),
+        Ntilde_c(q) = e^{<q,c>} sum_i T_p(<q, k_i - c>) v_i,   ohat = Ntilde / Zhat,
+
+    exact in the limit p -> infinity because e^{<q,c>} e^{<q, k - c>} = e^{<q, k>}.
+    The moments are those of the shifted keys k - c; the factor e^{<q,c>} cancels
+    in ohat.  Returns (ohat [m, dv], Zhat [m])."""
+    K = np.asarray(K, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    out, Z = sketch_direct(K - c[None, :], V, Q, p)
+    return out, Z * np.exp(Q @ c)

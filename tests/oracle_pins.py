@@ -375,3 +375,88 @@ def pin_sym_merge(impl, p=3, d=3, dv=2, seed=24):
     S1, S2 = a.canonical_state(), ab.canonical_state()
     err = float(np.max(np.abs(S1 - S2) / np.maximum(np.abs(S2), 1.0)))
     return max(err, abs(a.count - ab.count))
+
+
+# Recentred sketch (oracle.sketch_direct_centered) -------------------------------------
+
+def _clustered(seed, n, m, d, dv, offset=1.2, spread=0.15):
+    """Keys in a tight cluster away from the origin, queries of norm about 0.8."""
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal(d)
+    mu *= offset / np.linalg.norm(mu)
+    K = mu + spread * rng.standard_normal((n, d)) / np.sqrt(d)
+    V = rng.standard_normal((n, dv))
+    Q = rng.standard_normal((m, d))
+    Q *= 0.8 / np.linalg.norm(Q, axis=1, keepdims=True)
+    return K, V, Q, mu
+
+
+def pin_centered_zero_centre(impl, p=3, seed=31):
+    """C1: centre 0 is the plain sketch."""
+    K, V, Q = _small(seed, 40, 6, 5, 3)
+    o1, z1 = impl.sketch_direct_centered(K, V, Q, p, np.zeros(5))
+    o2, z2 = impl.sketch_direct(K, V, Q, p)
+    return max(relmax(z1, z2), absmax(o1, o2))
+
+
+def pin_centered_identical_keys(impl, seed=32):
+    """C2: every key equal to the centre: Zhat = n e^{<q,c>}, ohat = mean(v), for
+    every p (T_p(0) = 1), against math.exp and math.fsum."""
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal(4)
+    K = np.tile(c, (30, 1))
+    V = rng.standard_normal((30, 2))
+    Q = rng.standard_normal((5, 4))
+    err = 0.0
+    for p in (0, 1, 4):
+        o, Z = impl.sketch_direct_centered(K, V, Q, p, c)
+        for qi in range(5):
+            zref = 30 * math.exp(math.fsum(float(Q[qi, a]) * float(c[a]) for a in range(4)))
+            err = max(err, abs(Z[qi] - zref) / zref)
+            vbar = [math.fsum(V[:, j]) / 30 for j in range(2)]
+            err = max(err, float(np.max(np.abs(o[qi] - vbar))))
+    return err
+
+
+def pin_centered_kron(impl, d=3, p=3, seed=33):
+    """C3: brute force with np.kron powers of k - c and math.exp(<q, c>)."""
+    K, V, Q = _small(seed, 15, 3, d, 2)
+    c = np.array([0.3, -0.2, 0.5][:d])
+    coef = taylor_coeffs(p)
+    Zb = np.zeros(3)
+    Nb = np.zeros((3, 2))
+    for qi in range(3):
+        f = math.exp(float(Q[qi] @ c))
+        for i in range(15):
+            w = f * sum(coef[j] * float(kron_power(Q[qi], j) @ kron_power(K[i] - c, j))
+                        for j in range(p + 1))
+            Zb[qi] += w
+            Nb[qi] += w * V[i]
+    o, Z = impl.sketch_direct_centered(K, V, Q, p, c)
+    return max(relmax(Z, Zb), absmax(o, Nb / Zb[:, None]))
+
+
+def pin_centered_bound(impl, seed=34):
+    """C4: on a cluster away from the origin the recentred error obeys the
+    Lagrange bound with the shifted radius rho_c = max|q| max|k - c|, and falls to
+    rounding as p grows; returns the largest (error / bound) and the p = 14 error."""
+    K, V, Q, mu = _clustered(seed, 200, 8, 6, 3)
+    o_e, Z_e = impl.exact_attention(K, V, Q)
+    worst = 0.0
+    for p in (1, 2, 3, 5):
+        o, Z = impl.sketch_direct_centered(K, V, Q, p, mu)
+        rho = float(np.max(np.linalg.norm(Q, axis=1)) * np.max(np.linalg.norm(K - mu, axis=1)))
+        bound = rho ** (p + 1) / math.factorial(p + 1) * math.exp(2 * rho)
+        worst = max(worst, float(np.max(np.abs(Z - Z_e) / Z_e)) / bound)
+    o, Z = impl.sketch_direct_centered(K, V, Q, 14, mu)
+    return worst, max(relmax(Z, Z_e), absmax(o, o_e))
+
+
+def pin_centered_moments(impl, p=3, seed=35):
+    """C5: the moment route on the shifted keys, answers times e^{<q,c>}, equals
+    the plain definition."""
+    K, V, Q, mu = _clustered(seed, 120, 5, 4, 2)
+    sk = impl.MomentSketch(4, 2, p).update(K - mu, V, chunk=17)
+    o, Z = sk.query(Q)
+    od, Zd = impl.sketch_direct_centered(K, V, Q, p, mu)
+    return max(relmax(Z * np.exp(Q @ mu), Zd), absmax(o, od))

@@ -250,3 +250,45 @@ def test_sym_mutant_caught(impl):
 
 def test_sym_pins_pass_on_oracle():
     assert _sym_pins(_sym_impl()) < 1e-11
+
+
+# Recentred sketch mutants ------------------------------------------------------------
+
+def _centred_no_factor(K, V, Q, p, c):
+    return oracle.sketch_direct(np.asarray(K) - np.asarray(c)[None, :], V, Q, p)
+
+
+def _centred_plus(K, V, Q, p, c):
+    o, Z = oracle.sketch_direct(np.asarray(K) + np.asarray(c)[None, :], V, Q, p)
+    return o, Z * np.exp(np.asarray(Q) @ np.asarray(c))
+
+
+def _centred_neg_factor(K, V, Q, p, c):
+    o, Z = oracle.sketch_direct(np.asarray(K) - np.asarray(c)[None, :], V, Q, p)
+    return o, Z * np.exp(-(np.asarray(Q) @ np.asarray(c)))
+
+
+def _centred_pins(impl):
+    ratio, err14 = pins.pin_centered_bound(impl)
+    return max(pins.pin_centered_zero_centre(impl), pins.pin_centered_identical_keys(impl),
+               pins.pin_centered_kron(impl), pins.pin_centered_moments(impl),
+               err14, 0.0 if ratio <= 1.0 else ratio)
+
+
+@pytest.mark.parametrize("fn", [_centred_no_factor, _centred_plus, _centred_neg_factor],
+                         ids=["no_factor", "plus_centre", "negative_factor"])
+def test_centred_mutant_caught(fn):
+    impl = types.SimpleNamespace(sketch_direct_centered=fn, sketch_direct=oracle.sketch_direct,
+                                 exact_attention=oracle.exact_attention,
+                                 MomentSketch=oracle.MomentSketch)
+    with np.errstate(all="ignore"):
+        err = _centred_pins(impl)
+    assert not err < 1e-9, "mutant survived every recentring pin"
+
+
+def test_centred_pins_pass_on_oracle():
+    impl = types.SimpleNamespace(sketch_direct_centered=oracle.sketch_direct_centered,
+                                 sketch_direct=oracle.sketch_direct,
+                                 exact_attention=oracle.exact_attention,
+                                 MomentSketch=oracle.MomentSketch)
+    assert _centred_pins(impl) < 1e-11
