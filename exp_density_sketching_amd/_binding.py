@@ -19,7 +19,7 @@ LAYOUTS = {"full": 0, "sym": 1}
 
 EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy",
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
-            "sketch_query", "sketch_step", "exact_attend",
+            "sketch_query", "sketch_step", "sketch_set_center", "exact_attend",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
 
@@ -55,6 +55,7 @@ def _lib():
             "sketch_merge": (c_int, [vp, vp]),
             "sketch_query": (c_int, [vp, vp, c_i64, vp, vp]),
             "sketch_step": (c_int, [vp, vp, vp, vp, vp, vp]),
+            "sketch_set_center": (c_int, [vp, vp]),
             "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
                                      vp, vp]),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
@@ -205,6 +206,19 @@ def sketch_query(s, Q, out=None, Z=None):
     _check(_lib().sketch_query(s._handle(), _dev(Q, "Q", 3), m, _dev(out, "out", 3),
                                _dev(Z, "Z", 2)), "sketch_query")
     return (out[0], Z[0]) if squeeze else (out, Z)
+
+
+def sketch_set_center(s, c):
+    """Recentre an empty sketch at c [h, d] (or [d] for one head); None removes it."""
+    if c is None:
+        _check(_lib().sketch_set_center(s._handle(), None), "sketch_set_center")
+        return
+    if c.dim() == 1:
+        c = c.unsqueeze(0)
+    if tuple(c.shape) != (s.h, s.d):
+        raise ValueError(f"c {tuple(c.shape)} does not match h={s.h}, d={s.d}")
+    _check(_lib().sketch_set_center(s._handle(), _dev(c.contiguous(), "c", 2)),
+           "sketch_set_center")
 
 
 def sketch_step(s, k, v, q, out=None, Z=None):

@@ -85,7 +85,7 @@ int current_device(int* dev) {
 
 size_t update_lds_bytes(int d, int dv) {
   // Ks + Vs (transposed, stride SK_KB + 1) + Lt + Rt with (TM + TN + 2 * pad) <= 384
-  return sizeof(float) * ((size_t)(SK_KB + 1) * (d + dv) + (size_t)SK_KB * 384);
+  return sizeof(float) * ((size_t)(SK_KB + 1) * (d + dv) + (size_t)SK_KB * 384 + d);
 }
 size_t query_lds_bytes(int d) {
   // Qs + max(At + Bt, Ys)
@@ -96,7 +96,7 @@ size_t query_lds_bytes(int d) {
 
 size_t sym_update_lds_bytes(int d, int dv) {
   // Ks (+ ones and zeros rows) + Vs, prefix products
-  return sizeof(float) * ((size_t)(d + 2 + dv) * SY_LDK + (size_t)SY_KB * SY_LDP);
+  return sizeof(float) * ((size_t)(d + 2 + dv) * SY_LDK + (size_t)SY_KB * SY_LDP + d);
 }
 size_t sym_query_lds_bytes(int d) {
   // Qs + At + Bt (widest column tile, 128 columns: row stride 144) + row codes
@@ -127,7 +127,7 @@ int sym_query_rows() {
 // The multiset update kernel is instantiated per tile shape (rb, cb).
 using SymUpdateKernel = void (*)(const float*, const float*, long long, int, int,
                                  const SymUpdTile*, int, SymTables, long long, int, int,
-                                 float*, long long, long long, int);
+                                 float*, long long, long long, int, const float*);
 SymUpdateKernel sym_update_kernel_for(int rb, int cb) {
   switch (rb * 8 + cb) {
     case 4 * 8 + 1: return sk_sym_update_kernel<4, 1>;
@@ -193,6 +193,9 @@ struct sk_sketch {
   std::vector<StepTile> stiles;
   StepTile* d_stiles = nullptr;
   float* sparts = nullptr;                 // [h][tiles][1 + dv]
+  // fixed centre (sketch_set_center): moments are of k - c; null = no centre
+  float* center = nullptr;                 // device [h][d]
+  std::vector<float> center_host;          // the same values, for merge checks
 };
 
 namespace {
@@ -688,6 +691,7 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->symbuf);
   (void)hipFree(s->d_stiles);
   (void)hipFree(s->sparts);
+  (void)hipFree(s->center);
   (void)hipFree(s->view);
   for (int k = 0; k < 3; ++k)
     for (int w = 0; w < 2; ++w)
@@ -751,14 +755,15 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
       hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb),
                          dim3((unsigned)((long long)nt * nsplit * s->h)), dim3(SK_WG), lds,
                          s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles + t0, nt,
-                         s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc);
+                         s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) err = e;
     }
   } else {
     hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
                        dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
-                       s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc);
+                       s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,
+                       s->center);
     err = hipGetLastError();
   }
   timing_mark(s, 0, true);
@@ -780,7 +785,7 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
 int sketch_merge(sk_handle dst, sk_handle src) {
   if (dst == nullptr || src == nullptr || dst == src) return SK_EINVAL;
   if (dst->d != src->d || dst->dv != src->dv || dst->p != src->p || dst->h != src->h ||
-      dst->layout != src->layout)
+      dst->layout != src->layout || dst->center_host != src->center_host)
     return SK_EMISMATCH;
   const long long c4 = dst->XS * dst->h / 4;
   const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
@@ -826,10 +831,34 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / qg) * s->h)),
                      dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
-                     s->dv, qg, (float)s->count, out, Z);
+                     s->dv, qg, (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
+  return SK_OK;
+}
+
+int sketch_set_center(sk_handle s, const float* c) {
+  if (s == nullptr) return SK_EINVAL;
+  if (s->count != 0) return SK_EINVAL;            // only on an empty sketch
+  if (c == nullptr) {
+    SK_TRY(hipStreamSynchronize(s->stream));
+    (void)hipFree(s->center);
+    s->center = nullptr;
+    s->center_host.clear();
+    return SK_OK;
+  }
+  if (!aligned16(c)) return SK_EINVAL;
+  const size_t bytes = sizeof(float) * (size_t)s->h * s->d;
+  SK_TRY(hipStreamSynchronize(s->stream));
+  if (s->center == nullptr && hipMalloc(&s->center, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    s->center = nullptr;
+    return SK_ENOMEM;
+  }
+  s->center_host.assign((size_t)s->h * s->d, 0.f);
+  SK_TRY(hipMemcpy(s->center, c, bytes, hipMemcpyDeviceToDevice));
+  SK_TRY(hipMemcpy(s->center_host.data(), s->center, bytes, hipMemcpyDeviceToHost));
   return SK_OK;
 }
 
@@ -843,11 +872,11 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
   timing_mark(s, 2, false);
   hipLaunchKernelGGL(sk_step_kernel, dim3((unsigned)((long long)nt * s->h)), dim3(256), 0,
                      s->stream, s->state, s->XS, s->d_stiles, nt, s->d, s->dv, s->logd, k, v,
-                     q, s->tb, s->sparts);
+                     q, s->tb, s->sparts, s->center);
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 2, true);
   hipLaunchKernelGGL(sk_step_finish, dim3((unsigned)s->h), dim3(256), 0, s->stream, s->sparts,
-                     nt, s->dv, (float)(s->count + 1), out, Z);
+                     nt, s->d, s->dv, (float)(s->count + 1), q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   s->count += 1;

@@ -211,7 +211,9 @@ void sk_query_kernel(const float* __restrict__ Q, long long m,
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
                      int ntiles, int nqt, long long PB, long long m, int d, int dv, int qg,
-                     float count, float* __restrict__ out, float* __restrict__ Z) {
+                     float count, const float* __restrict__ Q,
+                     const float* __restrict__ center, float* __restrict__ out,
+                     float* __restrict__ Z) {
   __shared__ long long tp[SK_QFIN_LDS];
   __shared__ int tc[SK_QFIN_LDS];
   __shared__ int tt[SK_QFIN_LDS];
@@ -272,5 +274,16 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
   __syncthreads();
   const long long q = qbase + ql;
   if (act && col >= d && q < m) out[(head * m + q) * dv + (col - d)] = cs[tid] / zq[ql];
-  if (tid < qg && qbase + tid < m) Z[head * m + qbase + tid] = zq[tid];
+  // with a centre c the moments are those of k - c: the returned Zhat carries
+  // e^{<q,c>}, which cancels in ohat
+  if (tid < qg && qbase + tid < m) {
+    float f = 1.f;
+    if (center != nullptr) {
+      const float* q = Q + (head * m + qbase + tid) * d;
+      float dot = 0.f;
+      for (int e = 0; e < d; ++e) dot += q[e] * center[head * d + e];
+      f = expf(dot);
+    }
+    Z[head * m + qbase + tid] = zq[tid] * f;
+  }
 }

@@ -43,7 +43,7 @@ void sk_step_kernel(float* __restrict__ X, long long head_stride,
                     const StepTile* __restrict__ tiles, int ntiles, int d, int dv, int logd,
                     const float* __restrict__ kin, const float* __restrict__ vin,
                     const float* __restrict__ qin, SymTables tb,
-                    float* __restrict__ parts) {
+                    float* __restrict__ parts, const float* __restrict__ center) {
   __shared__ float ks[128], vs[128], qs[128];
   __shared__ float fk[ST_ROWS], fq[ST_ROWS];
   __shared__ int lastr[ST_ROWS], lmulr[ST_ROWS];
@@ -53,7 +53,7 @@ void sk_step_kernel(float* __restrict__ X, long long head_stride,
   const long long head = blockIdx.x / ntiles;
   const StepTile T = tiles[tile];
   for (int i = tid; i < d; i += 256) {
-    ks[i] = kin[head * d + i];
+    ks[i] = kin[head * d + i] - (center != nullptr ? center[head * d + i] : 0.f);
     qs[i] = qin[head * d + i];
   }
   for (int i = tid; i < dv; i += 256) vs[i] = vin[head * dv + i];
@@ -152,9 +152,11 @@ void sk_step_kernel(float* __restrict__ X, long long head_stride,
 }
 
 // Per head: Zhat = count + the tiles' Zhat parts in tile order, Ntilde likewise,
-// ohat = Ntilde / Zhat.
+// ohat = Ntilde / Zhat; with a centre c the moments are those of k - c and the
+// returned Zhat carries the factor e^{<q,c>} (which cancels in ohat).
 __global__ __launch_bounds__(256)
-void sk_step_finish(const float* __restrict__ parts, int ntiles, int dv, float count,
+void sk_step_finish(const float* __restrict__ parts, int ntiles, int d, int dv, float count,
+                    const float* __restrict__ qin, const float* __restrict__ center,
                     float* __restrict__ out, float* __restrict__ Z) {
   __shared__ float zs;
   const int tid = threadIdx.x;
@@ -169,7 +171,13 @@ void sk_step_finish(const float* __restrict__ parts, int ntiles, int dv, float c
     }
     if (t < ntiles) z0 += P[(long long)t * (1 + dv)];
     zs = (z0 + z1) + count;
-    Z[head] = zs;
+    float f = 1.f;
+    if (center != nullptr) {
+      float dot = 0.f;
+      for (int e = 0; e < d; ++e) dot += qin[head * d + e] * center[head * d + e];
+      f = expf(dot);
+    }
+    Z[head] = zs * f;
   }
   __syncthreads();
   for (int c = tid; c < dv; c += 256) {

@@ -112,7 +112,8 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
                         long long n, int d, int dv, const SymUpdTile& T, const SymTables& tb,
                         long long split, long long head, long long keys_per_split,
                         float* __restrict__ out, long long head_stride,
-                        long long split_stride, int accumulate) {
+                        long long split_stride, int accumulate,
+                        const float* __restrict__ center) {
   static_assert(RB * CB <= 16 && 64 * RB <= SY_NS, "tile shape");
   constexpr int LDK = SY_LDK;
   constexpr int NPF = 4;              // float4 per thread per stage, for d, dv <= 128
@@ -121,6 +122,7 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
   float* Ks = lds;                                  // [d + 2][LDK]
   float* Vs = Ks + (d + 2) * LDK;                   // [dv][LDK]
   float* P = Vs + dv * LDK;                         // [SY_KB][SY_LDP]
+  float* Cs = P + SY_KB * SY_LDP;                   // [d] the sketch's centre
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
@@ -186,6 +188,13 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
 
   const int nK4 = SY_KB * d / 4, nV4 = SY_KB * dv / 4;
   const int d4 = d >> 2, dv4 = dv >> 2;
+  // keys are shifted by the sketch's centre as they are staged into LDS (the
+  // centre is kept in LDS); rows past the key range stay zero
+  const bool centered = center != nullptr;
+  if (centered) {   // uniform: every thread takes the same branch
+    for (int i = tid; i < d; i += SK_WG) Cs[i] = center[head * d + i];
+    __syncthreads();
+  }
   float4 kreg[NPF], vreg[NPF];
   auto fetch = [&](long long kb0) {
     const long long left = k_end - kb0;
@@ -204,15 +213,21 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
 
   if (k_begin < k_end) fetch(k_begin);
   for (long long kb0 = k_begin; kb0 < k_end; kb0 += SY_KB) {
+    const long long left = k_end - kb0;
+    const int nk = left < SY_KB ? (int)left : SY_KB;
 #pragma unroll
     for (int r = 0; r < NPF; ++r) {
       const int i = tid + r * SK_WG;
       if (i < nK4) {
         const int key = i / d4, c = 4 * (i - key * d4);
-        Ks[(c + 0) * LDK + key] = kreg[r].x;
-        Ks[(c + 1) * LDK + key] = kreg[r].y;
-        Ks[(c + 2) * LDK + key] = kreg[r].z;
-        Ks[(c + 3) * LDK + key] = kreg[r].w;
+        float4 kv = kreg[r];
+        if (centered && key < nk) {
+          kv.x -= Cs[c]; kv.y -= Cs[c + 1]; kv.z -= Cs[c + 2]; kv.w -= Cs[c + 3];
+        }
+        Ks[(c + 0) * LDK + key] = kv.x;
+        Ks[(c + 1) * LDK + key] = kv.y;
+        Ks[(c + 2) * LDK + key] = kv.z;
+        Ks[(c + 3) * LDK + key] = kv.w;
       }
       if (i < nV4) {
         const int key = i / dv4, c = 4 * (i - key * dv4);
@@ -289,7 +304,8 @@ void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__
                           const SymUpdTile* __restrict__ tiles, int ntiles, SymTables tb,
                           long long keys_per_split, int nsplit, int nhead,
                           float* __restrict__ out, long long head_stride,
-                          long long split_stride, int accumulate) {
+                          long long split_stride, int accumulate,
+                          const float* __restrict__ center) {
   const long long total = (long long)ntiles * nsplit * nhead;
   const long long lg = xcd_remap(blockIdx.x, total);
   const int tile = (int)(lg % ntiles);
@@ -297,7 +313,7 @@ void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__
   const long long head = lg / ((long long)ntiles * nsplit);
   const SymUpdTile T = tiles[tile];
   sk_sym_update_tile<RB, CB>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
-                             head_stride, split_stride, accumulate);
+                             head_stride, split_stride, accumulate, center);
 }
 
 // ---------------------------------------------------------------------------

@@ -33,7 +33,8 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
                     long long n, int d, int dv, int logd, const UpdTile& T,
                     long long split, long long head, long long keys_per_split,
                     float* __restrict__ out, long long head_stride,
-                    long long split_stride, int accumulate) {
+                    long long split_stride, int accumulate,
+                    const float* __restrict__ center) {
   constexpr int TM = SK_WG / WC;      // 256, 128 or 64 rows
   constexpr int TN = 64 * WC;         // 64, 128 or 256 columns
   constexpr int LDL = TM + SK_PAD;
@@ -54,6 +55,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   float* Vs = Ks + d * LDK;           // [dv][LDK]
   float* Lt = Vs + dv * LDK;          // [SK_KB][LDL]
   float* Rt = Lt + SK_KB * LDL;       // [SK_KB][LDR]
+  float* Cs = Rt + SK_KB * LDR;       // [d] the sketch's centre
 
   const long long k_begin = split * keys_per_split;
   long long k_end = k_begin + keys_per_split;
@@ -100,6 +102,13 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
 
   // Next stage's K and V rows are fetched into registers while the MFMAs of the
   // current stage run; rows past the key range read as zero.
+  // keys are shifted by the sketch's centre as they are staged into LDS (the
+  // centre is kept in LDS); rows past the key range stay zero
+  const bool centered = center != nullptr;
+  if (centered) {   // uniform: every thread takes the same branch
+    for (int i = tid; i < d; i += SK_WG) Cs[i] = center[head * d + i];
+    __syncthreads();
+  }
   float4 kreg[NPF], vreg[NPF];
   auto fetch = [&](long long kb0) {
     const long long left = k_end - kb0;
@@ -119,15 +128,21 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   if (k_begin < k_end) fetch(k_begin);
   for (long long kb0 = k_begin; kb0 < k_end; kb0 += SK_KB) {
     // 1. this stage's K and V rows -> LDS, transposed
+    const long long left = k_end - kb0;
+    const int nk = left < SK_KB ? (int)left : SK_KB;
 #pragma unroll
     for (int r = 0; r < NPF; ++r) {
       const int i = tid + r * SK_WG;
       if (i < nK4) {
         const int key = i / d4, c = 4 * (i - key * d4);
-        Ks[(c + 0) * LDK + key] = kreg[r].x;
-        Ks[(c + 1) * LDK + key] = kreg[r].y;
-        Ks[(c + 2) * LDK + key] = kreg[r].z;
-        Ks[(c + 3) * LDK + key] = kreg[r].w;
+        float4 kv = kreg[r];
+        if (centered && key < nk) {
+          kv.x -= Cs[c]; kv.y -= Cs[c + 1]; kv.z -= Cs[c + 2]; kv.w -= Cs[c + 3];
+        }
+        Ks[(c + 0) * LDK + key] = kv.x;
+        Ks[(c + 1) * LDK + key] = kv.y;
+        Ks[(c + 2) * LDK + key] = kv.z;
+        Ks[(c + 3) * LDK + key] = kv.w;
       }
       if (i < nV4) {
         const int key = i / dv4, c = 4 * (i - key * dv4);
@@ -228,7 +243,8 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                       const UpdTile* __restrict__ tiles, int ntiles,
                       long long keys_per_split, int nsplit, int nhead,
                       float* __restrict__ out, long long head_stride,
-                      long long split_stride, int accumulate) {
+                      long long split_stride, int accumulate,
+                      const float* __restrict__ center) {
   // 1-D grid over (tile, split, head), tile fastest, remapped per XCD
   const long long total = (long long)ntiles * nsplit * nhead;
   const long long lg = xcd_remap(blockIdx.x, total);
@@ -238,11 +254,11 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   const UpdTile T = tiles[tile_id];
   if (T.wc == 2)
     sk_update_tile<2>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
-                      head_stride, split_stride, accumulate);
+                      head_stride, split_stride, accumulate, center);
   else if (T.wc == 1)
     sk_update_tile<1>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
-                      head_stride, split_stride, accumulate);
+                      head_stride, split_stride, accumulate, center);
   else
     sk_update_tile<4>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
-                      head_stride, split_stride, accumulate);
+                      head_stride, split_stride, accumulate, center);
 }

@@ -93,6 +93,23 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
  */
 int sketch_layout(sk_handle s, int* layout, int64_t* rows);
 
+/*
+ * sketch_set_center -- recentre the expansion at a fixed centre c per head
+ * ("Metodologia", pillar "Particionamento de Espaço e Recentramento": a dense
+ * cluster is shifted to the origin, which shrinks the radius the expansion
+ * covers).  Since exp<q,k> = e^{<q,c>} exp<q, k - c>, the sketch keeps the
+ * moments of the shifted keys k - c and answers
+ *     Z = e^{<q,c>} sum_j <q^(x)j, M_j(k - c)> / j!,    out unchanged by the factor.
+ * Only on an empty sketch (count 0, e.g. right after create or reset; reset
+ * keeps the centre).  c: device [h][d] (copied; the caller keeps ownership), or
+ * NULL to remove the centre.  Synchronises the handle's stream.  Merging needs
+ * equal centres (SK_EMISMATCH otherwise); sketch_state/sketch_export show the
+ * moments of the shifted keys.
+ * Errors: SK_EINVAL (NULL handle, misaligned c, sketch not empty), SK_ENOMEM,
+ * SK_EHIP.
+ */
+int sketch_set_center(sk_handle s, const float* c);
+
 /* sketch_destroy -- synchronises the handle's stream, frees everything the
  * handle owns.  NULL is accepted (no-op).  Returns SK_EHIP if a pending kernel
  * had failed (the memory is still freed). */
@@ -118,8 +135,8 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n);
 
 /*
  * sketch_merge -- dst += src (Merge-and-Reduce, merge step: moments add, counts
- * add).  src is unchanged.  Both handles must have equal (d, dv, p, h) and the
- * same layout; the work
+ * add).  src is unchanged.  Both handles must have equal (d, dv, p, h), the
+ * same layout and the same centre; the work
  * runs on dst's stream (the caller orders src's stream before it).
  * Errors: SK_EINVAL (NULL, dst == src), SK_EMISMATCH, SK_EHIP.
  */
