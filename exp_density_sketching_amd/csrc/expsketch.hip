@@ -127,18 +127,22 @@ int sym_query_rows() {
 // The multiset update kernel is instantiated per tile shape (rb, cb).
 using SymUpdateKernel = void (*)(const float*, const float*, long long, int, int,
                                  const SymUpdTile*, int, SymTables, long long, int, int,
-                                 float*, long long, long long, int, const float*);
-SymUpdateKernel sym_update_kernel_for(int rb, int cb) {
+                                 float*, long long, long long, int, const float*,
+                                 PendingReduce);
+SymUpdateKernel sym_update_kernel_for(int rb, int cb, bool center) {
+#define SY_PICK(RB_, CB_) \
+  return center ? sk_sym_update_kernel<RB_, CB_, true> : sk_sym_update_kernel<RB_, CB_, false>
   switch (rb * 8 + cb) {
-    case 4 * 8 + 1: return sk_sym_update_kernel<4, 1>;
-    case 4 * 8 + 2: return sk_sym_update_kernel<4, 2>;
-    case 4 * 8 + 4: return sk_sym_update_kernel<4, 4>;
-    case 2 * 8 + 1: return sk_sym_update_kernel<2, 1>;
-    case 2 * 8 + 2: return sk_sym_update_kernel<2, 2>;
-    case 2 * 8 + 4: return sk_sym_update_kernel<2, 4>;
-    case 1 * 8 + 4: return sk_sym_update_kernel<1, 4>;
+    case 4 * 8 + 1: SY_PICK(4, 1);
+    case 4 * 8 + 2: SY_PICK(4, 2);
+    case 4 * 8 + 4: SY_PICK(4, 4);
+    case 2 * 8 + 1: SY_PICK(2, 1);
+    case 2 * 8 + 2: SY_PICK(2, 2);
+    case 2 * 8 + 4: SY_PICK(2, 4);
+    case 1 * 8 + 4: SY_PICK(1, 4);
     default: return nullptr;
   }
+#undef SY_PICK
 }
 
 // The query kernel is instantiated per log2(d) (d = 4 .. 128).
@@ -196,6 +200,15 @@ struct sk_sketch {
   // fixed centre (sketch_set_center): moments are of k - c; null = no centre
   float* center = nullptr;                 // device [h][d]
   std::vector<float> center_host;          // the same values, for merge checks
+  // split partials of update calls: two buffers used in turn; the last call's
+  // partials are added into the state by the next update launch (or by a
+  // reduce kernel before anything else reads or writes the state)
+  float* pbuf[2] = {nullptr, nullptr};
+  size_t pbuf_floats = 0;                  // capacity of each buffer
+  int pcur = 0;                            // buffer the next call writes
+  float* pend = nullptr;                   // partials not yet in the state
+  int pend_ns = 0;
+  hipEvent_t flush_ev = nullptr;           // orders a flush before another stream
 };
 
 namespace {
@@ -532,6 +545,24 @@ int choose_update_splits(const sk_sketch* s, long long n) {
   return best;
 }
 
+// Bytes of each of the two split-partials buffers above which an update call
+// takes per-call partials and reduces them at once instead.
+constexpr size_t kDeferBytes = size_t(1) << 30;
+
+// Adds the last update call's pending partials into the state (fixed split order).
+int flush_pending(sk_sketch* s) {
+  if (s->pend == nullptr) return SK_OK;
+  const long long c4 = s->XS * s->h / 4;
+  const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
+  hipLaunchKernelGGL(sk_split_reduce_kernel, dim3(grid), dim3(256), 0, s->stream,
+                     reinterpret_cast<float4*>(s->state),
+                     reinterpret_cast<const float4*>(s->pend), c4, s->pend_ns, c4);
+  s->pend = nullptr;
+  s->pend_ns = 0;
+  SK_TRY(hipGetLastError());
+  return SK_OK;
+}
+
 int launch_fill_zero(float* p, long long count, hipStream_t st) {
   const long long c4 = count / 4;
   if (c4 == 0) return SK_OK;
@@ -646,12 +677,15 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
   for (size_t g = 0; ok && sym && g + 1 < s->sgroup.size(); ++g) {
     const SymUpdTile& t0 = s->sutiles[s->sgroup[g]];
-    ok = hipFuncSetAttribute((const void*)sym_update_kernel_for(t0.rb, t0.cb),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess;
+    for (int cen = 0; cen < 2 && ok; ++cen)
+      ok = hipFuncSetAttribute((const void*)sym_update_kernel_for(t0.rb, t0.cb, cen != 0),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess;
   }
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
-         hipFuncSetAttribute((const void*)sk_update_kernel,
+         hipFuncSetAttribute((const void*)sk_update_kernel<false>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
+         hipFuncSetAttribute((const void*)sk_update_kernel<true>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
          hipFuncSetAttribute((const void*)query_kernel_for(s->logd),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
@@ -692,6 +726,9 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->d_stiles);
   (void)hipFree(s->sparts);
   (void)hipFree(s->center);
+  (void)hipFree(s->pbuf[0]);
+  (void)hipFree(s->pbuf[1]);
+  if (s->flush_ev != nullptr) (void)hipEventDestroy(s->flush_ev);
   (void)hipFree(s->view);
   for (int k = 0; k < 3; ++k)
     for (int w = 0; w < 2; ++w)
@@ -709,6 +746,7 @@ int sketch_set_stream(sk_handle s, void* hip_stream) {
 int sketch_reset(sk_handle s) {
   if (s == nullptr) return SK_EINVAL;
   s->count = 0;
+  s->pend = nullptr;            // pending partials belong to the old contents
   return launch_fill_zero(s->state, s->XS * s->h, s->stream);
 }
 
@@ -733,49 +771,100 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   const int nsplit = (int)((n + kps - 1) / kps);
   const bool sym = s->layout == SK_LAYOUT_SYM;
   const int ntiles = update_tile_count(s);
-  if ((long long)ntiles * nsplit * s->h > 0x7fffffffLL) return SK_EINVAL;
-  const size_t lds = sym ? sym_update_lds_bytes(s->d, s->dv) : update_lds_bytes(s->d, s->dv);
   const long long total = s->XS * s->h;
-  float* parts = nullptr;
-  if (nsplit > 1 &&
-      hipMallocAsync((void**)&parts, sizeof(float) * (size_t)total * nsplit, s->stream) !=
-          hipSuccess) {
-    (void)hipGetLastError();
-    return SK_ENOMEM;
+  const long long rmax = (total / 4 + SK_RED4 - 1) / SK_RED4;     // reduce workgroups
+  if ((long long)ntiles * nsplit * s->h + rmax > 0x7fffffffLL) return SK_EINVAL;
+  const size_t lds = sym ? sym_update_lds_bytes(s->d, s->dv) : update_lds_bytes(s->d, s->dv);
+  int rc = SK_OK;
+  float* dst = s->state;
+  float* tmp = nullptr;         // per-call partials (states too large to defer)
+  bool deferred = false;
+  PendingReduce red{};
+  red.state = reinterpret_cast<float4*>(s->state);
+  red.count4 = total / 4;
+  if (nsplit == 1) {
+    rc = flush_pending(s);      // this call adds into the state itself
+    if (rc != SK_OK) return rc;
+  } else {
+    const size_t need = (size_t)total * nsplit;
+    if (need * sizeof(float) <= kDeferBytes) {
+      if (s->pbuf_floats < need) {
+        rc = flush_pending(s);
+        if (rc != SK_OK) return rc;
+        SK_TRY(hipStreamSynchronize(s->stream));
+        (void)hipFree(s->pbuf[0]);
+        (void)hipFree(s->pbuf[1]);
+        s->pbuf[0] = s->pbuf[1] = nullptr;
+        s->pbuf_floats = 0;
+        if (hipMalloc(&s->pbuf[0], need * sizeof(float)) == hipSuccess &&
+            hipMalloc(&s->pbuf[1], need * sizeof(float)) == hipSuccess) {
+          s->pbuf_floats = need;
+        } else {
+          (void)hipGetLastError();
+          (void)hipFree(s->pbuf[0]);
+          (void)hipFree(s->pbuf[1]);
+          s->pbuf[0] = s->pbuf[1] = nullptr;
+        }
+      }
+      deferred = s->pbuf_floats >= need;
+    }
+    if (deferred) {
+      dst = s->pbuf[s->pcur];
+      if (s->pend != nullptr) {
+        red.parts = reinterpret_cast<const float4*>(s->pend);
+        red.nsplit = s->pend_ns;
+      }
+    } else {
+      rc = flush_pending(s);
+      if (rc != SK_OK) return rc;
+      if (hipMallocAsync((void**)&tmp, sizeof(float) * need, s->stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return SK_ENOMEM;
+      }
+      dst = tmp;
+    }
   }
-  float* dst = nsplit > 1 ? parts : s->state;
   const long long sstride = nsplit > 1 ? total : 0;
   const int acc = nsplit > 1 ? 0 : 1;
+  const long long rwgs = red.parts != nullptr ? rmax : 0;
   hipError_t err = hipSuccess;
   timing_mark(s, 0, false);
   if (sym) {
     for (size_t g = 0; g + 1 < s->sgroup.size(); ++g) {
       const int t0 = s->sgroup[g], nt = s->sgroup[g + 1] - t0;
       const SymUpdTile& sh = s->sutiles[t0];
-      hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb),
-                         dim3((unsigned)((long long)nt * nsplit * s->h)), dim3(SK_WG), lds,
-                         s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles + t0, nt,
-                         s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center);
+      PendingReduce rg = red;                  // the reduce rides on the first launch
+      if (g > 0) rg.parts = nullptr;
+      const long long extra = g == 0 ? rwgs : 0;
+      hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb, s->center != nullptr),
+                         dim3((unsigned)((long long)nt * nsplit * s->h + extra)), dim3(SK_WG),
+                         lds, s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles + t0,
+                         nt, s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center, rg);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) err = e;
     }
   } else {
-    hipLaunchKernelGGL(sk_update_kernel, dim3((unsigned)((long long)ntiles * nsplit * s->h)),
-                       dim3(SK_WG), lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
+    hipLaunchKernelGGL(s->center != nullptr ? sk_update_kernel<true> : sk_update_kernel<false>,
+                       dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)), dim3(SK_WG),
+                       lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
                        s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,
-                       s->center);
+                       s->center, red);
     err = hipGetLastError();
   }
   timing_mark(s, 0, true);
-  if (nsplit > 1) {
+  if (deferred) {
+    s->pend = dst;
+    s->pend_ns = nsplit;
+    s->pcur ^= 1;
+  } else if (tmp != nullptr) {
     const long long c4 = total / 4;
     const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
     hipLaunchKernelGGL(sk_split_reduce_kernel, dim3(grid), dim3(256), 0, s->stream,
                        reinterpret_cast<float4*>(s->state),
-                       reinterpret_cast<const float4*>(parts), c4, nsplit, c4);
+                       reinterpret_cast<const float4*>(tmp), c4, nsplit, c4);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) err = e;
-    (void)hipFreeAsync(parts, s->stream);
+    (void)hipFreeAsync(tmp, s->stream);
   }
   if (err != hipSuccess) return SK_EHIP;
   s->count += n;
@@ -787,6 +876,18 @@ int sketch_merge(sk_handle dst, sk_handle src) {
   if (dst->d != src->d || dst->dv != src->dv || dst->p != src->p || dst->h != src->h ||
       dst->layout != src->layout || dst->center_host != src->center_host)
     return SK_EMISMATCH;
+  // src's pending partials go into its state on src's stream; dst's stream then
+  // waits for that before reading it
+  const bool src_pending = src->pend != nullptr;
+  int rc = flush_pending(src);
+  if (rc == SK_OK && src_pending && src->stream != dst->stream) {
+    if (src->flush_ev == nullptr)
+      SK_TRY(hipEventCreateWithFlags(&src->flush_ev, hipEventDisableTiming));
+    SK_TRY(hipEventRecord(src->flush_ev, src->stream));
+    SK_TRY(hipStreamWaitEvent(dst->stream, src->flush_ev, 0));
+  }
+  if (rc == SK_OK) rc = flush_pending(dst);
+  if (rc != SK_OK) return rc;
   const long long c4 = dst->XS * dst->h / 4;
   const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
   hipLaunchKernelGGL(sk_add_kernel, dim3(grid), dim3(256), 0, dst->stream,
@@ -801,6 +902,10 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (s == nullptr || m < 0) return SK_EINVAL;
   if (m == 0) return SK_OK;
   if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
+  {
+    const int rc = flush_pending(s);
+    if (rc != SK_OK) return rc;
+  }
   const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
   const long long nlaunch = std::max<long long>(
@@ -869,6 +974,10 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
     return SK_EINVAL;
   const int nt = (int)s->stiles.size();
   if ((long long)nt * s->h > 0x7fffffffLL) return SK_EINVAL;
+  {
+    const int rc = flush_pending(s);
+    if (rc != SK_OK) return rc;
+  }
   timing_mark(s, 2, false);
   hipLaunchKernelGGL(sk_step_kernel, dim3((unsigned)((long long)nt * s->h)), dim3(256), 0,
                      s->stream, s->state, s->XS, s->d_stiles, nt, s->d, s->dv, s->logd, k, v,
@@ -913,6 +1022,10 @@ int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count) {
 
 int sketch_export(sk_handle s, float* dst) {
   if (s == nullptr || dst == nullptr || !aligned16(dst)) return SK_EINVAL;
+  {
+    const int rc = flush_pending(s);
+    if (rc != SK_OK) return rc;
+  }
   if (s->layout == SK_LAYOUT_SYM) {
     const long long total = s->Dsym * (1 + s->dv) * s->h;
     const int grid = (int)std::min<long long>((total + 255) / 256, 16384);

@@ -32,6 +32,7 @@
 #pragma once
 
 #include "sk_common.h"
+#include "sk_elementwise.h"
 
 // v_mfma_f32_16x16x4_f32: D(16x16) += A(16x4) * B(4x16), fp32 in and out.
 // Lane l supplies A[l%16][l/16] and B[l/16][l%16]; accumulator register r of lane
@@ -106,7 +107,7 @@ struct SymQryTile {
 //   3. per k-step of 4 keys, each lane forms its A operand P[key][slot(row)] *
 //      k[last(row)] in a register and reads its B operand u[key][col] from LDS.
 // ---------------------------------------------------------------------------
-template <int RB, int CB>
+template <int RB, int CB, bool CENTER>
 __device__ __forceinline__
 void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V,
                         long long n, int d, int dv, const SymUpdTile& T, const SymTables& tb,
@@ -190,7 +191,7 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
   const int d4 = d >> 2, dv4 = dv >> 2;
   // keys are shifted by the sketch's centre as they are staged into LDS (the
   // centre is kept in LDS); rows past the key range stay zero
-  const bool centered = center != nullptr;
+  constexpr bool centered = CENTER;
   if (centered) {   // uniform: every thread takes the same branch
     for (int i = tid; i < d; i += SK_WG) Cs[i] = center[head * d + i];
     __syncthreads();
@@ -297,7 +298,7 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
 // count its own: at most 128 VGPRs, four waves per SIMD, so the stages of other
 // workgroups cover the latency of a workgroup's barriers (two waves for the
 // 16-block shape, whose accumulators alone take 64 registers).
-template <int RB, int CB>
+template <int RB, int CB, bool CENTER>
 __global__ __launch_bounds__(SK_WG, (RB * CB >= 16) ? 2 : 4)
 void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                           long long n, int d, int dv,
@@ -305,14 +306,18 @@ void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__
                           long long keys_per_split, int nsplit, int nhead,
                           float* __restrict__ out, long long head_stride,
                           long long split_stride, int accumulate,
-                          const float* __restrict__ center) {
+                          const float* __restrict__ center, PendingReduce red) {
   const long long total = (long long)ntiles * nsplit * nhead;
+  if ((long long)blockIdx.x >= total) {   // the previous call's partials -> state
+    pending_reduce_wg(red, (long long)blockIdx.x - total);
+    return;
+  }
   const long long lg = xcd_remap(blockIdx.x, total);
   const int tile = (int)(lg % ntiles);
   const long long split = (lg / ntiles) % nsplit;
   const long long head = lg / ((long long)ntiles * nsplit);
   const SymUpdTile T = tiles[tile];
-  sk_sym_update_tile<RB, CB>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
+  sk_sym_update_tile<RB, CB, CENTER>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
                              head_stride, split_stride, accumulate, center);
 }
 

@@ -26,8 +26,9 @@
 #pragma once
 
 #include "sk_common.h"
+#include "sk_elementwise.h"
 
-template <int WC>
+template <int WC, bool CENTER>
 __device__ __forceinline__
 void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
                     long long n, int d, int dv, int logd, const UpdTile& T,
@@ -104,7 +105,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   // current stage run; rows past the key range read as zero.
   // keys are shifted by the sketch's centre as they are staged into LDS (the
   // centre is kept in LDS); rows past the key range stay zero
-  const bool centered = center != nullptr;
+  constexpr bool centered = CENTER;
   if (centered) {   // uniform: every thread takes the same branch
     for (int i = tid; i < d; i += SK_WG) Cs[i] = center[head * d + i];
     __syncthreads();
@@ -237,6 +238,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
 }
 
 // One launch covers every tile of every level; the tile's shape picks the body.
+template <bool CENTER>
 __global__ __launch_bounds__(SK_WG, 2)
 void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                       long long n, int d, int dv, int logd,
@@ -244,21 +246,26 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                       long long keys_per_split, int nsplit, int nhead,
                       float* __restrict__ out, long long head_stride,
                       long long split_stride, int accumulate,
-                      const float* __restrict__ center) {
-  // 1-D grid over (tile, split, head), tile fastest, remapped per XCD
+                      const float* __restrict__ center, PendingReduce red) {
+  // 1-D grid over (tile, split, head), tile fastest, remapped per XCD; blocks
+  // past them add the previous call's partials into the state
   const long long total = (long long)ntiles * nsplit * nhead;
+  if ((long long)blockIdx.x >= total) {
+    pending_reduce_wg(red, (long long)blockIdx.x - total);
+    return;
+  }
   const long long lg = xcd_remap(blockIdx.x, total);
   const int tile_id = (int)(lg % ntiles);
   const long long split = (lg / ntiles) % nsplit;
   const long long head = lg / ((long long)ntiles * nsplit);
   const UpdTile T = tiles[tile_id];
   if (T.wc == 2)
-    sk_update_tile<2>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<2, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else if (T.wc == 1)
-    sk_update_tile<1>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<1, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else
-    sk_update_tile<4>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<4, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
 }

@@ -247,3 +247,42 @@ def test_kernel_timing_events():
     E.sketch_update(sk, Kg[:, :4096], Vg[:, :4096])
     assert E.sketch_kernel_times(sk, "update") == []
     sk.destroy()
+
+
+@pytest.mark.parametrize("layout", ["full", "sym"])
+def test_pending_partials_are_always_added(layout):
+    """Split update calls leave their partials for the next launch to add; every
+    reader (export, query, merge) and reset must see the right state.  Calls of
+    4096 keys (split) alternate with calls of 100 keys (one split, added in
+    place); a reset drops what is pending; a merge takes pending partials of
+    both sides."""
+    w = CONFIGS[2].scaled(n=25000, m=8)
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = gpu(K, V, Q)
+    sizes = [4096, 4096, 100, 4096, 257, 4096, 4096]
+    bounds = np.cumsum([0] + sizes)
+    a = E.sketch_create(w.d, w.dv, w.p, 1, layout)
+    # garbage that the reset must drop, pending at the time of the reset
+    E.sketch_update(a, Kg[:, :4096], Vg[:, :4096])
+    E.sketch_update(a, Kg[:, 4096:8192], Vg[:, 4096:8192])
+    E.sketch_reset(a)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        E.sketch_update(a, Kg[:, lo:hi], Vg[:, lo:hi])
+    n_a = int(bounds[-1])
+    # a second sketch with its own pending partials, merged into the first
+    b = E.sketch_create(w.d, w.dv, w.p, 1, layout)
+    E.sketch_update(b, Kg[:, n_a:n_a + 4096 + 2], Vg[:, n_a:n_a + 4096 + 2])
+    E.sketch_merge(a, b)
+    n = n_a + 4096 + 2
+    S = host(E.sketch_export(a))[0][0]
+    Ref = oracle.SymMomentSketch if layout == "sym" else oracle.MomentSketch
+    ref = Ref(w.d, w.dv, w.p).update(K[0, :n], V[0, :n]).canonical_state()
+    mag = Ref(w.d, w.dv, w.p).update(np.abs(K[0, :n].astype(np.float64)),
+                                     np.abs(V[0, :n].astype(np.float64))).canonical_state()
+    assert a.count == n
+    assert np.all(np.abs(S - ref) <= 2e-6 * mag + 1e-30)
+    out, Z = host(*E.sketch_query(a, Qg))
+    o_ref, z_ref = oracle.sketch_direct(K[0, :n], V[0, :n], Q[0], w.p)
+    assert zrel(Z[0], z_ref) <= SK_Z_REL and oabs(out[0], o_ref) <= SK_O_ABS
+    a.destroy()
+    b.destroy()
