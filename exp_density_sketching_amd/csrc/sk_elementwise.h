@@ -27,6 +27,7 @@ __device__ __forceinline__ void split_reduce_one(float4* __restrict__ state,
                                                  long long i, int nsplit,
                                                  long long split_stride4) {
   float4 t = parts[i];
+#pragma unroll 8
   for (int sp = 1; sp < nsplit; ++sp) {
     const float4 b = parts[sp * split_stride4 + i];
     t.x += b.x; t.y += b.y; t.z += b.z; t.w += b.w;
@@ -47,9 +48,10 @@ void sk_split_reduce_kernel(float4* __restrict__ state, const float4* __restrict
 // The previous update call's split partials, added into the state by extra
 // workgroups of the next update launch (queued after its tiles, so they run in
 // the launch's tail).  Workgroup w of them takes float4 [w * SK_RED4, (w + 1) *
-// SK_RED4).  The launch's own tiles write the other partials buffer, never the
-// state, so the two do not touch the same memory.
-#define SK_RED4 1024
+// SK_RED4), one per thread, so small states still spread over many workgroups.
+// The launch's own tiles write the other partials buffer, never the state, so
+// the two do not touch the same memory.
+#define SK_RED4 256
 struct PendingReduce {
   float4* state;
   const float4* parts;   // null: nothing pending
