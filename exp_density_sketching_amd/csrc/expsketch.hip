@@ -1094,7 +1094,11 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   if (rc != SK_OK) return rc;
   const int bmax = std::max(d, dv);
   const bool decode = m <= 8;
-  const long long nqt = decode ? 1 : (m + 255) / 256;
+  // many queries: fp32 MFMA when the rows are wide enough to fill its operands,
+  // one thread per query on the VALU for d, dv <= 8 (there the value columns
+  // would be padded 4x and the exponentials dominate)
+  const bool use_mfma = !decode && bmax >= 16;
+  const long long nqt = decode ? 1 : (m + (use_mfma ? SK_XQ : 256) - 1) / (use_mfma ? SK_XQ : 256);
   // EXPSKETCH_EXACT_MINKEYS=<k> sets the fewest keys per slice (tuning aid).
   static const long long min_keys_env = [] {
     const char* v = std::getenv("EXPSKETCH_EXACT_MINKEYS");
@@ -1150,20 +1154,37 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     }
 #undef SK_DEC_B
 #undef SK_DEC
-  } else {
+  } else if (!use_mfma) {
     dim3 grid((unsigned)(nsplit * nqt), h), blk(256);
-#define SK_TIL(BB, KS)                                                                 \
-  hipLaunchKernelGGL((sk_exact_tiled<BB, KS>), grid, blk, 0, st, K, V, nn, d, dv, Q, mm, \
-                     kps, nsplit, parts)
-    switch (bmax) {
-      case 4: SK_TIL(4, 32); break;
-      case 8: SK_TIL(8, 32); break;
-      case 16: SK_TIL(16, 32); break;
-      case 32: SK_TIL(32, 32); break;
-      case 64: SK_TIL(64, 32); break;
-      default: SK_TIL(128, 16); break;
+    if (bmax <= 4)
+      hipLaunchKernelGGL((sk_exact_tiled<4, 32>), grid, blk, 0, st, K, V, nn, d, dv, Q, mm,
+                         kps, nsplit, parts);
+    else
+      hipLaunchKernelGGL((sk_exact_tiled<8, 32>), grid, blk, 0, st, K, V, nn, d, dv, Q, mm,
+                         kps, nsplit, parts);
+  } else {
+    // fp32 MFMA: queries x keys, then values x keys; value columns in blocks of 32
+    dim3 grid((unsigned)(nsplit * nqt), h), blk(256);
+    const int ncb = dv <= 32 ? 1 : (dv <= 64 ? 2 : 4);
+#define SK_XM(DD, NC)                                                                \
+  hipLaunchKernelGGL((sk_exact_mfma<DD, NC>), grid, blk, 0, st, K, V, nn, dv, Q, mm, kps, \
+                     nsplit, parts)
+#define SK_XM_D(DD)                   \
+  switch (ncb) {                      \
+    case 1: SK_XM(DD, 1); break;      \
+    case 2: SK_XM(DD, 2); break;      \
+    default: SK_XM(DD, 4); break;     \
+  }
+    switch (d) {
+      case 4: SK_XM_D(4); break;
+      case 8: SK_XM_D(8); break;
+      case 16: SK_XM_D(16); break;
+      case 32: SK_XM_D(32); break;
+      case 64: SK_XM_D(64); break;
+      default: SK_XM_D(128); break;
     }
-#undef SK_TIL
+#undef SK_XM_D
+#undef SK_XM
   }
   hipError_t e1 = hipGetLastError();
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,

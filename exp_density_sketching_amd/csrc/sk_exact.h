@@ -12,9 +12,11 @@
 //   key row, each loading one float4 of K and one of V; the dot product is
 //   reduced across the G lanes with xor shuffles.  Each group walks U keys per
 //   step so that many 128-bit loads are in flight.
-// sk_exact_tiled   (many queries per head): one thread per query, key and value
-//   rows staged through LDS and read as broadcasts; per stage of 32 keys one
-//   rescale.
+// sk_exact_mfma    (many queries per head, d or dv >= 16): fp32 MFMA for both
+//   products (queries x keys, then values x keys), online softmax in between.
+// sk_exact_tiled   (many queries per head, d, dv <= 8): one thread per query, key
+//   and value rows staged through LDS and read as broadcasts; per stage of 32
+//   keys one rescale.
 // sk_exact_combine: folds the slice partials of each (head, query).
 #pragma once
 
@@ -34,6 +36,123 @@ __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
   for (int o = G / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
+}
+
+// sk_exact_mfma (many queries per head): one workgroup = 4 waves x 32 queries,
+// one key slice; per stage of 32 keys (K and V rows staged in LDS):
+//   S^T = K Q^T         v_mfma_f32_32x32x2_f32, rows = keys, columns = queries;
+//                       the lane's query components stay in registers
+//   online softmax      the stage's row maximum of a query is the larger of its
+//                       two lanes' 16 entries (one cross-lane exchange); p =
+//                       e^{s - mu}, previous sums rescaled by e^{mu_old - mu}
+//   O^T += V^T P^T      the same MFMA with P taken straight from the first
+//                       product's accumulator registers: an MFMA sums over its K
+//                       index in any order, so at k-step t each lane half uses
+//                       the key its register t holds, and reads that key's value
+//                       row from LDS as the other operand.
+// The partial record per (head, query, slice) is the one of sk_exact_decode.
+#define SK_XQ 128          // queries per workgroup (4 waves x 32)
+#define SK_XK 32           // keys per stage
+template <int D, int NCB>
+__global__ __launch_bounds__(256)
+void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
+                   long long n, int dv, const float* __restrict__ Q, long long m,
+                   long long keys_per_split, int nsplit, float* __restrict__ parts) {
+  constexpr int LDKE = D + 1;               // K stage row stride (keys x D)
+  constexpr int DVP = 32 * NCB;             // value columns, padded to 32
+  constexpr int LDV = DVP + 8;              // the two lane halves' rows 32 banks apart
+  __shared__ float Ks[SK_XK * LDKE];
+  __shared__ float Vs[SK_XK * LDV];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const long long split = blockIdx.x % nsplit;
+  const long long qt = blockIdx.x / nsplit;
+  const long long head = blockIdx.y;
+  const long long q = qt * SK_XQ + wave * 32 + l32;
+  const bool qok = q < m;
+  const long long k_begin = split * keys_per_split;
+  long long k_end = k_begin + keys_per_split;
+  if (k_end > n) k_end = n;
+  const float* Kh = K + head * n * D;
+  const float* Vh = V + head * n * dv;
+
+  float qreg[D / 2];                        // Q[q][2 st + g]
+#pragma unroll
+  for (int st = 0; st < D / 2; ++st)
+    qreg[st] = qok ? Q[(head * m + q) * D + 2 * st + g] : 0.f;
+
+  float mu = -INFINITY, l = 0.f;
+  floatx16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx16{0.f};
+
+  for (long long kb = k_begin; kb < k_end; kb += SK_XK) {
+    const long long left = k_end - kb;
+    const int nk = left < SK_XK ? (int)left : SK_XK;
+    for (int i = tid; i < SK_XK * D / 4; i += 256) {
+      const int key = i / (D / 4), e = 4 * (i - key * (D / 4));
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (key < nk) x = *reinterpret_cast<const float4*>(Kh + (kb + key) * D + e);
+      float* dst = Ks + key * LDKE + e;
+      dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+    }
+    for (int i = tid; i < SK_XK * DVP / 4; i += 256) {
+      const int key = i / (DVP / 4), c = 4 * (i - key * (DVP / 4));
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (key < nk && c < dv) x = *reinterpret_cast<const float4*>(Vh + (kb + key) * dv + c);
+      *reinterpret_cast<float4*>(Vs + key * LDV + c) = x;
+    }
+    __syncthreads();
+    floatx16 s = {0.f};
+#pragma unroll
+    for (int st = 0; st < D / 2; ++st)
+      s = mfma32x32x2(Ks[l32 * LDKE + 2 * st + g], qreg[st], s);
+    // s[r] = <q, k_key>, key = acc_row(r, lane) of the stage
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (acc_row(r, lane) >= nk) s[r] = -INFINITY;
+      mloc = fmaxf(mloc, s[r]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(mu, mloc);     // finite: every stage has a key
+    const float alpha = expf(mu - mnew);    // 0 on the first stage
+    float p[16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = expf(s[r] - mnew);             // 0 for keys past the slice
+      lsum += p[r];
+    }
+    l = l * alpha + lsum;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        acc[cb] = mfma32x32x2(Vs[acc_row(t, lane) * LDV + 32 * cb + l32], p[t], acc[cb]);
+    }
+    mu = mnew;
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 32, 64);               // the query's two lane halves
+  if (qok) {
+    float* P = parts + ((head * m + q) * nsplit + split) * (2 + dv);
+    if (g == 0) {
+      P[0] = mu;
+      P[1] = l;
+    }
+    // acc[cb][r] = sum_i p_i v_i[c], c = 32 cb + acc_row(r, lane)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * cb + acc_row(r, lane);
+        if (c < dv) P[2 + c] = acc[cb][r];
+      }
+  }
 }
 
 // partial record per (head, query, slice): [mu, l, acc[dv]]
