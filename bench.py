@@ -142,9 +142,10 @@ def decode_steps(w, E, torch, Kg, Vg, Qg, steps, exact_us):
     for layout in ("full", "sym"):
         sk = E.sketch_create(w.d, w.dv, w.p, w.h, layout)
         E.sketch_update(sk, Kg, Vg)
-        ks = [Kg[:, i].contiguous() for i in range(steps)]
-        vs = [Vg[:, i].contiguous() for i in range(steps)]
-        qs = [Qg[:, i % w.m].contiguous() for i in range(steps)]
+        cnt = max(steps, 3)                      # 3 warm-up steps
+        ks = [Kg[:, i].contiguous() for i in range(cnt)]
+        vs = [Vg[:, i].contiguous() for i in range(cnt)]
+        qs = [Qg[:, i % w.m].contiguous() for i in range(cnt)]
         out = torch.empty((w.h, w.dv), device="cuda")
         z = torch.empty((w.h,), device="cuda")
         for i in range(3):
@@ -343,6 +344,12 @@ def main():
         "query_kernel_mfma_frac": flop_per_key * w.h * w.m / t_qk / PEAK_FP32_MFMA,
         "update_call_us": call_dur * 1e6,
         "update_call_mfma_frac": flop_per_key * keys_per_call * w.h / call_dur / PEAK_FP32_MFMA,
+        "exact_batched": {"ms": t_ex * 1e3, "flop": 2.0 * w.h * w.m * w.n * (w.d + w.dv),
+                          "TFLOPs": 2.0 * w.h * w.m * w.n * (w.d + w.dv) / t_ex / 1e12,
+                          "mfma_frac": 2.0 * w.h * w.m * w.n * (w.d + w.dv) / t_ex /
+                          PEAK_FP32_MFMA,
+                          "kernel": "sk_exact_mfma" if max(w.d, w.dv) >= 16 else
+                          "sk_exact_tiled (VALU)"},
         "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
                          "kv_bytes": kv_bytes,
                          "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
