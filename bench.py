@@ -43,7 +43,7 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "sk_update_kernel": ["sk_update.h", "sk_common.h"],
+    "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h"],
     "sk_exact_decode": ["sk_exact.h", "sk_common.h"],
 }
 
