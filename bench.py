@@ -141,7 +141,9 @@ def decode_steps(w, E, torch, Kg, Vg, Qg, steps, exact_us):
     res = {}
     for layout in ("full", "sym"):
         sk = E.sketch_create(w.d, w.dv, w.p, w.h, layout)
-        E.sketch_update(sk, Kg, Vg)
+        step_n = w.chunk or w.n                  # the workload's own update calls
+        for c0 in range(0, w.n, step_n):
+            E.sketch_update(sk, Kg[:, c0:c0 + step_n], Vg[:, c0:c0 + step_n])
         cnt = max(steps, 3)                      # 3 warm-up steps
         ks = [Kg[:, i].contiguous() for i in range(cnt)]
         vs = [Vg[:, i].contiguous() for i in range(cnt)]
