@@ -28,6 +28,48 @@
 #include "sk_common.h"
 #include "sk_elementwise.h"
 
+// Multiplies f[u] by the key entries named by S digit offsets dg[0..S), for the
+// keys at base + STEP * u.  S is a compile-time count so that every LDS read of
+// the S digits is issued before the first product (no wait per digit).
+template <int S, int CH, int STEP>
+__device__ __forceinline__ void mul_digits(float (&f)[CH], const float* __restrict__ Ks,
+                                           const int* dg, int base) {
+  // keys in sub-chunks of SUB so that at most 16 values are in flight
+  constexpr int SUB = (16 / S) < CH ? ((16 / S) > 0 ? (16 / S) : 1) : CH;
+#pragma unroll
+  for (int u0 = 0; u0 < CH; u0 += SUB) {
+    float v[S][SUB];
+#pragma unroll
+    for (int c = 0; c < S; ++c)
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+        if (u0 + u < CH) v[c][u] = Ks[dg[c] + base + STEP * (u0 + u)];
+#pragma unroll
+    for (int c = 0; c < S; ++c)
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+        if (u0 + u < CH) f[u0 + u] *= v[c][u];
+  }
+}
+
+// The same for a digit count n known only at run time (uniform across the
+// workgroup: one scalar branch per call).
+template <int CH, int STEP>
+__device__ __forceinline__ void mul_digits_n(int n, float (&f)[CH], const float* __restrict__ Ks,
+                                             const int* dg, int base) {
+  switch (n) {
+    case 0: break;
+    case 1: mul_digits<1, CH, STEP>(f, Ks, dg, base); break;
+    case 2: mul_digits<2, CH, STEP>(f, Ks, dg, base); break;
+    case 3: mul_digits<3, CH, STEP>(f, Ks, dg, base); break;
+    case 4: mul_digits<4, CH, STEP>(f, Ks, dg, base); break;
+    case 5: mul_digits<5, CH, STEP>(f, Ks, dg, base); break;
+    case 6: mul_digits<6, CH, STEP>(f, Ks, dg, base); break;
+    case 7: mul_digits<7, CH, STEP>(f, Ks, dg, base); break;
+    default: mul_digits<8, CH, STEP>(f, Ks, dg, base); break;
+  }
+}
+
 template <int WC, bool CENTER>
 __device__ __forceinline__
 void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
@@ -154,22 +196,14 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
       }
     }
     __syncthreads();
-    // 2. feature tiles: L = prod of s key entries, R = u[e] * prod of t entries.
-    //    One digit at a time over all of the thread's keys, so the LDS reads of
-    //    a digit are issued together.
+    // 2. feature tiles: L = prod of s key entries, R = u[e] * prod of t entries,
+    //    all digit reads of a chunk of the thread's keys issued together.
 #pragma unroll
     for (int h0 = 0; h0 < NKL; h0 += CHL) {
       float f[CHL];
 #pragma unroll
       for (int u = 0; u < CHL; ++u) f[u] = validL ? 1.f : 0.f;
-#pragma unroll
-      for (int c = 0; c < SK_MAXDIG; ++c) {
-        if (c < s) {
-          const int off = dl[c] + STEPL * h0;
-#pragma unroll
-          for (int u = 0; u < CHL; ++u) f[u] *= Ks[off + STEPL * u];
-        }
-      }
+      mul_digits_n<CHL, STEPL>(s, f, Ks, dl, STEPL * h0);
 #pragma unroll
       for (int u = 0; u < CHL; ++u) Lt[(kpL + STEPL * (h0 + u)) * LDL + rL] = f[u];
     }
@@ -178,14 +212,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
       float f[CHR];
 #pragma unroll
       for (int u = 0; u < CHR; ++u) f[u] = validR ? usrc[STEPR * (h0 + u)] : 0.f;
-#pragma unroll
-      for (int c = 0; c < SK_MAXDIG; ++c) {
-        if (c < t) {
-          const int off = dr[c] + STEPR * h0;
-#pragma unroll
-          for (int u = 0; u < CHR; ++u) f[u] *= Ks[off + STEPR * u];
-        }
-      }
+      mul_digits_n<CHR, STEPR>(t, f, Ks, dr, STEPR * h0);
 #pragma unroll
       for (int u = 0; u < CHR; ++u) Rt[(kpR + STEPR * (h0 + u)) * LDR + cR] = f[u];
     }
