@@ -28,7 +28,8 @@ def ingest(w, K, V, sketches=None, layout="full"):
         step = w.chunk if w.chunk > 0 else max(hi - lo, 1)
         for c0 in range(lo, hi, step):
             c1 = min(hi, c0 + step)
-            B.sketch_update(sketches[i], K[:, c0:c1], V[:, c0:c1])
+            # a chunk of a multi-head stream is strided; the C ABI takes [h][n][d]
+            B.sketch_update(sketches[i], K[:, c0:c1].contiguous(), V[:, c0:c1].contiguous())
     for i in range(1, S):
         B.sketch_merge(sketches[0], sketches[i])
     return sketches[0], sketches

@@ -153,3 +153,20 @@ def test_sym_kernel_timing_events():
     assert len(ups) == 3 and all(t > 0 for t in ups)
     assert len(qs) == 1 and qs[0] > 0
     sk.destroy()
+
+
+@pytest.mark.parametrize("layout", ["full", "sym"])
+@pytest.mark.parametrize("d,dv,p,h,n,m,chunk", [
+    (128, 128, 2, 1, 2000, 130, 0),      # wide rows, large state
+    (4, 4, 2, 64, 700, 33, 0),           # many heads
+    (16, 8, 3, 2, 50, 127, 1),           # one key per call: no splits
+    (8, 16, 2, 1, 3000, 1, 1000),        # a single query
+    (8, 8, 3, 1, 2500, 128, 0),          # exactly one query tile
+    (8, 8, 3, 1, 2500, 129, 0),          # one query past a tile
+])
+def test_edge_shapes(layout, d, dv, p, h, n, m, chunk):
+    w = CONFIGS[1].scaled(n=n, m=m, h=h, chunk=chunk)
+    w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
+    K, V, Q = generate(w)
+    _check_sketch(w, K, V, Q, label=f"edge d={d} dv={dv} p={p} h={h} n={n} m={m}",
+                  layout=layout)
