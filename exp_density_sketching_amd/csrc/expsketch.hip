@@ -124,6 +124,19 @@ int sym_query_rows() {
   return v;
 }
 
+// The full-layout update kernel is instantiated per centring and per prefetch
+// depth (float4 of K and of V per thread per 32-key stage: 1 up to d, dv = 32,
+// 2 for 64, 4 for 128), so narrow keys do not hold registers for wide ones.
+using UpdateKernel = void (*)(const float*, const float*, long long, int, int, int,
+                              const UpdTile*, int, long long, int, int, float*, long long,
+                              long long, int, const float*, PendingReduce);
+UpdateKernel update_kernel_for(bool center, int d, int dv) {
+  const int w = std::max(d, dv);
+  if (w <= 32) return center ? sk_update_kernel<true, 1> : sk_update_kernel<false, 1>;
+  if (w <= 64) return center ? sk_update_kernel<true, 2> : sk_update_kernel<false, 2>;
+  return center ? sk_update_kernel<true, 4> : sk_update_kernel<false, 4>;
+}
+
 // The multiset update kernel is instantiated per tile shape (rb, cb).
 using SymUpdateKernel = void (*)(const float*, const float*, long long, int, int,
                                  const SymUpdTile*, int, SymTables, long long, int, int,
@@ -683,9 +696,9 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   }
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
-         hipFuncSetAttribute((const void*)sk_update_kernel<false>,
+         hipFuncSetAttribute((const void*)update_kernel_for(false, d, dv),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
-         hipFuncSetAttribute((const void*)sk_update_kernel<true>,
+         hipFuncSetAttribute((const void*)update_kernel_for(true, d, dv),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
          hipFuncSetAttribute((const void*)query_kernel_for(s->logd),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
@@ -844,7 +857,7 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
       if (e != hipSuccess) err = e;
     }
   } else {
-    hipLaunchKernelGGL(s->center != nullptr ? sk_update_kernel<true> : sk_update_kernel<false>,
+    hipLaunchKernelGGL(update_kernel_for(s->center != nullptr, s->d, s->dv),
                        dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)), dim3(SK_WG),
                        lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
                        s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,

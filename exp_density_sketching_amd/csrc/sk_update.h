@@ -70,7 +70,7 @@ __device__ __forceinline__ void mul_digits_n(int n, float (&f)[CH], const float*
   }
 }
 
-template <int WC, bool CENTER>
+template <int WC, bool CENTER, int NPF>
 __device__ __forceinline__
 void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
                     long long n, int d, int dv, int logd, const UpdTile& T,
@@ -85,7 +85,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   constexpr int STEPL = SK_WG / TM, NKL = SK_KB / STEPL;   // keys per thread (L)
   constexpr int STEPR = SK_WG / TN, NKR = SK_KB / STEPR;   // keys per thread (R)
   constexpr int CHL = NKL < 16 ? NKL : 16, CHR = NKR < 16 ? NKR : 16;  // keys per pass
-  constexpr int NPF = 4;              // float4 per thread per stage, for d <= 128
+  // NPF: float4 of K (and of V) per thread per stage, 32 max(d, dv) / 1024
   extern __shared__ float lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,7 +265,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
 }
 
 // One launch covers every tile of every level; the tile's shape picks the body.
-template <bool CENTER>
+template <bool CENTER, int NPF>
 __global__ __launch_bounds__(SK_WG, 2)
 void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
                       long long n, int d, int dv, int logd,
@@ -287,12 +287,12 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   const long long head = lg / ((long long)ntiles * nsplit);
   const UpdTile T = tiles[tile_id];
   if (T.wc == 2)
-    sk_update_tile<2, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<2, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else if (T.wc == 1)
-    sk_update_tile<1, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<1, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else
-    sk_update_tile<4, CENTER>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<4, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
 }
