@@ -244,21 +244,29 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   }
 
   // Epilogue: rows of X_j are contiguous, so (row, col) -> xoff + row * N + col.
+  // A wave whose 64 rows are all inside the level (nearly every tile) stores
+  // without row checks; accumulate is uniform too.
   float* o = out + split * split_stride + head * head_stride + T.xoff;
   const floatx16* accs[4] = {&acc00, &acc01, &acc10, &acc11};
+  const bool rows_in = T.row0 + wr0 + 64 <= T.M;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi) {
     const int i = bi >> 1, jj = bi & 1;
     const int col = T.col0 + wc0 + 32 * jj + l32;
     if (col >= T.N) continue;
     const floatx16 a = *accs[bi];
+    float* ob = o + (long long)(T.row0 + wr0 + 32 * i) * T.N + col;
+    if (rows_in && !accumulate) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = T.row0 + wr0 + 32 * i + acc_row(r, lane);
-      if (row < T.M) {
-        const long long idx = (long long)row * T.N + col;
-        if (accumulate) o[idx] += a[r];
-        else o[idx] = a[r];
+      for (int r = 0; r < 16; ++r) ob[(long long)acc_row(r, lane) * T.N] = a[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = T.row0 + wr0 + 32 * i + acc_row(r, lane);
+        if (row < T.M) {
+          float* dst = ob + (long long)acc_row(r, lane) * T.N;
+          *dst = accumulate ? *dst + a[r] : a[r];
+        }
       }
     }
   }
