@@ -282,6 +282,7 @@ def main():
         for sk in sketches:
             E.sketch_timing(sk, False)
         r["dur"] = float(np.mean(upd_ms)) / 1e3
+        r["ktime"] = float(np.sum(upd_ms)) / 1e3     # all update launches of the steps
         r["launches"] = len(upd_ms)
         r["t_qk"] = float(np.mean(qry_ms)) / 1e3
         return r
@@ -291,20 +292,27 @@ def main():
     t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
     dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
-    achieved = flop_per_key * keys_per_call * w.h / dur
+    # every key of every timed step went through the update launches (small calls
+    # are staged, so a launch may hold several calls' keys): algorithmic flops of
+    # all keys / the launches' total time
+    keys_timed = float(w.n) * w.h * args.steps
+    achieved = flop_per_key * keys_timed / full["ktime"]
 
-    # one whole sketch_update call (update kernel + split reduce), per call
+    # whole sketch_update calls of one sub-stream, per call: every launch, copy
+    # and partial reduction they cause, up to a state that is complete (export)
     sk = sketches[0]
     E.sketch_reset(sk)
-    per_call = []
-    for c0 in range(0, w.n // S, chunk):
-        a, b = ev(), ev()
-        a.record()
-        E.sketch_update(sk, Kg[:, c0:c0 + chunk], Vg[:, c0:c0 + chunk])
-        b.record()
-        per_call.append((a, b))
+    calls = list(range(0, w.n // S, chunk))
+    view = E.sketch_export(sk)
     torch.cuda.synchronize()
-    call_dur = float(np.mean([a.elapsed_time(b) for a, b in per_call])) / 1e3
+    a, b = ev(), ev()
+    a.record()
+    for c0 in calls:
+        E.sketch_update(sk, Kg[:, c0:c0 + chunk], Vg[:, c0:c0 + chunk])
+    E.sketch_export(sk, view)
+    b.record()
+    torch.cuda.synchronize()
+    call_dur = a.elapsed_time(b) / 1e3 / len(calls)
 
     # exact path in decode mode (one query per head), streaming the whole KV
     dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
@@ -359,7 +367,7 @@ def main():
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
                      "traffic": committed_traffic("sk_update_kernel", w.name),
-                     "flop_per_launch": flop_per_key * keys_per_call * w.h,
+                     "flop_per_launch": flop_per_key * keys_timed / full["launches"],
                      "launch_us": dur * 1e6, "launches": full["launches"]},
     }
     for s_ in sketches:
@@ -371,7 +379,7 @@ def main():
         s_.destroy()
     rows = math.comb(w.d + w.p, w.p)
     sflop = 2.0 * rows * (1 + w.dv)
-    s_ach = sflop * keys_per_call * w.h / sym["dur"]
+    s_ach = sflop * keys_timed / sym["ktime"]
     line["sym_layout"] = {
         "value": w.h * (w.n + w.m) / sym["t_step"],
         "ms_per_step": sym["t_step"] * 1e3,
@@ -385,7 +393,7 @@ def main():
         "roofline": {"kernel": "sk_sym_update_kernel", "bound": "mfma",
                      "achieved": s_ach / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": s_ach / PEAK_FP32_MFMA,
-                     "flop_per_launch": sflop * keys_per_call * w.h,
+                     "flop_per_launch": sflop * keys_timed / sym["launches"],
                      "launch_us": sym["dur"] * 1e6, "launches": sym["launches"]},
     }
     line["decode_step"] = decode_steps(w, E, torch, Kg, Vg, Qg, args.decode_steps,

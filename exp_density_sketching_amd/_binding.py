@@ -19,7 +19,8 @@ LAYOUTS = {"full": 0, "sym": 1}
 
 EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy",
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
-            "sketch_query", "sketch_step", "sketch_set_center", "exact_attend",
+            "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
+            "exact_attend",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
 
@@ -56,6 +57,7 @@ def _lib():
             "sketch_query": (c_int, [vp, vp, c_i64, vp, vp]),
             "sketch_step": (c_int, [vp, vp, vp, vp, vp, vp]),
             "sketch_set_center": (c_int, [vp, vp]),
+            "sketch_set_staging": (c_int, [vp, c_i64]),
             "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
                                      vp, vp]),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
@@ -219,6 +221,11 @@ def sketch_set_center(s, c):
         raise ValueError(f"c {tuple(c.shape)} does not match h={s.h}, d={s.d}")
     _check(_lib().sketch_set_center(s._handle(), _dev(c.contiguous(), "c", 2)),
            "sketch_set_center")
+
+
+def sketch_set_staging(s, keys):
+    """Staging size of sketch_update in keys per head (0: off)."""
+    _check(_lib().sketch_set_staging(s._handle(), int(keys)), "sketch_set_staging")
 
 
 def sketch_step(s, k, v, q, out=None, Z=None):

@@ -127,7 +127,7 @@ int sym_query_rows() {
 // The full-layout update kernel is instantiated per centring and per prefetch
 // depth (float4 of K and of V per thread per 32-key stage: 1 up to d, dv = 32,
 // 2 for 64, 4 for 128), so narrow keys do not hold registers for wide ones.
-using UpdateKernel = void (*)(const float*, const float*, long long, int, int, int,
+using UpdateKernel = void (*)(const float*, const float*, long long, long long, int, int, int,
                               const UpdTile*, int, long long, int, int, float*, long long,
                               long long, int, const float*, PendingReduce);
 UpdateKernel update_kernel_for(bool center, int d, int dv) {
@@ -138,7 +138,7 @@ UpdateKernel update_kernel_for(bool center, int d, int dv) {
 }
 
 // The multiset update kernel is instantiated per tile shape (rb, cb).
-using SymUpdateKernel = void (*)(const float*, const float*, long long, int, int,
+using SymUpdateKernel = void (*)(const float*, const float*, long long, long long, int, int,
                                  const SymUpdTile*, int, SymTables, long long, int, int,
                                  float*, long long, long long, int, const float*,
                                  PendingReduce);
@@ -222,6 +222,12 @@ struct sk_sketch {
   float* pend = nullptr;                   // partials not yet in the state
   int pend_ns = 0;
   hipEvent_t flush_ev = nullptr;           // orders a flush before another stream
+  // staging of small update calls: their keys and values are copied here and
+  // contracted in one launch when the buffer fills or the state is needed
+  float* stage_k = nullptr;                // [h][stage_cap][d]
+  float* stage_v = nullptr;                // [h][stage_cap][dv]
+  long long stage_cap = -1;                // keys per head; 0 = off, -1 = default
+  long long stage_n = 0;                   // keys per head staged
 };
 
 namespace {
@@ -741,6 +747,8 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->center);
   (void)hipFree(s->pbuf[0]);
   (void)hipFree(s->pbuf[1]);
+  (void)hipFree(s->stage_k);
+  (void)hipFree(s->stage_v);
   if (s->flush_ev != nullptr) (void)hipEventDestroy(s->flush_ev);
   (void)hipFree(s->view);
   for (int k = 0; k < 3; ++k)
@@ -759,7 +767,8 @@ int sketch_set_stream(sk_handle s, void* hip_stream) {
 int sketch_reset(sk_handle s) {
   if (s == nullptr) return SK_EINVAL;
   s->count = 0;
-  s->pend = nullptr;            // pending partials belong to the old contents
+  s->pend = nullptr;            // pending partials and staged keys belong to the
+  s->stage_n = 0;               // old contents
   return launch_fill_zero(s->state, s->XS * s->h, s->stream);
 }
 
@@ -774,10 +783,13 @@ int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D, int64_
   return SK_OK;
 }
 
-int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
-  if (s == nullptr || n < 0) return SK_EINVAL;
-  if (n == 0) return SK_OK;
-  if (K == nullptr || V == nullptr || !aligned16(K) || !aligned16(V)) return SK_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The moment update of n keys per head, K [h][hkeys][d] (keys of head h start at
+// K + h * hkeys * d), V likewise: one launch (plus the deferred reduce).
+int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long long hkeys) {
   const int ns = choose_update_splits(s, n);
   long long kps = (n + ns - 1) / ns;
   kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
@@ -851,7 +863,7 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
       const long long extra = g == 0 ? rwgs : 0;
       hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb, s->center != nullptr),
                          dim3((unsigned)((long long)nt * nsplit * s->h + extra)), dim3(SK_WG),
-                         lds, s->stream, K, V, (long long)n, s->d, s->dv, s->d_sutiles + t0,
+                         lds, s->stream, K, V, (long long)n, hkeys, s->d, s->dv, s->d_sutiles + t0,
                          nt, s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center, rg);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) err = e;
@@ -859,7 +871,7 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
   } else {
     hipLaunchKernelGGL(update_kernel_for(s->center != nullptr, s->d, s->dv),
                        dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)), dim3(SK_WG),
-                       lds, s->stream, K, V, (long long)n, s->d, s->dv, s->logd,
+                       lds, s->stream, K, V, (long long)n, hkeys, s->d, s->dv, s->logd,
                        s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,
                        s->center, red);
     err = hipGetLastError();
@@ -880,7 +892,86 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
     (void)hipFreeAsync(tmp, s->stream);
   }
   if (err != hipSuccess) return SK_EHIP;
+  return SK_OK;
+}
+
+// Contracts the staged keys (if any) into the state.
+int flush_stage(sk_sketch* s) {
+  if (s->stage_n == 0) return SK_OK;
+  const long long n = s->stage_n;
+  s->stage_n = 0;
+  return run_update(s, s->stage_k, s->stage_v, n, s->stage_cap);
+}
+
+// Everything a reader of the state needs done first: staged keys, then pending
+// split partials.
+int settle(sk_sketch* s) {
+  int rc = flush_stage(s);
+  if (rc == SK_OK) rc = flush_pending(s);
+  return rc;
+}
+
+// Default staging size: up to 16384 keys per head in at most 32 MB, off below
+// 1024 keys.
+long long default_stage_cap(const sk_sketch* s) {
+  const long long per_key = (long long)sizeof(float) * (s->d + s->dv) * s->h;
+  long long cap = std::min<long long>(16384, (32LL << 20) / per_key);
+  cap = cap / SK_KB * SK_KB;
+  return cap >= 1024 ? cap : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
+  if (s == nullptr || n < 0) return SK_EINVAL;
+  if (n == 0) return SK_OK;
+  if (K == nullptr || V == nullptr || !aligned16(K) || !aligned16(V)) return SK_EINVAL;
+  if (s->stage_cap < 0) s->stage_cap = default_stage_cap(s);
+  // calls of fewer than half the staging size are staged; larger ones run at once
+  if (s->stage_cap > 0 && 2 * n <= s->stage_cap) {
+    int rc = SK_OK;
+    if (s->stage_n + n > s->stage_cap) rc = flush_stage(s);
+    if (rc != SK_OK) return rc;
+    if (s->stage_k == nullptr) {
+      const size_t kb = sizeof(float) * (size_t)s->h * s->stage_cap * s->d;
+      const size_t vb = sizeof(float) * (size_t)s->h * s->stage_cap * s->dv;
+      if (hipMalloc(&s->stage_k, kb) != hipSuccess || hipMalloc(&s->stage_v, vb) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(s->stage_k);
+        (void)hipFree(s->stage_v);
+        s->stage_k = s->stage_v = nullptr;
+        s->stage_cap = 0;          // no staging from now on
+      }
+    }
+    if (s->stage_cap > 0) {
+      const size_t ks = sizeof(float) * (size_t)s->d, vs = sizeof(float) * (size_t)s->dv;
+      SK_TRY(hipMemcpy2DAsync(s->stage_k + s->stage_n * s->d, ks * s->stage_cap, K, ks * n,
+                              ks * n, s->h, hipMemcpyDeviceToDevice, s->stream));
+      SK_TRY(hipMemcpy2DAsync(s->stage_v + s->stage_n * s->dv, vs * s->stage_cap, V, vs * n,
+                              vs * n, s->h, hipMemcpyDeviceToDevice, s->stream));
+      s->stage_n += n;
+      s->count += n;
+      return s->stage_n == s->stage_cap ? flush_stage(s) : SK_OK;
+    }
+  }
+  int rc = flush_stage(s);           // staged keys go first (the order is fixed)
+  if (rc == SK_OK) rc = run_update(s, K, V, n, n);
+  if (rc != SK_OK) return rc;
   s->count += n;
+  return SK_OK;
+}
+
+int sketch_set_staging(sk_handle s, int64_t keys) {
+  if (s == nullptr || keys < 0) return SK_EINVAL;
+  int rc = flush_stage(s);
+  if (rc != SK_OK) return rc;
+  SK_TRY(hipStreamSynchronize(s->stream));
+  (void)hipFree(s->stage_k);
+  (void)hipFree(s->stage_v);
+  s->stage_k = s->stage_v = nullptr;
+  s->stage_cap = keys / SK_KB * SK_KB;
   return SK_OK;
 }
 
@@ -891,15 +982,15 @@ int sketch_merge(sk_handle dst, sk_handle src) {
     return SK_EMISMATCH;
   // src's pending partials go into its state on src's stream; dst's stream then
   // waits for that before reading it
-  const bool src_pending = src->pend != nullptr;
-  int rc = flush_pending(src);
+  const bool src_pending = src->pend != nullptr || src->stage_n > 0;
+  int rc = settle(src);
   if (rc == SK_OK && src_pending && src->stream != dst->stream) {
     if (src->flush_ev == nullptr)
       SK_TRY(hipEventCreateWithFlags(&src->flush_ev, hipEventDisableTiming));
     SK_TRY(hipEventRecord(src->flush_ev, src->stream));
     SK_TRY(hipStreamWaitEvent(dst->stream, src->flush_ev, 0));
   }
-  if (rc == SK_OK) rc = flush_pending(dst);
+  if (rc == SK_OK) rc = settle(dst);
   if (rc != SK_OK) return rc;
   const long long c4 = dst->XS * dst->h / 4;
   const int grid = (int)std::min<long long>((c4 + 255) / 256, 16384);
@@ -916,7 +1007,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (m == 0) return SK_OK;
   if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
   {
-    const int rc = flush_pending(s);
+    const int rc = settle(s);
     if (rc != SK_OK) return rc;
   }
   const int ntiles = (int)s->qtiles.size();
@@ -988,7 +1079,7 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
   const int nt = (int)s->stiles.size();
   if ((long long)nt * s->h > 0x7fffffffLL) return SK_EINVAL;
   {
-    const int rc = flush_pending(s);
+    const int rc = settle(s);
     if (rc != SK_OK) return rc;
   }
   timing_mark(s, 2, false);
@@ -1036,7 +1127,7 @@ int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count) {
 int sketch_export(sk_handle s, float* dst) {
   if (s == nullptr || dst == nullptr || !aligned16(dst)) return SK_EINVAL;
   {
-    const int rc = flush_pending(s);
+    const int rc = settle(s);
     if (rc != SK_OK) return rc;
   }
   if (s->layout == SK_LAYOUT_SYM) {

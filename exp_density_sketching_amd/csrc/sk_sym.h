@@ -110,7 +110,8 @@ struct SymQryTile {
 template <int RB, int CB, bool CENTER>
 __device__ __forceinline__
 void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V,
-                        long long n, int d, int dv, const SymUpdTile& T, const SymTables& tb,
+                        long long n, long long hkeys, int d, int dv, const SymUpdTile& T,
+                        const SymTables& tb,
                         long long split, long long head, long long keys_per_split,
                         float* __restrict__ out, long long head_stride,
                         long long split_stride, int accumulate,
@@ -131,8 +132,8 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
   const long long k_begin = split * keys_per_split;
   long long k_end = k_begin + keys_per_split;
   if (k_end > n) k_end = n;
-  const float* Kh = K + head * n * d;
-  const float* Vh = V + head * n * dv;
+  const float* Kh = K + head * hkeys * d;     // hkeys: keys between heads (>= n)
+  const float* Vh = V + head * hkeys * dv;
 
   for (int i = tid; i < LDK; i += SK_WG) {
     Ks[d * LDK + i] = 1.f;
@@ -301,7 +302,7 @@ void sk_sym_update_tile(const float* __restrict__ K, const float* __restrict__ V
 template <int RB, int CB, bool CENTER>
 __global__ __launch_bounds__(SK_WG, (RB * CB >= 16) ? 2 : 4)
 void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
-                          long long n, int d, int dv,
+                          long long n, long long hkeys, int d, int dv,
                           const SymUpdTile* __restrict__ tiles, int ntiles, SymTables tb,
                           long long keys_per_split, int nsplit, int nhead,
                           float* __restrict__ out, long long head_stride,
@@ -317,8 +318,9 @@ void sk_sym_update_kernel(const float* __restrict__ K, const float* __restrict__
   const long long split = (lg / ntiles) % nsplit;
   const long long head = lg / ((long long)ntiles * nsplit);
   const SymUpdTile T = tiles[tile];
-  sk_sym_update_tile<RB, CB, CENTER>(K, V, n, d, dv, T, tb, split, head, keys_per_split, out,
-                             head_stride, split_stride, accumulate, center);
+  sk_sym_update_tile<RB, CB, CENTER>(K, V, n, hkeys, d, dv, T, tb, split, head,
+                                     keys_per_split, out, head_stride, split_stride,
+                                     accumulate, center);
 }
 
 // ---------------------------------------------------------------------------

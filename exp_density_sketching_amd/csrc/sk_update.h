@@ -73,7 +73,7 @@ __device__ __forceinline__ void mul_digits_n(int n, float (&f)[CH], const float*
 template <int WC, bool CENTER, int NPF>
 __device__ __forceinline__
 void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
-                    long long n, int d, int dv, int logd, const UpdTile& T,
+                    long long n, long long hkeys, int d, int dv, int logd, const UpdTile& T,
                     long long split, long long head, long long keys_per_split,
                     float* __restrict__ out, long long head_stride,
                     long long split_stride, int accumulate,
@@ -104,8 +104,8 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
   long long k_end = k_begin + keys_per_split;
   if (k_end > n) k_end = n;
 
-  const float* Kh = K + head * n * d;
-  const float* Vh = V + head * n * dv;
+  const float* Kh = K + head * hkeys * d;     // hkeys: keys between heads (>= n)
+  const float* Vh = V + head * hkeys * dv;
 
   // Feature assignment (fixed for the whole key loop): row rL of the L tile for
   // keys kpL + STEPL*u, column cR of the R tile for keys kpR + STEPR*u.
@@ -276,7 +276,7 @@ void sk_update_tile(const float* __restrict__ K, const float* __restrict__ V,
 template <bool CENTER, int NPF>
 __global__ __launch_bounds__(SK_WG, 2)
 void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
-                      long long n, int d, int dv, int logd,
+                      long long n, long long hkeys, int d, int dv, int logd,
                       const UpdTile* __restrict__ tiles, int ntiles,
                       long long keys_per_split, int nsplit, int nhead,
                       float* __restrict__ out, long long head_stride,
@@ -295,12 +295,12 @@ void sk_update_kernel(const float* __restrict__ K, const float* __restrict__ V,
   const long long head = lg / ((long long)ntiles * nsplit);
   const UpdTile T = tiles[tile_id];
   if (T.wc == 2)
-    sk_update_tile<2, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<2, CENTER, NPF>(K, V, n, hkeys, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else if (T.wc == 1)
-    sk_update_tile<1, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<1, CENTER, NPF>(K, V, n, hkeys, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
   else
-    sk_update_tile<4, CENTER, NPF>(K, V, n, d, dv, logd, T, split, head, keys_per_split, out,
+    sk_update_tile<4, CENTER, NPF>(K, V, n, hkeys, d, dv, logd, T, split, head, keys_per_split, out,
                       head_stride, split_stride, accumulate, center);
 }

@@ -234,6 +234,7 @@ def test_kernel_timing_events():
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     sk = E.sketch_create(w.d, w.dv, w.p)
+    E.sketch_set_staging(sk, 0)         # one update launch per call
     E.sketch_timing(sk, True)
     for c0 in range(0, w.n, 4096):
         E.sketch_update(sk, Kg[:, c0:c0 + 4096], Vg[:, c0:c0 + 4096])
@@ -249,8 +250,9 @@ def test_kernel_timing_events():
     sk.destroy()
 
 
+@pytest.mark.parametrize("staging", [0, None])
 @pytest.mark.parametrize("layout", ["full", "sym"])
-def test_pending_partials_are_always_added(layout):
+def test_pending_partials_are_always_added(layout, staging):
     """Split update calls leave their partials for the next launch to add; every
     reader (export, query, merge) and reset must see the right state.  Calls of
     4096 keys (split) alternate with calls of 100 keys (one split, added in
@@ -262,6 +264,8 @@ def test_pending_partials_are_always_added(layout):
     sizes = [4096, 4096, 100, 4096, 257, 4096, 4096]
     bounds = np.cumsum([0] + sizes)
     a = E.sketch_create(w.d, w.dv, w.p, 1, layout)
+    if staging is not None:
+        E.sketch_set_staging(a, staging)     # 0: every call launches (split partials)
     # garbage that the reset must drop, pending at the time of the reset
     E.sketch_update(a, Kg[:, :4096], Vg[:, :4096])
     E.sketch_update(a, Kg[:, 4096:8192], Vg[:, 4096:8192])
@@ -271,6 +275,8 @@ def test_pending_partials_are_always_added(layout):
     n_a = int(bounds[-1])
     # a second sketch with its own pending partials, merged into the first
     b = E.sketch_create(w.d, w.dv, w.p, 1, layout)
+    if staging is not None:
+        E.sketch_set_staging(b, staging)
     E.sketch_update(b, Kg[:, n_a:n_a + 4096 + 2], Vg[:, n_a:n_a + 4096 + 2])
     E.sketch_merge(a, b)
     n = n_a + 4096 + 2
@@ -286,3 +292,44 @@ def test_pending_partials_are_always_added(layout):
     assert zrel(Z[0], z_ref) <= SK_Z_REL and oabs(out[0], o_ref) <= SK_O_ABS
     a.destroy()
     b.destroy()
+
+
+@pytest.mark.parametrize("layout", ["full", "sym"])
+def test_staged_calls_equal_direct_calls(layout):
+    """Staged small calls (default staging) give the moments of the same keys as
+    one direct call; staged keys are contracted before every reader, dropped by
+    reset, and kept in order around a large call and a staging change."""
+    w = CONFIGS[2].scaled(n=40000, m=16, h=2)
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = gpu(K, V, Q)
+    st = E.sketch_create(w.d, w.dv, w.p, 2, layout)
+    E.sketch_update(st, Kg[:, :300].contiguous(), Vg[:, :300].contiguous())
+    E.sketch_reset(st)                             # staged keys dropped
+    cuts = [0, 1000, 1001, 4097, 20000, 20033, 24000, 40000]
+    for i, (lo, hi) in enumerate(zip(cuts[:-1], cuts[1:])):
+        if i == 4:
+            E.sketch_set_staging(st, 2048)         # change of size mid-stream
+        E.sketch_update(st, Kg[:, lo:hi].contiguous(), Vg[:, lo:hi].contiguous())
+    assert st.count == 40000
+    ref = E.sketch_create(w.d, w.dv, w.p, 2, layout)
+    E.sketch_set_staging(ref, 0)
+    E.sketch_update(ref, Kg, Vg)
+    o1, z1 = host(*E.sketch_query(st, Qg))
+    o2, z2 = host(*E.sketch_query(ref, Qg))
+    assert zrel(z1, z2) <= 1e-5 and oabs(o1, o2) <= 1e-5
+    S1, S2 = host(E.sketch_export(st), E.sketch_export(ref))
+    assert np.abs(S1 - S2).max() <= 1e-5 * np.abs(S2).max()
+    # merge and decode step with keys still staged on both sides
+    a = E.sketch_create(w.d, w.dv, w.p, 2, layout)
+    b = E.sketch_create(w.d, w.dv, w.p, 2, layout)
+    E.sketch_update(a, Kg[:, :3000].contiguous(), Vg[:, :3000].contiguous())
+    E.sketch_update(b, Kg[:, 3000:6000].contiguous(), Vg[:, 3000:6000].contiguous())
+    E.sketch_merge(a, b)
+    out, Z = host(*E.sketch_step(a, Kg[:, 6000].contiguous(), Vg[:, 6000].contiguous(),
+                                 Qg[:, 0].contiguous()))
+    for hd in range(2):
+        o_ref, z_ref = oracle.sketch_direct(K[hd, :6001], V[hd, :6001], Q[hd, :1], w.p)
+        assert abs(Z[hd] - z_ref[0]) / z_ref[0] <= SK_Z_REL
+        assert np.max(np.abs(out[hd] - o_ref[0])) <= SK_O_ABS
+    for x in (st, ref, a, b):
+        x.destroy()

@@ -144,6 +144,7 @@ def test_sym_kernel_timing_events():
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     sk = E.sketch_create(w.d, w.dv, w.p, layout="sym")
+    E.sketch_set_staging(sk, 0)         # one update launch per call
     E.sketch_timing(sk, True)
     for c0 in range(0, w.n, 4096):
         E.sketch_update(sk, Kg[:, c0:c0 + 4096], Vg[:, c0:c0 + 4096])
