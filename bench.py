@@ -44,6 +44,7 @@ def parse():
 
 KERNEL_SOURCES = {
     "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h"],
+    "sk_update_kr_kernel": ["sk_update_kr.h", "sk_common.h", "sk_elementwise.h"],
     "sk_exact_decode": ["sk_exact.h", "sk_common.h"],
 }
 
@@ -191,6 +192,7 @@ def counters_pass(w, E, torch, generate, layout="full"):
     S = max(1, w.substreams)
     sketches = [E.sketch_create(w.d, w.dv, w.p, w.h, layout) for _ in range(S)]
     ingest(w, Kg, Vg, sketches)
+    ukern = E.UPDATE_KERNELS[E.sketch_update_path(sketches[0])]
     Qg = torch.from_numpy(Q).cuda()
     for _ in range(3):
         E.sketch_query(sketches[0], Qg)
@@ -202,7 +204,8 @@ def counters_pass(w, E, torch, generate, layout="full"):
         sk.destroy()
     print(json.dumps({"counters_pass": w.name, "layout": layout, "copy_bytes": nbytes,
                       "copies": 3,
-                      "update_sources": source_hash("sk_update_kernel"),
+                      "update_kernel": ukern,
+                      "update_sources": source_hash(ukern) if ukern in KERNEL_SOURCES else None,
                       "decode_sources": source_hash("sk_exact_decode"),
                       "kv_bytes": 4 * w.h * w.n * (w.d + w.dv)}), flush=True)
     return 0
@@ -289,6 +292,7 @@ def main():
 
     full = measure("full")
     sketches = full["sketches"]
+    ukern = E.UPDATE_KERNELS[E.sketch_update_path(sketches[0])]
     t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
     dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
@@ -363,10 +367,10 @@ def main():
         "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
                          "kv_bytes": kv_bytes,
                          "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
-        "roofline": {"kernel": "sk_update_kernel", "bound": "mfma",
+        "roofline": {"kernel": ukern, "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
-                     "traffic": committed_traffic("sk_update_kernel", w.name),
+                     "traffic": committed_traffic(ukern, w.name),
                      "flop_per_launch": flop_per_key * keys_timed / full["launches"],
                      "launch_us": dur * 1e6, "launches": full["launches"]},
     }

@@ -9,13 +9,13 @@ Problema" and "Metodologia" (pillar "O Método Polinomial", Merge-and-Reduce).
 """
 
 from ._binding import (LIB_PATH, EXPORTED, LAYOUTS, Sketch, SketchError, sketch_create,
-                       sketch_layout, sketch_destroy, sketch_reset, sketch_update, sketch_merge,
+                       sketch_layout, sketch_update_path, UPDATE_KERNELS, sketch_destroy, sketch_reset, sketch_update, sketch_merge,
                        sketch_query, sketch_step, sketch_set_center, sketch_set_staging,
                        sketch_export, sketch_state, sketch_timing,
                        sketch_kernel_times, exact_attend, raw)
 
 __all__ = ["LIB_PATH", "EXPORTED", "LAYOUTS", "Sketch", "SketchError", "sketch_create",
-           "sketch_layout",
+           "sketch_layout", "sketch_update_path", "UPDATE_KERNELS",
            "sketch_destroy", "sketch_reset", "sketch_update", "sketch_merge",
            "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
            "sketch_export", "sketch_state", "sketch_timing",

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libexpsketch.so")
 SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
 LAYOUTS = {"full": 0, "sym": 1}
 
-EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_destroy",
+EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_update_path",
+            "sketch_destroy",
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
             "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
             "exact_attend",
@@ -49,6 +50,7 @@ def _lib():
             "sketch_create_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, vp,
                                          ctypes.POINTER(vp)]),
             "sketch_layout": (c_int, [vp, ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
+            "sketch_update_path": (c_int, [vp, ctypes.POINTER(c_int)]),
             "sketch_destroy": (c_int, [vp]),
             "sketch_set_stream": (c_int, [vp, vp]),
             "sketch_reset": (c_int, [vp]),
@@ -168,6 +170,19 @@ def sketch_layout(s):
     _check(_lib().sketch_layout(s._handle(), ctypes.byref(lay), ctypes.byref(rows)),
            "sketch_layout")
     return {v: k for k, v in LAYOUTS.items()}[lay.value], rows.value
+
+
+UPDATE_PATHS = {0: "tiles", 1: "digits", 2: "multiset"}
+UPDATE_KERNELS = {"tiles": "sk_update_kernel", "digits": "sk_update_kr_kernel",
+                  "multiset": "sk_sym_update_kernel"}
+
+
+def sketch_update_path(s):
+    """Name of the kernel family the handle's updates launch: "tiles", "digits"
+    or "multiset"."""
+    kind = ctypes.c_int()
+    _check(_lib().sketch_update_path(s._handle(), ctypes.byref(kind)), "sketch_update_path")
+    return UPDATE_PATHS[kind.value]
 
 
 def sketch_destroy(s):

@@ -19,6 +19,7 @@
 #include "sk_step.h"
 #include "sk_sym.h"
 #include "sk_update.h"
+#include "sk_update_kr.h"
 
 namespace {
 
@@ -130,11 +131,32 @@ int sym_query_rows() {
 using UpdateKernel = void (*)(const float*, const float*, long long, long long, int, int, int,
                               const UpdTile*, int, long long, int, int, float*, long long,
                               long long, int, const float*, PendingReduce);
+using UpdateKrKernel = void (*)(const float*, const float*, long long, long long, int,
+                                const KrUnit*, int, long long, int, int, float*, long long,
+                                long long, int, const float*, PendingReduce);
 UpdateKernel update_kernel_for(bool center, int d, int dv) {
   const int w = std::max(d, dv);
   if (w <= 32) return center ? sk_update_kernel<true, 1> : sk_update_kernel<false, 1>;
   if (w <= 64) return center ? sk_update_kernel<true, 2> : sk_update_kernel<false, 2>;
   return center ? sk_update_kernel<true, 4> : sk_update_kernel<false, 4>;
+}
+
+// The digit-organised update kernel (sk_update_kr.h) per key width d = 16 RT.
+// It runs for d = 16 and 32, where it is the faster of the two full-layout
+// kernels; at d = 64 and 128 the tile kernel is.
+UpdateKrKernel update_kr_kernel_for(bool center, int d) {
+  if (d == 16) return center ? sk_update_kr_kernel<1, true> : sk_update_kr_kernel<1, false>;
+  return center ? sk_update_kr_kernel<2, true> : sk_update_kr_kernel<2, false>;
+}
+// waves of that kernel resident per SIMD (its register use)
+int update_kr_waves_per_simd() { return 2; }
+// EXPSKETCH_UPDATE_KR=0 keeps the tile kernels for every key width.
+bool use_update_kr() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_UPDATE_KR");
+    return e == nullptr || std::atoi(e) != 0;
+  }();
+  return v;
 }
 
 // The multiset update kernel is instantiated per tile shape (rb, cb).
@@ -188,6 +210,8 @@ struct sk_sketch {
   std::vector<UpdTile> utiles;
   std::vector<QryTile> qtiles;
   UpdTile* d_utiles = nullptr;
+  std::vector<KrUnit> kunits;      // digit-organised update units (d >= 16)
+  KrUnit* d_kunits = nullptr;
   QryTile* d_qtiles = nullptr;
   long long qpb = 0;        // floats of query partials per (head, query tile)
   float* view = nullptr;    // canonical view buffer
@@ -281,6 +305,57 @@ void plan_update_level(sk_sketch* s, int j, std::vector<UpdTile>* out) {
       t.col0 = c0;
       out->push_back(t);
     }
+}
+
+// Units of the digit-organised update (key widths d >= 16), see sk_update_kr.h:
+// levels 0 and 1 per 16-column tile; level 2 per (16-chunk of c, 8 b1 digits,
+// 64 columns); levels >= 3 per (leading digits F, 4 b2 digits and 8 b1 digits,
+// 16-chunk of c) when the row width is at most 16, else per (F, 2 b2 digits, 8 b1
+// digits, 16-chunk of c, 32 columns).  Returns false (no units: the tile kernels
+// run instead) past KR_MAXF leading digits or when the count would not fit.
+bool plan_kr_units(sk_sketch* s) {
+  const int d = s->d, RT = d / 16;
+  std::vector<KrUnit> u;
+  auto add = [&](int j, int mode, long long F, int b2, int b1, int rc, int ct) {
+    u.push_back(KrUnit{s->xoff[j], j, s->C[j], j == s->p ? 1 : 0, mode, (int)F, b2, b1, rc, ct, 0});
+  };
+  for (int j = 0; j <= s->p; ++j) {
+    const int C = s->C[j];
+    double count = 0.0;
+    if (j <= 1) {
+      count = (C + 15) / 16;
+    } else if (j == 2) {
+      count = (double)RT * (d / 8) * ((C + 63) / 64);
+    } else {
+      if (j - 3 > KR_MAXF) return false;
+      const double nF = std::pow((double)d, j - 3);
+      count = C <= 16 ? nF * (d / 4) * (d / 8) * RT : nF * (d / 2) * (d / 8) * RT * ((C + 31) / 32);
+    }
+    if (count + (double)u.size() > (double)(1 << 26)) return false;
+    if (j <= 1) {
+      for (int ct = 0; ct < (C + 15) / 16; ++ct) add(j, KR_SMALL, 0, 0, 0, 0, ct);
+    } else if (j == 2) {
+      for (int rc = 0; rc < RT; ++rc)
+        for (int b1 = 0; b1 < d; b1 += 8)
+          for (int cg = 0; cg < (C + 63) / 64; ++cg) add(j, KR_WIDE, 0, 0, b1, rc, cg);
+    } else {
+      const long long nF = (long long)std::llround(std::pow((double)d, j - 3));
+      for (long long F = 0; F < nF; ++F) {
+        if (C <= 16) {
+          for (int b2 = 0; b2 < d; b2 += 4)
+            for (int b1 = 0; b1 < d; b1 += 8)
+              for (int rc = 0; rc < RT; ++rc) add(j, KR_PAIR, F, b2, b1, rc, 0);
+        } else {
+          for (int b2 = 0; b2 < d; b2 += 2)
+            for (int b1 = 0; b1 < d; b1 += 8)
+              for (int rc = 0; rc < RT; ++rc)
+                for (int ct = 0; ct < (C + 31) / 32; ++ct) add(j, KR_SINGLE, F, b2, b1, rc, ct);
+        }
+      }
+    }
+  }
+  s->kunits.swap(u);
+  return true;
 }
 
 // Query tiles of level j: t trailing digits in the columns (the fewest giving at
@@ -527,6 +602,32 @@ int update_tile_count(const sk_sketch* s) {
   return (int)(s->layout == SK_LAYOUT_SYM ? s->sutiles.size() : s->utiles.size());
 }
 
+// Key splits of the digit-organised update: fill the wave slots (each
+// workgroup holds one wave per SIMD) in whole rounds, at least 256 keys a split.
+int choose_kr_splits(const sk_sketch* s, long long n) {
+  static const int forced = [] {
+    const char* v = std::getenv("EXPSKETCH_UPDATE_SPLITS");
+    return v ? std::max(0, std::atoi(v)) : 0;
+  }();
+  if (forced > 0) return (int)std::max(1LL, std::min<long long>(forced, (n + SK_KB - 1) / SK_KB));
+  const long long items = (long long)s->kunits.size() * s->h;
+  const long long slots = (long long)std::max(1, s->dev.num_cu) * update_kr_waves_per_simd();
+  const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
+  int best = 1;
+  double best_score = -1.0;
+  for (long long ns = 1; ns <= max_ns; ++ns) {
+    const long long wgs = (items * ns + KR_WAVES - 1) / KR_WAVES;
+    const long long rounds = (wgs + slots - 1) / slots;
+    const double eff = (double)wgs / (double)(rounds * slots);
+    const double score = eff - 0.005 * (double)ns;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = (int)ns;
+    }
+  }
+  return best;
+}
+
 int choose_update_splits(const sk_sketch* s, long long n) {
   // EXPSKETCH_UPDATE_SPLITS=<k> fixes the number of key splits (tuning aid).
   static const int forced = [] {
@@ -667,6 +768,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   } else {
     for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
     for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
+    if ((d == 16 || d == 32) && use_update_kr()) plan_kr_units(s);
   }
 
   plan_step(s);
@@ -702,6 +804,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   }
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
+         upload((void**)&s->d_kunits, s->kunits.data(), sizeof(KrUnit) * s->kunits.size()) &&
          hipFuncSetAttribute((const void*)update_kernel_for(false, d, dv),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess &&
          hipFuncSetAttribute((const void*)update_kernel_for(true, d, dv),
@@ -712,6 +815,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   if (!ok) {
     (void)hipGetLastError();
     (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
+    (void)hipFree(s->d_kunits);
     (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
     (void)hipFree(s->d_stiles); (void)hipFree(s->sparts);
     delete s;
@@ -732,12 +836,21 @@ int sketch_layout(sk_handle s, int* layout, int64_t* rows) {
   return SK_OK;
 }
 
+int sketch_update_path(sk_handle s, int* kind) {
+  if (s == nullptr || kind == nullptr) return SK_EINVAL;
+  *kind = s->layout == SK_LAYOUT_SYM ? SK_UPDATE_MULTISET
+          : s->kunits.empty()        ? SK_UPDATE_TILES
+                                     : SK_UPDATE_DIGITS;
+  return SK_OK;
+}
+
 int sketch_destroy(sk_handle s) {
   if (s == nullptr) return SK_OK;
   int rc = SK_OK;
   if (hipStreamSynchronize(s->stream) != hipSuccess) rc = SK_EHIP;
   (void)hipFree(s->state);
   (void)hipFree(s->d_utiles);
+  (void)hipFree(s->d_kunits);
   (void)hipFree(s->d_qtiles);
   (void)hipFree(s->d_sutiles);
   (void)hipFree(s->d_sqtiles);
@@ -790,7 +903,8 @@ namespace {
 // The moment update of n keys per head, K [h][hkeys][d] (keys of head h start at
 // K + h * hkeys * d), V likewise: one launch (plus the deferred reduce).
 int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long long hkeys) {
-  const int ns = choose_update_splits(s, n);
+  const bool kr = s->layout == SK_LAYOUT_FULL && !s->kunits.empty();
+  const int ns = kr ? choose_kr_splits(s, n) : choose_update_splits(s, n);
   long long kps = (n + ns - 1) / ns;
   kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
   const int nsplit = (int)((n + kps - 1) / kps);
@@ -798,7 +912,9 @@ int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long lon
   const int ntiles = update_tile_count(s);
   const long long total = s->XS * s->h;
   const long long rmax = (total / 4 + SK_RED4 - 1) / SK_RED4;     // reduce workgroups
-  if ((long long)ntiles * nsplit * s->h + rmax > 0x7fffffffLL) return SK_EINVAL;
+  const long long kr_wgs = kr ? ((long long)s->kunits.size() * nsplit * s->h + KR_WAVES - 1) / KR_WAVES : 0;
+  if ((long long)ntiles * nsplit * s->h + rmax > 0x7fffffffLL || kr_wgs + rmax > 0x7fffffffLL)
+    return SK_EINVAL;
   const size_t lds = sym ? sym_update_lds_bytes(s->d, s->dv) : update_lds_bytes(s->d, s->dv);
   int rc = SK_OK;
   float* dst = s->state;
@@ -868,9 +984,16 @@ int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long lon
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) err = e;
     }
+  } else if (kr) {
+    hipLaunchKernelGGL(update_kr_kernel_for(s->center != nullptr, s->d),
+                       dim3((unsigned)(kr_wgs + rwgs)), dim3(64 * KR_WAVES), 0, s->stream, K, V,
+                       (long long)n, hkeys, s->dv, s->d_kunits, (int)s->kunits.size(), kps,
+                       nsplit, s->h, dst, s->XS, sstride, acc, s->center, red);
+    err = hipGetLastError();
   } else {
     hipLaunchKernelGGL(update_kernel_for(s->center != nullptr, s->d, s->dv),
-                       dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)), dim3(SK_WG),
+                       dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)),
+                       dim3(SK_WG),
                        lds, s->stream, K, V, (long long)n, hkeys, s->d, s->dv, s->logd,
                        s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,
                        s->center, red);
@@ -915,7 +1038,12 @@ int settle(sk_sketch* s) {
 // 1024 keys.
 long long default_stage_cap(const sk_sketch* s) {
   const long long per_key = (long long)sizeof(float) * (s->d + s->dv) * s->h;
-  long long cap = std::min<long long>(16384, (32LL << 20) / per_key);
+  static const long long keys = [] {   // EXPSKETCH_STAGE_KEYS overrides 32768 (tuning aid)
+    const char* e = std::getenv("EXPSKETCH_STAGE_KEYS");
+    const long long v = e ? std::atoll(e) : 0;
+    return v > 0 ? v : 32768LL;
+  }();
+  long long cap = std::min<long long>(keys, (32LL << 20) / per_key);
   cap = cap / SK_KB * SK_KB;
   return cap >= 1024 ? cap : 0;
 }
@@ -946,11 +1074,16 @@ int sketch_update(sk_handle s, const float* K, const float* V, int64_t n) {
       }
     }
     if (s->stage_cap > 0) {
-      const size_t ks = sizeof(float) * (size_t)s->d, vs = sizeof(float) * (size_t)s->dv;
-      SK_TRY(hipMemcpy2DAsync(s->stage_k + s->stage_n * s->d, ks * s->stage_cap, K, ks * n,
-                              ks * n, s->h, hipMemcpyDeviceToDevice, s->stream));
-      SK_TRY(hipMemcpy2DAsync(s->stage_v + s->stage_n * s->dv, vs * s->stage_cap, V, vs * n,
-                              vs * n, s->h, hipMemcpyDeviceToDevice, s->stream));
+      // one launch appends K and V of every head (n <= stage_cap / 2 keys)
+      const long long w4 = std::max(s->d, s->dv) / 4;
+      const int nb = (int)std::min<long long>(64, (n * w4 + 255) / 256);
+      if ((long long)nb * 2 * s->h > 0x7fffffffLL) return SK_EINVAL;
+      hipLaunchKernelGGL(sk_stage_copy_kernel, dim3((unsigned)(nb * 2 * s->h)), dim3(256), 0,
+                         s->stream, reinterpret_cast<const float4*>(K),
+                         reinterpret_cast<const float4*>(V), (long long)n, s->d / 4, s->dv / 4,
+                         nb, reinterpret_cast<float4*>(s->stage_k),
+                         reinterpret_cast<float4*>(s->stage_v), s->stage_cap, s->stage_n);
+      SK_TRY(hipGetLastError());
       s->stage_n += n;
       s->count += n;
       return s->stage_n == s->stage_cap ? flush_stage(s) : SK_OK;

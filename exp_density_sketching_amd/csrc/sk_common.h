@@ -19,6 +19,13 @@ __device__ __forceinline__ floatx16 mfma32x32x2(float a, float b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x4_f32: D(16x16) += A(16x4) * B(4x16), fp32 in and out.
+// Lane l supplies A[l%16][l/16] and B[l/16][l%16]; accumulator register r of lane
+// l holds D[4*(l/16) + r][l%16].
+__device__ __forceinline__ floatx4v mfma16x16x4(float a, float b, floatx4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }

@@ -65,6 +65,29 @@ __device__ __forceinline__ void pending_reduce_wg(const PendingReduce& r, long l
     split_reduce_one(r.state, r.parts, i, r.nsplit, r.count4);
 }
 
+// Appends one call's keys and values to the staging buffers: the n rows of head
+// hh of K (d4 float4 each) and of V (dv4 float4 each) go to rows [off, off + n)
+// of that head's block of cap rows.  Workgroup w copies part w % nb of segment
+// w / nb, segment 2 hh being head hh's K rows and 2 hh + 1 its V rows, so one
+// launch moves both, 128 bits per thread.
+__global__ __launch_bounds__(256)
+void sk_stage_copy_kernel(const float4* __restrict__ K, const float4* __restrict__ V,
+                          long long n, int d4, int dv4, int nb,
+                          float4* __restrict__ sk, float4* __restrict__ sv,
+                          long long cap, long long off) {
+  const long long seg = blockIdx.x / nb;
+  const int part = (int)(blockIdx.x - seg * nb);
+  const long long hh = seg >> 1;
+  const bool isv = (seg & 1) != 0;
+  const int w4 = isv ? dv4 : d4;
+  const long long cnt = n * w4;
+  const float4* src = (isv ? V : K) + hh * cnt;
+  float4* dst = (isv ? sv : sk) + (hh * cap + off) * w4;
+  for (long long i = (long long)part * blockDim.x + threadIdx.x; i < cnt;
+       i += (long long)nb * blockDim.x)
+    dst[i] = src[i];
+}
+
 __global__ __launch_bounds__(256)
 void sk_fill_zero_kernel(float4* __restrict__ p, long long count4) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < count4;

@@ -34,13 +34,6 @@
 #include "sk_common.h"
 #include "sk_elementwise.h"
 
-// v_mfma_f32_16x16x4_f32: D(16x16) += A(16x4) * B(4x16), fp32 in and out.
-// Lane l supplies A[l%16][l/16] and B[l/16][l%16]; accumulator register r of lane
-// l holds D[4*(l/16) + r][l%16].
-__device__ __forceinline__ floatx4v mfma16x16x4(float a, float b, floatx4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 #define SY_KB 32                 // keys per update stage
 #ifndef SY_LDK
 // row stride of the transposed key/value stage: the A operand reads rows

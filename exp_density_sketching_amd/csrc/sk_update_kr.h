@@ -1,0 +1,406 @@
+// Moment update for key widths d >= 16, organised around the Kronecker digits.
+// Same contraction and state layout as sk_update.h (level j holds
+// X_j[a][e] = sum_i k_i^(x)j[a] u_i[e], u = [k, v] below the top level and
+// u = v at the top; Taylor moments of the polynomial method, "Rumo a Limites
+// Estritos para Atenção em Streaming", "Metodologia", pillar "O Método
+// Polinomial").
+//
+// Write the row index of level j >= 3 as a = (F, b2, b1, c): c the last digit,
+// b1 the one before, b2 the one before that and F the leading j - 3 digits.  Then
+//     X_j[(F, b2, b1, c)][e] = sum_i (k_i[c] k_i[b1]) * (u_i[e] k_i[b2] P_F(k_i)),
+//     P_F(k) = prod of k[f] over the digits f of F,
+// so a block over (b1, c) rows and (b2, e) columns is a v_mfma_f32_32x32x2_f32
+// product over keys (two keys per instruction) whose operands are the raw key
+// and value components, each scaled by one key component.  The 32 rows of a
+// block are (x, c) for a pair b1 = b1p + x, x in {0, 1}, and 16 values of c; the
+// 32 columns are, by the level's row width C:
+//   C <= 16 ("pair"):   (y, e) for a pair b2 = b2p + y and the 16 values of e,
+//   C > 16 ("single"):  32 values of e for one b2,
+// and at level 2 (no b2 digit, "wide") 32 values of e.  A wave owns a unit: 4
+// b1 pairs x 2 b2 pairs (or b2 values, or 32-column chunks), one 16-chunk of c
+// and F, i.e. 8 blocks (128 accumulator registers).  Per two keys it loads the
+// key and value components it needs with 64-byte loads, rotates the key row so
+// that the unit's b1 (b2) digits line up, and forms each operand with one
+// VALU multiply whose second factor is a DPP row broadcast (v_mul_f32_dpp
+// row_newbcast): 6 such multiplies feed 8 matrix instructions, and no feature
+// tile passes through LDS.  Levels 0 and 1 (no b1 digit) run a small 16x16x4
+// path: level 1 is k[c] u[e], level 0 the sum of u[e] (A operand 1 in row 0).
+//
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l % 32][l / 32] and
+// B[l / 32][l % 32]; accumulator register r of lane l holds
+// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  Here l / 32 is the key of the
+// step, and within a 16-lane DPP row (lanes 16 q .. 16 q + 15) the row parity
+// q & 1 is x (A side) or y (B side, pair mode) and the lane's position m is c
+// or e mod 16.
+#pragma once
+
+#include "sk_common.h"
+#include "sk_elementwise.h"
+
+#include <type_traits>
+
+#define KR_WAVES 4          // independent waves per workgroup
+#define KR_PF 3             // key steps fetched ahead
+#define KR_SLOTS 4          // prefetch ring slots (one more than KR_PF: a step
+                            // loads into the slot the previous step consumed)
+#define KR_NA 4             // b1 pairs per unit
+#define KR_NB 2             // b2 pairs (pair mode), b2 values (single) or 32-column chunks (wide)
+#define KR_MAXF 4           // leading digits F per unit
+
+// Unit modes
+#define KR_SMALL 0          // levels 0 and 1
+#define KR_PAIR 1           // levels >= 3, C <= 16
+#define KR_SINGLE 2         // levels >= 3, C > 16
+#define KR_WIDE 3           // level 2
+
+// One unit of work.
+struct KrUnit {
+  long long xoff;   // float offset of level j inside one head's state
+  int j;            // level
+  int C;            // row width of the level (d + dv, or dv at the top)
+  int top;          // 1 at the top level (u = v)
+  int mode;         // KR_SMALL, KR_PAIR, KR_SINGLE or KR_WIDE
+  int F;            // leading digits (KR_PAIR, KR_SINGLE) as a number in base d
+  int b2;           // first b2 digit (KR_PAIR, KR_SINGLE)
+  int b1;           // first b1 digit (not KR_SMALL)
+  int rc;           // 16-chunk of the last digit c (not KR_SMALL)
+  int ct;           // column chunk: 32 wide (KR_SINGLE), 64 wide (KR_WIDE), 16 wide (KR_SMALL)
+  int pad_;
+};
+
+// src[lane N of this lane's 16-lane row] * y: one v_mul_f32_dpp row_newbcast.
+template <int N>
+__device__ __forceinline__ float kr_bmul(float src, float y) {
+  const float b = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), 0x150 + N, 0xf, 0xf,
+                                         false));
+  return b * y;
+}
+
+// u component e of one key: a key component below the top level for e < d,
+// else a value component; zero past the row width or the value width.
+__device__ __forceinline__ float kr_u(const float* __restrict__ krow, const float* __restrict__ vrow,
+                                      int e, int d, int dv, int C, int top, bool ok) {
+  if (!ok || e >= C) return 0.f;
+  if (!top && e < d) return krow[e];
+  const int c = top ? e : e - d;
+  return c < dv ? vrow[c] : 0.f;
+}
+
+// One unit at levels >= 2 (see the layout above), specialised by mode, number
+// of blocks per b1 pair (NBE) and number of leading digits (NF), so that a key
+// step is straight-line code: loads for a later step, the centring, two row
+// rotations, 4 + NBE fused broadcast multiplies and 4 NBE matrix instructions.
+// Loads past the key range read the last key of the range; its A operands are
+// then zeroed, so it adds nothing.
+template <int RT, bool CENTER, int MODE, int NBE, int NF>
+__device__ __forceinline__
+void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restrict__ Vh, int dv,
+             long long k_begin, long long k_end, const float* __restrict__ cen,
+             float* __restrict__ o, int accumulate) {
+  constexpr int d = 16 * RT;
+  constexpr int LOGD = RT == 1 ? 4 : RT == 2 ? 5 : RT == 4 ? 6 : 7;
+  constexpr int NBU = MODE == KR_WIDE ? NBE : 1;     // distinct u operands
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15;
+  const int khalf = lane >> 5;                        // key of the step
+  const int l32 = lane & 31;
+  const int par = (lane >> 4) & 1;                    // x (A rows) or y (B columns, pair mode)
+  const int rowbase = lane & 48;
+  const int nstep = (int)((k_end - k_begin + 1) / 2);
+  const long long klast = k_end - 1;
+  // rows of this lane's key at step 0 (clamped into the range); the key of step
+  // st is key0 + min(2 st, kmax), so loads never leave the range
+  const bool valid0 = k_begin + khalf < k_end;
+  const long long key0 = valid0 ? k_begin + khalf : klast;
+  const int kmax = (int)(klast - key0);
+  const float* krow0 = Kh + key0 * d;
+  // u columns: e, its source row pointer at step 0 and stride per row (floats)
+  const float* up[NBU];
+  int ustr[NBU];
+  float umask[NBU];
+#pragma unroll
+  for (int y = 0; y < NBU; ++y) {
+    const int e = MODE == KR_PAIR ? m : MODE == KR_SINGLE ? 32 * U.ct + l32 : 64 * U.ct + 32 * y + l32;
+    const bool fromk = !U.top && e < d;
+    const int col = fromk ? e : (U.top ? e : e - d);
+    const bool valid = e < U.C && (fromk || col < dv);
+    up[y] = fromk ? krow0 + (valid ? col : 0) : Vh + key0 * dv + (valid ? col : 0);
+    ustr[y] = fromk ? d : dv;
+    umask[y] = valid ? 1.f : 0.f;
+  }
+  float cu[NBU];
+#pragma unroll
+  for (int y = 0; y < NBU; ++y) {
+    const int e = MODE == KR_PAIR ? m : MODE == KR_SINGLE ? 32 * U.ct + l32 : 64 * U.ct + 32 * y + l32;
+    cu[y] = (CENTER && !U.top && e < d) ? cen[e] : 0.f;
+  }
+  const int q1 = U.b1 >> 4, q2 = U.b2 >> 4;
+  const int src1 = (rowbase + ((m + (U.b1 & 15) + par) & 15)) * 4;
+  const int src2 = (rowbase + ((m + (U.b2 & 15) + (MODE == KR_PAIR ? par : 0)) & 15)) * 4;
+  int fdig[NF > 0 ? NF : 1];
+  float cf[NF > 0 ? NF : 1];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    fdig[f] = (U.F >> (LOGD * (NF - 1 - f))) & (d - 1);
+    cf[f] = CENTER ? cen[fdig[f]] : 0.f;
+  }
+  const float ca = CENTER ? cen[16 * U.rc + m] : 0.f;
+  const float c1 = CENTER ? cen[16 * q1 + m] : 0.f;
+  const float c2 = CENTER ? cen[16 * q2 + m] : 0.f;
+
+  // prefetch ring (static slots)
+  float ra[KR_SLOTS], r1[KR_SLOTS], r2[KR_SLOTS], ru[KR_SLOTS][NBU], rf[KR_SLOTS][NF > 0 ? NF : 1];
+  auto fetch = [&](int st, int sl) {      // unconditional: no merge of old and new slots
+    const int off = 2 * st < kmax ? 2 * st : kmax;
+    const float* kr = krow0 + off * d;
+    ra[sl] = kr[16 * U.rc + m];
+    if (RT > 1) {
+      r1[sl] = kr[16 * q1 + m];
+      if (MODE != KR_WIDE) r2[sl] = kr[16 * q2 + m];
+    }
+#pragma unroll
+    for (int y = 0; y < NBU; ++y) ru[sl][y] = up[y][off * ustr[y]];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) rf[sl][f] = kr[fdig[f]];
+  };
+#pragma unroll
+  for (int s = 0; s < KR_PF; ++s) fetch(s, s);
+
+  floatx16 acc[KR_NA][NBE];
+#pragma unroll
+  for (int x = 0; x < KR_NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NBE; ++y) acc[x][y] = floatx16{0};
+
+  // the row rotations of the key components holding b1 and b2 for a step:
+  // lane 2 x of row parity x' gets k[b1 + 2 x + x'], and lane 2 y of parity y'
+  // k[b2 + 2 y + y'] (pair) or lane y k[b2 + y] (single)
+  auto rotate = [&](int sl, float& x1, float& x2) {
+    float k1 = RT > 1 ? r1[sl] : ra[sl];
+    float k2 = RT > 1 ? (MODE != KR_WIDE ? r2[sl] : 0.f) : ra[sl];
+    if (CENTER) {
+      k1 -= RT > 1 ? c1 : ca;
+      k2 -= RT > 1 ? c2 : ca;
+    }
+    x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, k1)));
+    x2 = MODE == KR_WIDE ? 0.f
+         : __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src2, __builtin_bit_cast(int, k2)));
+  };
+  // rotations of the current step, issued one step ahead
+  float xr1, xr2;
+  rotate(0, xr1, xr2);
+
+  auto step = [&](int st, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const bool ok = valid0 && 2 * st <= kmax;
+    float a = ra[SL], u[NBU], p = 1.f;
+#pragma unroll
+    for (int y = 0; y < NBU; ++y) u[y] = ru[SL][y];
+    float fv[NF > 0 ? NF : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fv[f] = rf[SL][f];
+    const float x1 = xr1, x2 = xr2;
+    // the loads for step st + KR_PF and the rotations for step st + 1 go out
+    // here, ahead of this step's work (the scheduler would otherwise sink them
+    // next to their use)
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(st + KR_PF, (SL + KR_PF) % KR_SLOTS);
+    rotate((SL + 1) % KR_SLOTS, xr1, xr2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (CENTER) {
+      a -= ca;
+#pragma unroll
+      for (int y = 0; y < NBU; ++y) u[y] -= cu[y];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) fv[f] -= cf[f];
+    }
+    a = ok ? a : 0.f;                    // a key past the range adds nothing
+#pragma unroll
+    for (int f = 0; f < NF; ++f) p *= fv[f];
+    float A[KR_NA];
+    A[0] = kr_bmul<0>(x1, a);
+    A[1] = kr_bmul<2>(x1, a);
+    A[2] = kr_bmul<4>(x1, a);
+    A[3] = kr_bmul<6>(x1, a);
+    float B[NBE];
+    if constexpr (MODE == KR_WIDE) {
+#pragma unroll
+      for (int y = 0; y < NBE; ++y) B[y] = u[y] * umask[y];
+    } else {
+      const float pu = u[0] * umask[0] * p;
+      if constexpr (MODE == KR_PAIR) {
+        B[0] = kr_bmul<0>(x2, pu);
+        B[1] = kr_bmul<2>(x2, pu);
+      } else {
+        B[0] = kr_bmul<0>(x2, pu);
+        B[1] = kr_bmul<1>(x2, pu);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < KR_NA; ++x)
+#pragma unroll
+      for (int y = 0; y < NBE; ++y) acc[x][y] = mfma32x32x2(A[x], B[y], acc[x][y]);
+  };
+  static_assert(KR_PF == 3 && KR_SLOTS == 4 && KR_NA == 4, "the step is written for these sizes");
+  // whole groups of KR_SLOTS steps with no branches inside (a merge of ring slots
+  // would make the compiler wait for loads just issued); steps past the range
+  // have zero A operands
+  for (int st0 = 0; st0 < nstep; st0 += KR_SLOTS) {
+    step(st0, std::integral_constant<int, 0>{});
+    step(st0 + 1, std::integral_constant<int, 1>{});
+    step(st0 + 2, std::integral_constant<int, 2>{});
+    step(st0 + 3, std::integral_constant<int, 3>{});
+  }
+
+  // Epilogue.  Block (x, y), register r: row 8 (r / 4) + 4 khalf + r % 4 =
+  // (x' = row / 16, c = 16 rc + row % 16) with b1 = b1 + 2 x + x'; column l32 =
+  // (y' = l32 / 16, e = l32 % 16) with b2 = b2 + 2 y + y' (pair), or e in the
+  // unit's 32-column chunk with b2 = b2 + y (single), or e in 32-column chunk y
+  // of the unit's 64 (wide).
+#pragma unroll
+  for (int y = 0; y < NBE; ++y) {
+    int e, b2;
+    if (MODE == KR_PAIR) { e = m; b2 = U.b2 + 2 * y + par; }
+    else if (MODE == KR_SINGLE) { e = 32 * U.ct + l32; b2 = U.b2 + y; }
+    else { e = 64 * U.ct + 32 * y + l32; b2 = 0; }
+    if (e >= U.C) continue;
+    // rows above b1: F and b2 for levels >= 3, nothing at level 2
+    const long long hi = MODE == KR_WIDE ? 0 : (long long)U.F * d + b2;
+#pragma unroll
+    for (int x = 0; x < KR_NA; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * khalf + (r & 3);
+        const int b1 = U.b1 + 2 * x + (row >> 4);
+        const int c = 16 * U.rc + (row & 15);
+        const long long a = (hi * d + b1) * d + c;
+        float* dst = o + a * U.C + e;
+        *dst = accumulate ? *dst + acc[x][y][r] : acc[x][y][r];
+      }
+  }
+}
+
+template <int RT, bool CENTER>
+__global__ __launch_bounds__(64 * KR_WAVES, 2)
+void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ V,
+                         long long n, long long hkeys, int dv,
+                         const KrUnit* __restrict__ units, int nunits,
+                         long long keys_per_split, int nsplit, int nhead,
+                         float* __restrict__ out, long long head_stride,
+                         long long split_stride, int accumulate,
+                         const float* __restrict__ center, PendingReduce red) {
+  constexpr int d = 16 * RT;
+  const long long nitems = (long long)nunits * nsplit * nhead;
+  const long long nwg = (nitems + KR_WAVES - 1) / KR_WAVES;
+  if ((long long)blockIdx.x >= nwg) {
+    pending_reduce_wg(red, (long long)blockIdx.x - nwg);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // workgroups of one XCD take a contiguous range of items: the items of one key
+  // split (all units) read the same key rows from that XCD's L2
+  const long long item = xcd_remap(blockIdx.x, nwg) * KR_WAVES + wave;
+  if (item >= nitems) return;
+  const int unit_id = (int)(item % nunits);
+  const long long split = (item / nunits) % nsplit;
+  const long long head = item / ((long long)nunits * nsplit);
+  const KrUnit U = units[unit_id];
+
+  const long long k_begin = split * keys_per_split;
+  long long k_end = k_begin + keys_per_split;
+  if (k_end > n) k_end = n;
+  const float* Kh = K + head * hkeys * d;
+  const float* Vh = V + head * hkeys * dv;
+  const float* cen = CENTER ? center + head * d : nullptr;
+  float* o = out + split * split_stride + head * head_stride + U.xoff;
+  const int m = lane & 15;
+
+  if (U.mode == KR_SMALL) {
+    // ---- levels 0 and 1 with v_mfma_f32_16x16x4_f32: lane 16 kk + i supplies
+    // A[i][kk] = k[16 r + i] (level 1) or [i == 0] (level 0) and B[kk][i] = u[e]
+    const int kk = lane >> 4;
+    const int nstep = k_end > k_begin ? (int)((k_end - k_begin + 3) / 4) : 0;
+    const int e = 16 * U.ct + m;
+    floatx4v acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = floatx4v{0.f, 0.f, 0.f, 0.f};
+    // prefetch ring (static slots): key components 16 r + m and the u component
+    float sa[KR_PF][RT], su[KR_PF];
+    auto sfetch = [&](int st, int sl) {
+      const long long key = k_begin + 4LL * st + kk;
+      const bool ok = key < k_end;
+      const float* krow = Kh + key * d;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sa[sl][r] = (ok && U.j == 1) ? krow[16 * r + m] : 0.f;
+      su[sl] = kr_u(krow, Vh + key * dv, e, d, dv, U.C, U.top, ok);
+    };
+#pragma unroll
+    for (int s2 = 0; s2 < KR_PF; ++s2)
+      if (s2 < nstep) sfetch(s2, s2);
+    auto sstep = [&](int st, auto slot_c) {
+      constexpr int SL = decltype(slot_c)::value;
+      const bool ok = k_begin + 4LL * st + kk < k_end;
+      float u = su[SL], a[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[r] = sa[SL][r];
+      if (st + KR_PF < nstep) sfetch(st + KR_PF, SL);
+      if (CENTER && ok && !U.top && e < d) u -= cen[e];
+      if (U.j == 1) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          if (CENTER && ok) a[r] -= cen[16 * r + m];
+          acc[r] = mfma16x16x4(a[r], u, acc[r]);
+        }
+      } else {
+        acc[0] = mfma16x16x4(m == 0 ? 1.f : 0.f, u, acc[0]);
+      }
+    };
+    for (int st0 = 0; st0 < nstep; st0 += KR_PF) {
+      sstep(st0, std::integral_constant<int, 0>{});
+      if (st0 + 1 < nstep) sstep(st0 + 1, std::integral_constant<int, 1>{});
+      if (st0 + 2 < nstep) sstep(st0 + 2, std::integral_constant<int, 2>{});
+    }
+    if (e >= U.C) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 16 * r + 4 * kk + q;       // row of level 1, or 0 at level 0
+        const bool keep = U.j == 1 ? true : (r == 0 && c == 0);
+        if (keep) {
+          float* dst = o + (long long)c * U.C + e;
+          *dst = accumulate ? *dst + acc[r][q] : acc[r][q];
+        }
+      }
+    return;
+  }
+
+  // ---- levels >= 2 with v_mfma_f32_32x32x2_f32: a loop specialised per mode,
+  // number of blocks and number of leading digits
+  const int nbe = U.mode == KR_WIDE ? (U.C - 64 * U.ct > 32 ? 2 : 1) : KR_NB;
+  const int nf = U.mode == KR_WIDE ? 0 : U.j - 3;
+#define KR_CALL(MODE, NBE, NF)                                                              \
+  kr_body<RT, CENTER, MODE, NBE, NF>(U, Kh, Vh, dv, k_begin, k_end, cen, o, accumulate)
+  if (U.mode == KR_WIDE) {
+    if (nbe == 2) KR_CALL(KR_WIDE, 2, 0); else KR_CALL(KR_WIDE, 1, 0);
+  } else if (U.mode == KR_PAIR) {
+    switch (nf) {
+      case 0: KR_CALL(KR_PAIR, 2, 0); break;
+      case 1: KR_CALL(KR_PAIR, 2, 1); break;
+      case 2: KR_CALL(KR_PAIR, 2, 2); break;
+      case 3: KR_CALL(KR_PAIR, 2, 3); break;
+      default: KR_CALL(KR_PAIR, 2, 4); break;
+    }
+  } else {
+    switch (nf) {
+      case 0: KR_CALL(KR_SINGLE, 2, 0); break;
+      case 1: KR_CALL(KR_SINGLE, 2, 1); break;
+      case 2: KR_CALL(KR_SINGLE, 2, 2); break;
+      case 3: KR_CALL(KR_SINGLE, 2, 3); break;
+      default: KR_CALL(KR_SINGLE, 2, 4); break;
+    }
+  }
+#undef KR_CALL
+}

@@ -93,6 +93,19 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
  */
 int sketch_layout(sk_handle s, int* layout, int64_t* rows);
 
+/* Update kernels (sketch_update_path). */
+#define SK_UPDATE_TILES 0     /* full layout: feature tiles in LDS, any d */
+#define SK_UPDATE_DIGITS 1    /* full layout, d = 16 or 32: operands scaled in registers */
+#define SK_UPDATE_MULTISET 2  /* multiset layout */
+
+/*
+ * sketch_update_path -- which kernel the handle's update calls launch (one of
+ * SK_UPDATE_*), fixed at creation.  All compute the same moments; this lets a
+ * caller (a profiler, a benchmark) name the kernel it measures.
+ * Errors: SK_EINVAL (NULL handle or NULL kind).
+ */
+int sketch_update_path(sk_handle s, int* kind);
+
 /*
  * sketch_set_center -- recentre the expansion at a fixed centre c per head
  * ("Metodologia", pillar "Particionamento de Espaço e Recentramento": a dense

@@ -97,6 +97,7 @@ def test_null_handles_are_rejected():
     assert lib.sketch_info(None, None, None, None, None, None, None) == -1
     assert lib.sketch_set_stream(None, None) == -1
     assert lib.sketch_layout(None, None, None) == -1
+    assert lib.sketch_update_path(None, None) == -1
     assert lib.sketch_set_center(None, None) == -1
     assert lib.sketch_step(None, None, None, None, None, None) == -1
 

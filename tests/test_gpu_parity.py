@@ -333,3 +333,17 @@ def test_staged_calls_equal_direct_calls(layout):
         assert np.max(np.abs(out[hd] - o_ref[0])) <= SK_O_ABS
     for x in (st, ref, a, b):
         x.destroy()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d,layout,want", [(16, "full", "digits"), (32, "full", "digits"),
+                                           (64, "full", "tiles"), (8, "full", "tiles"),
+                                           (16, "sym", "multiset")])
+def test_update_path(d, layout, want):
+    """Key widths 16 and 32 run the digit-organised kernel, the others the tile
+    kernel (both checked against the oracle above); the multiset layout its own."""
+    s = E.sketch_create(d, d, 3, 1, layout)
+    try:
+        assert E.sketch_update_path(s) == want
+    finally:
+        s.destroy()
