@@ -38,6 +38,7 @@
 #include "sk_elementwise.h"
 
 #include <type_traits>
+#include <utility>
 
 #define KR_WAVES 4          // independent waves per workgroup
 #define KR_PF 3             // key steps fetched ahead
@@ -107,17 +108,18 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   const int l32 = lane & 31;
   const int par = (lane >> 4) & 1;                    // x (A rows) or y (B columns, pair mode)
   const int rowbase = lane & 48;
-  const int nstep = (int)((k_end - k_begin + 1) / 2);
-  const long long klast = k_end - 1;
-  // rows of this lane's key at step 0 (clamped into the range); the key of step
-  // st is key0 + min(2 st, kmax), so loads never leave the range
-  const bool valid0 = k_begin + khalf < k_end;
-  const long long key0 = valid0 ? k_begin + khalf : klast;
-  const int kmax = (int)(klast - key0);
-  const float* krow0 = Kh + key0 * d;
-  // u columns: e, its source row pointer at step 0 and stride per row (floats)
-  const float* up[NBU];
-  int ustr[NBU];
+  // Steps of two keys.  The npair full steps read their rows at a row base that
+  // is the same for the whole wave (keys k_begin + 2 st and k_begin + 2 st + 1,
+  // the step clamped to the last full one), so a load is a scalar base plus a
+  // fixed lane offset; a lone last key (odd count) gets a step of its own.
+  const long long nk = k_end - k_begin;
+  const int npair = (int)(nk >> 1);
+  const float* Kb = Kh + k_begin * d;
+  const float* Vb = Vh + k_begin * dv;
+  // u columns: lane offsets into the key row (lk) and the value row (lv), which
+  // of the two the lane takes, and a mask for columns past the row width
+  int lk[NBU], lv[NBU];
+  bool usel[NBU];
   float umask[NBU];
 #pragma unroll
   for (int y = 0; y < NBU; ++y) {
@@ -125,8 +127,9 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     const bool fromk = !U.top && e < d;
     const int col = fromk ? e : (U.top ? e : e - d);
     const bool valid = e < U.C && (fromk || col < dv);
-    up[y] = fromk ? krow0 + (valid ? col : 0) : Vh + key0 * dv + (valid ? col : 0);
-    ustr[y] = fromk ? d : dv;
+    lk[y] = khalf * d + (fromk && valid ? col : 0);
+    lv[y] = khalf * dv + (!fromk && valid ? col : 0);
+    usel[y] = fromk;
     umask[y] = valid ? 1.f : 0.f;
   }
   float cu[NBU];
@@ -136,13 +139,17 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     cu[y] = (CENTER && !U.top && e < d) ? cen[e] : 0.f;
   }
   const int q1 = U.b1 >> 4, q2 = U.b2 >> 4;
+  const int la = khalf * d + 16 * U.rc + m;           // lane offsets of key components
+  const int l1 = khalf * d + 16 * q1 + m;
+  const int l2 = khalf * d + 16 * q2 + m;
   const int src1 = (rowbase + ((m + (U.b1 & 15) + par) & 15)) * 4;
   const int src2 = (rowbase + ((m + (U.b2 & 15) + (MODE == KR_PAIR ? par : 0)) & 15)) * 4;
-  int fdig[NF > 0 ? NF : 1];
+  int fdig[NF > 0 ? NF : 1], lf[NF > 0 ? NF : 1];
   float cf[NF > 0 ? NF : 1];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     fdig[f] = (U.F >> (LOGD * (NF - 1 - f))) & (d - 1);
+    lf[f] = khalf * d + fdig[f];
     cf[f] = CENTER ? cen[fdig[f]] : 0.f;
   }
   const float ca = CENTER ? cen[16 * U.rc + m] : 0.f;
@@ -151,21 +158,31 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
 
   // prefetch ring (static slots)
   float ra[KR_SLOTS], r1[KR_SLOTS], r2[KR_SLOTS], ru[KR_SLOTS][NBU], rf[KR_SLOTS][NF > 0 ? NF : 1];
-  auto fetch = [&](int st, int sl) {      // unconditional: no merge of old and new slots
-    const int off = 2 * st < kmax ? 2 * st : kmax;
-    const float* kr = krow0 + off * d;
-    ra[sl] = kr[16 * U.rc + m];
+  // one step's components from the rows at kr (keys) and vr (values)
+  auto load = [&](const float* kr, const float* vr, float& va, float& v1, float& v2,
+                  float (&vu)[NBU], float (&vf)[NF > 0 ? NF : 1]) {
+    va = kr[la];
     if (RT > 1) {
-      r1[sl] = kr[16 * q1 + m];
-      if (MODE != KR_WIDE) r2[sl] = kr[16 * q2 + m];
+      v1 = kr[l1];
+      if (MODE != KR_WIDE) v2 = kr[l2];
     }
 #pragma unroll
-    for (int y = 0; y < NBU; ++y) ru[sl][y] = up[y][off * ustr[y]];
+    for (int y = 0; y < NBU; ++y) {
+      if constexpr (MODE == KR_PAIR) vu[y] = vr[lv[y]];   // the top level: u = v
+      else vu[y] = usel[y] ? kr[lk[y]] : vr[lv[y]];
+    }
 #pragma unroll
-    for (int f = 0; f < NF; ++f) rf[sl][f] = kr[fdig[f]];
+    for (int f = 0; f < NF; ++f) vf[f] = kr[lf[f]];
   };
+  auto fetch = [&](int st, int sl) {      // unconditional: no merge of old and new slots
+    const int lastp = npair > 0 ? 2 * (npair - 1) : 0;
+    const int off = 2 * st < lastp ? 2 * st : lastp;       // uniform
+    load(Kb + (long long)off * d, Vb + (long long)off * dv, ra[sl], r1[sl], r2[sl], ru[sl], rf[sl]);
+  };
+  if (npair > 0) {
 #pragma unroll
-  for (int s = 0; s < KR_PF; ++s) fetch(s, s);
+    for (int s = 0; s < KR_PF; ++s) fetch(s, s);
+  }
 
   floatx16 acc[KR_NA][NBE];
 #pragma unroll
@@ -176,9 +193,9 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   // the row rotations of the key components holding b1 and b2 for a step:
   // lane 2 x of row parity x' gets k[b1 + 2 x + x'], and lane 2 y of parity y'
   // k[b2 + 2 y + y'] (pair) or lane y k[b2 + y] (single)
-  auto rotate = [&](int sl, float& x1, float& x2) {
-    float k1 = RT > 1 ? r1[sl] : ra[sl];
-    float k2 = RT > 1 ? (MODE != KR_WIDE ? r2[sl] : 0.f) : ra[sl];
+  auto rotate = [&](float va, float v1, float v2, float& x1, float& x2) {
+    float k1 = RT > 1 ? v1 : va;
+    float k2 = RT > 1 ? (MODE != KR_WIDE ? v2 : 0.f) : va;
     if (CENTER) {
       k1 -= RT > 1 ? c1 : ca;
       k2 -= RT > 1 ? c2 : ca;
@@ -187,27 +204,10 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     x2 = MODE == KR_WIDE ? 0.f
          : __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src2, __builtin_bit_cast(int, k2)));
   };
-  // rotations of the current step, issued one step ahead
-  float xr1, xr2;
-  rotate(0, xr1, xr2);
-
-  auto step = [&](int st, auto slot_c) {
-    constexpr int SL = decltype(slot_c)::value;
-    const bool ok = valid0 && 2 * st <= kmax;
-    float a = ra[SL], u[NBU], p = 1.f;
-#pragma unroll
-    for (int y = 0; y < NBU; ++y) u[y] = ru[SL][y];
-    float fv[NF > 0 ? NF : 1];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) fv[f] = rf[SL][f];
-    const float x1 = xr1, x2 = xr2;
-    // the loads for step st + KR_PF and the rotations for step st + 1 go out
-    // here, ahead of this step's work (the scheduler would otherwise sink them
-    // next to their use)
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(st + KR_PF, (SL + KR_PF) % KR_SLOTS);
-    rotate((SL + 1) % KR_SLOTS, xr1, xr2);
-    __builtin_amdgcn_sched_barrier(0);
+  // operands and matrix instructions of one step from its components (a = 0 for
+  // a key that adds nothing)
+  auto compute = [&](float a, float (&u)[NBU], float (&fv)[NF > 0 ? NF : 1], float x1, float x2) {
+    float p = 1.f;
     if (CENTER) {
       a -= ca;
 #pragma unroll
@@ -215,9 +215,11 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
 #pragma unroll
       for (int f = 0; f < NF; ++f) fv[f] -= cf[f];
     }
-    a = ok ? a : 0.f;                    // a key past the range adds nothing
 #pragma unroll
     for (int f = 0; f < NF; ++f) p *= fv[f];
+    return std::make_pair(a, p);
+  };
+  auto mma = [&](float a, float p, const float (&u)[NBU], float x1, float x2) {
     float A[KR_NA];
     A[0] = kr_bmul<0>(x1, a);
     A[1] = kr_bmul<2>(x1, a);
@@ -242,15 +244,50 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
 #pragma unroll
       for (int y = 0; y < NBE; ++y) acc[x][y] = mfma32x32x2(A[x], B[y], acc[x][y]);
   };
+
+  // rotations of the current step, issued one step ahead
+  float xr1 = 0.f, xr2 = 0.f;
+  if (npair > 0) rotate(ra[0], r1[0], r2[0], xr1, xr2);
+
+  auto step = [&](int st, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    float u[NBU], fv[NF > 0 ? NF : 1];
+    const float a0v = ra[SL];
+#pragma unroll
+    for (int y = 0; y < NBU; ++y) u[y] = ru[SL][y];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fv[f] = rf[SL][f];
+    const float x1 = xr1, x2 = xr2;
+    // the loads for step st + KR_PF and the rotations for step st + 1 go out
+    // here, ahead of this step's work (the scheduler would otherwise sink them
+    // next to their use)
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(st + KR_PF, (SL + KR_PF) % KR_SLOTS);
+    constexpr int SN = (SL + 1) % KR_SLOTS;
+    rotate(ra[SN], r1[SN], r2[SN], xr1, xr2);
+    __builtin_amdgcn_sched_barrier(0);
+    auto ap = compute(a0v, u, fv, x1, x2);
+    const float a = st < npair ? ap.first : 0.f;     // uniform: steps past the pairs add nothing
+    mma(a, ap.second, u, x1, x2);
+  };
   static_assert(KR_PF == 3 && KR_SLOTS == 4 && KR_NA == 4, "the step is written for these sizes");
   // whole groups of KR_SLOTS steps with no branches inside (a merge of ring slots
-  // would make the compiler wait for loads just issued); steps past the range
-  // have zero A operands
-  for (int st0 = 0; st0 < nstep; st0 += KR_SLOTS) {
+  // would make the compiler wait for loads just issued)
+  for (int st0 = 0; st0 < npair; st0 += KR_SLOTS) {
     step(st0, std::integral_constant<int, 0>{});
     step(st0 + 1, std::integral_constant<int, 1>{});
     step(st0 + 2, std::integral_constant<int, 2>{});
     step(st0 + 3, std::integral_constant<int, 3>{});
+  }
+  if (nk & 1) {
+    // the lone last key: both lane halves read its row, the second half adds nothing
+    const long long lastk = nk - 1;
+    float va = 0.f, v1 = 0.f, v2 = 0.f, u[NBU], fv[NF > 0 ? NF : 1];
+    load(Kb + lastk * d - khalf * d, Vb + lastk * dv - khalf * dv, va, v1, v2, u, fv);
+    float x1, x2;
+    rotate(va, v1, v2, x1, x2);
+    auto ap = compute(va, u, fv, x1, x2);
+    mma(khalf == 0 ? ap.first : 0.f, ap.second, u, x1, x2);
   }
 
   // Epilogue.  Block (x, y), register r: row 8 (r / 4) + 4 khalf + r % 4 =
