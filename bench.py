@@ -293,6 +293,17 @@ def main():
     full = measure("full")
     sketches = full["sketches"]
     ukern = E.UPDATE_KERNELS[E.sketch_update_path(sketches[0])]
+    # the last timed step's sketch answers against its exact answers, and the
+    # truncation bound rho^(p+1)/(p+1)! e^(2 rho), rho = max|q| max|k| per head
+    zs, ze = z_s.cpu().double().numpy(), z_e.cpu().double().numpy()
+    os_, oe = out_s.cpu().double().numpy(), out_e.cpu().double().numpy()
+    rho = max(float(np.linalg.norm(K[hd].astype(np.float64), axis=1).max() *
+                    np.linalg.norm(Q[hd].astype(np.float64), axis=1).max())
+              for hd in range(w.h))
+    sketch_error = {"z_rel_max": float(np.max(np.abs(zs - ze) / ze)),
+                    "o_abs_max": float(np.max(np.abs(os_ - oe))),
+                    "z_rel_bound": rho ** (w.p + 1) / math.factorial(w.p + 1) * math.exp(2 * rho),
+                    "rho": rho}
     t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
     dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
@@ -367,6 +378,7 @@ def main():
         "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
                          "kv_bytes": kv_bytes,
                          "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
+        "sketch_error": sketch_error,
         "roofline": {"kernel": ukern, "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,

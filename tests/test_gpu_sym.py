@@ -80,14 +80,15 @@ def test_sym_equals_full_layout():
 
 def test_sym_empty_degenerate_and_merge():
     sk = E.sketch_create(8, 4, 3, layout="sym")
-    Q = torch.randn(5, 8, device="cuda")
+    rng = np.random.default_rng(6)
+    Q = gpu(rng.standard_normal((5, 8)).astype(np.float32))[0]
     out, Z = host(*E.sketch_query(sk, Q))
     assert np.all(Z == 0.0) and np.all(np.isnan(out))
     E.sketch_update(sk, torch.empty(0, 8, device="cuda"), torch.empty(0, 4, device="cuda"))
     assert sk.count == 0
     # q = 0: Zhat = n, ohat = mean of the values
-    K = torch.randn(777, 8, device="cuda") * 0.3
-    V = torch.randn(777, 4, device="cuda")
+    K, V = gpu((rng.standard_normal((777, 8)) * 0.3).astype(np.float32),
+               rng.standard_normal((777, 4)).astype(np.float32))
     E.sketch_update(sk, K, V)
     out, Z = host(*E.sketch_query(sk, torch.zeros(3, 8, device="cuda")))
     vbar = V.double().mean(0).cpu().numpy()
