@@ -92,8 +92,8 @@ __device__ __forceinline__ float kr_u(const float* __restrict__ krow, const floa
 // of blocks per b1 pair (NBE) and number of leading digits (NF), so that a key
 // step is straight-line code: loads for a later step, the centring, two row
 // rotations, 4 + NBE fused broadcast multiplies and 4 NBE matrix instructions.
-// Loads past the key range read the last key of the range; its A operands are
-// then zeroed, so it adds nothing.
+// Steps past the last full pair of keys (the ring runs in groups of four)
+// re-read that pair's rows with zero A operands, so they add nothing.
 template <int RT, bool CENTER, int MODE, int NBE, int NF>
 __device__ __forceinline__
 void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restrict__ Vh, int dv,
