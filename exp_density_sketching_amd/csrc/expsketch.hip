@@ -132,7 +132,7 @@ using UpdateKernel = void (*)(const float*, const float*, long long, long long, 
                               const UpdTile*, int, long long, int, int, float*, long long,
                               long long, int, const float*, PendingReduce);
 using UpdateKrKernel = void (*)(const float*, const float*, long long, long long, int,
-                                const KrUnit*, int, long long, int, int, float*, long long,
+                                const KrUnit*, KrSplits, int, float*, long long,
                                 long long, int, const float*, PendingReduce);
 UpdateKernel update_kernel_for(bool center, int d, int dv) {
   const int w = std::max(d, dv);
@@ -148,8 +148,6 @@ UpdateKrKernel update_kr_kernel_for(bool center, int d) {
   if (d == 16) return center ? sk_update_kr_kernel<1, true> : sk_update_kr_kernel<1, false>;
   return center ? sk_update_kr_kernel<2, true> : sk_update_kr_kernel<2, false>;
 }
-// waves of that kernel resident per SIMD (its register use)
-int update_kr_waves_per_simd() { return 2; }
 // EXPSKETCH_UPDATE_KR=0 keeps the tile kernels for every key width.
 bool use_update_kr() {
   static const bool v = [] {
@@ -211,6 +209,8 @@ struct sk_sketch {
   std::vector<QryTile> qtiles;
   UpdTile* d_utiles = nullptr;
   std::vector<KrUnit> kunits;      // digit-organised update units (d >= 16)
+  std::vector<int> kgroup0;        // their groups (first unit of each, then the count)
+  std::vector<int> kweight;        // work per key of each group's units
   KrUnit* d_kunits = nullptr;
   QryTile* d_qtiles = nullptr;
   long long qpb = 0;        // floats of query partials per (head, query tile)
@@ -354,6 +354,26 @@ bool plan_kr_units(sk_sketch* s) {
       }
     }
   }
+  // groups by work per key (matrix instructions per key, in 32x32x2 units): the
+  // 8-block units 4, a 4-block level-2 unit 2, the level 0/1 units 1 (few matrix
+  // instructions, but each 4-key step waits on its loads); heaviest first, so a
+  // unit's position no longer follows its level
+  auto weight = [&](const KrUnit& x) {
+    if (x.mode == KR_SMALL) return 1;
+    if (x.mode == KR_WIDE) return x.C - 64 * x.ct > 32 ? 4 : 2;
+    return 4;
+  };
+  std::stable_sort(u.begin(), u.end(),
+                   [&](const KrUnit& a, const KrUnit& b) { return weight(a) > weight(b); });
+  s->kgroup0.clear();
+  s->kweight.clear();
+  for (size_t i = 0; i < u.size(); ++i)
+    if (i == 0 || weight(u[i]) != weight(u[i - 1])) {
+      s->kgroup0.push_back((int)i);
+      s->kweight.push_back(weight(u[i]));
+    }
+  s->kgroup0.push_back((int)u.size());
+  if (s->kweight.size() > KR_MAXG) return false;
   s->kunits.swap(u);
   return true;
 }
@@ -602,27 +622,69 @@ int update_tile_count(const sk_sketch* s) {
   return (int)(s->layout == SK_LAYOUT_SYM ? s->sutiles.size() : s->utiles.size());
 }
 
-// Key splits of the digit-organised update: fill the wave slots (each
-// workgroup holds one wave per SIMD) in whole rounds, at least 256 keys a split.
-int choose_kr_splits(const sk_sketch* s, long long n) {
+// Keys per launch of the digit-organised update: byte offsets from a split's
+// first key or value row stay below 2^31 (EXPSKETCH_UPDATE_MAXKEYS lowers it, to
+// test the cut).
+long long kr_max_keys(const sk_sketch* s) {
+  static const long long forced = [] {
+    const char* v = std::getenv("EXPSKETCH_UPDATE_MAXKEYS");
+    return v ? std::max(0LL, std::atoll(v)) : 0LL;
+  }();
+  const long long row = 4LL * std::max(s->d, s->dv);
+  const long long lim = ((1LL << 31) - (1LL << 20)) / row / 1024 * 1024;
+  return forced > 0 ? std::min(forced, lim) : lim;
+}
+
+// Key splits of the digit-organised update for n keys, given the split count of
+// the heaviest group: a lighter group takes proportionally fewer, longer splits.
+KrSplits kr_splits_for(const sk_sketch* s, long long n, long long ns0) {
+  KrSplits P{};
+  P.ngroup = (int)s->kweight.size();
+  P.nsplit = 1;
+  long long items = 0;
+  for (int g = 0; g < P.ngroup; ++g) {
+    const long long want =
+        std::max(1LL, (ns0 * s->kweight[g] + s->kweight[0] - 1) / s->kweight[0]);
+    const long long kps = std::max(1LL, (n + want - 1) / want);
+    const long long ns = std::max(1LL, (n + kps - 1) / kps);
+    P.unit0[g] = s->kgroup0[g];
+    P.ns[g] = (int)ns;
+    P.kps[g] = kps;
+    P.item0[g] = items;
+    items += (long long)(s->kgroup0[g + 1] - s->kgroup0[g]) * ns;
+    P.nsplit = std::max(P.nsplit, (int)ns);
+  }
+  P.unit0[P.ngroup] = s->kgroup0[P.ngroup];
+  P.item0[P.ngroup] = items;
+  return P;
+}
+
+// Splits of the heaviest group: the fewest key-steps on the busiest SIMD (waves
+// per SIMD times the heaviest group's split length), plus a small charge per
+// partial buffer (written, then read by the reduce); at least 256 keys a split.
+KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
   static const int forced = [] {
     const char* v = std::getenv("EXPSKETCH_UPDATE_SPLITS");
     return v ? std::max(0, std::atoi(v)) : 0;
   }();
-  if (forced > 0) return (int)std::max(1LL, std::min<long long>(forced, (n + SK_KB - 1) / SK_KB));
-  const long long items = (long long)s->kunits.size() * s->h;
-  const long long slots = (long long)std::max(1, s->dev.num_cu) * update_kr_waves_per_simd();
+  if (forced > 0) return kr_splits_for(s, n, std::min<long long>(forced, std::max(1LL, n)));
+  const long long simds = (long long)std::max(1, s->dev.num_cu) * 4;
   const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
-  int best = 1;
-  double best_score = -1.0;
+  KrSplits best = kr_splits_for(s, n, 1);
+  double best_cost = -1.0;
   for (long long ns = 1; ns <= max_ns; ++ns) {
-    const long long wgs = (items * ns + KR_WAVES - 1) / KR_WAVES;
-    const long long rounds = (wgs + slots - 1) / slots;
-    const double eff = (double)wgs / (double)(rounds * slots);
-    const double score = eff - 0.005 * (double)ns;
-    if (score > best_score + 1e-9) {
-      best_score = score;
-      best = (int)ns;
+    const KrSplits P = kr_splits_for(s, n, ns);
+    const long long waves = P.item0[P.ngroup] * s->h;
+    const long long per_simd = (waves + simds - 1) / simds;   // they share its matrix core
+    // measured on MI355X: one wave per SIMD runs about 20% slower (no other wave
+    // covers its waits), and exactly two resident waves that all finish together
+    // about 5% slower than three or more, where the workgroups dispatched last fill
+    // the slots that free up first
+    const double shape = per_simd == 1 ? 1.2 : per_simd == 2 ? 1.05 : 1.0;
+    const double cost = (double)per_simd * (double)P.kps[0] * (1.0 + 0.003 * P.nsplit) * shape;
+    if (best_cost < 0.0 || cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = P;
     }
   }
   return best;
@@ -904,15 +966,36 @@ namespace {
 // K + h * hkeys * d), V likewise: one launch (plus the deferred reduce).
 int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long long hkeys) {
   const bool kr = s->layout == SK_LAYOUT_FULL && !s->kunits.empty();
-  const int ns = kr ? choose_kr_splits(s, n) : choose_update_splits(s, n);
-  long long kps = (n + ns - 1) / ns;
-  kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
-  const int nsplit = (int)((n + kps - 1) / kps);
+  if (kr) {
+    // the digit kernel addresses a split's rows with 32-bit byte offsets: longer
+    // calls run as several launches
+    const long long maxkeys = kr_max_keys(s);
+    if (n > maxkeys) {
+      for (long long off = 0; off < n; off += maxkeys) {
+        const int rc = run_update(s, K + off * s->d, V + off * s->dv,
+                                  std::min<long long>(maxkeys, n - off), hkeys);
+        if (rc != SK_OK) return rc;
+      }
+      return SK_OK;
+    }
+  }
+  KrSplits ksp{};
+  long long kps = 0;
+  int nsplit = 1;
+  if (kr) {
+    ksp = choose_kr_splits(s, n);
+    nsplit = ksp.nsplit;
+  } else {
+    const int ns = choose_update_splits(s, n);
+    kps = (n + ns - 1) / ns;
+    kps = (kps + SK_KB - 1) / SK_KB * SK_KB;
+    nsplit = (int)((n + kps - 1) / kps);
+  }
   const bool sym = s->layout == SK_LAYOUT_SYM;
   const int ntiles = update_tile_count(s);
   const long long total = s->XS * s->h;
   const long long rmax = (total / 4 + SK_RED4 - 1) / SK_RED4;     // reduce workgroups
-  const long long kr_wgs = kr ? ((long long)s->kunits.size() * nsplit * s->h + KR_WAVES - 1) / KR_WAVES : 0;
+  const long long kr_wgs = kr ? (ksp.item0[ksp.ngroup] * s->h + KR_WAVES - 1) / KR_WAVES : 0;
   if ((long long)ntiles * nsplit * s->h + rmax > 0x7fffffffLL || kr_wgs + rmax > 0x7fffffffLL)
     return SK_EINVAL;
   const size_t lds = sym ? sym_update_lds_bytes(s->d, s->dv) : update_lds_bytes(s->d, s->dv);
@@ -987,8 +1070,8 @@ int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long lon
   } else if (kr) {
     hipLaunchKernelGGL(update_kr_kernel_for(s->center != nullptr, s->d),
                        dim3((unsigned)(kr_wgs + rwgs)), dim3(64 * KR_WAVES), 0, s->stream, K, V,
-                       (long long)n, hkeys, s->dv, s->d_kunits, (int)s->kunits.size(), kps,
-                       nsplit, s->h, dst, s->XS, sstride, acc, s->center, red);
+                       (long long)n, hkeys, s->dv, s->d_kunits, ksp, s->h, dst, s->XS, sstride,
+                       acc, s->center, red);
     err = hipGetLastError();
   } else {
     hipLaunchKernelGGL(update_kernel_for(s->center != nullptr, s->d, s->dv),

@@ -69,6 +69,23 @@ struct KrUnit {
   int pad_;
 };
 
+// Key splits of one launch.  The units form groups of consecutive units (heavy
+// units first); group g cuts the keys into ns[g] splits of kps[g] keys, so that a
+// unit doing less work per key takes longer key ranges and every wave of the
+// launch has about the same work.  Split s of a unit writes partial buffer s;
+// buffers ns[g] .. nsplit - 1 of a group with fewer splits get zeros in its rows
+// (from the wave of split s' mod ns[g]), so the reduce adds nsplit buffers
+// everywhere.
+#define KR_MAXG 4
+struct KrSplits {
+  int ngroup;
+  int nsplit;                    // partial buffers (the largest ns[g])
+  int unit0[KR_MAXG + 1];        // first unit of each group; unit0[ngroup] = unit count
+  int ns[KR_MAXG];               // splits of each group
+  long long item0[KR_MAXG + 1];  // first item of each group within a head; item0[ngroup] = items
+  long long kps[KR_MAXG];        // keys per split of each group
+};
+
 // src[lane N of this lane's 16-lane row] * y: one v_mul_f32_dpp row_newbcast.
 template <int N>
 __device__ __forceinline__ float kr_bmul(float src, float y) {
@@ -88,17 +105,34 @@ __device__ __forceinline__ float kr_u(const float* __restrict__ krow, const floa
   return c < dv ? vrow[c] : 0.f;
 }
 
+// Key and value components are read with raw buffer loads: a resource at the
+// split's first row (wave-uniform, in scalar registers), the lane's byte offset
+// in a vector register and the step's row offset in a scalar one, so a load
+// costs no per-lane address arithmetic.  Offsets stay below 2^31 (the host cuts
+// longer key ranges into several launches).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kr_rsrc(const float* base) {
+  // raw buffer: stride 0, the largest range, the gfx9 format word of 32-bit data
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+__device__ __forceinline__ float kr_ld(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
 // One unit at levels >= 2 (see the layout above), specialised by mode, number
-// of blocks per b1 pair (NBE) and number of leading digits (NF), so that a key
-// step is straight-line code: loads for a later step, the centring, two row
-// rotations, 4 + NBE fused broadcast multiplies and 4 NBE matrix instructions.
-// Steps past the last full pair of keys (the ring runs in groups of four)
-// re-read that pair's rows with zero A operands, so they add nothing.
-template <int RT, bool CENTER, int MODE, int NBE, int NF>
+// of blocks per b1 pair (NBE), number of leading digits (NF) and whether u is
+// the value row alone (TOP; the pair mode always is), so that a key step is
+// straight-line code: loads for a later step, the centring, two row rotations,
+// 4 + NBE fused broadcast multiplies and 4 NBE matrix instructions.  Columns
+// past the row width hold whatever their (in-bounds) loads give and are never
+// stored: a column of the product depends on its own B column only.  Steps past
+// the last full pair of keys (the ring runs in groups of four, the last group
+// separately) re-read that pair's rows with zero A operands, so they add nothing.
+template <int RT, bool CENTER, int MODE, int NBE, int NF, bool TOP>
 __device__ __forceinline__
 void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restrict__ Vh, int dv,
              long long k_begin, long long k_end, const float* __restrict__ cen,
-             float* __restrict__ o, int accumulate) {
+             float* __restrict__ o, int accumulate, int nzero, long long zstride) {
   constexpr int d = 16 * RT;
   constexpr int LOGD = RT == 1 ? 4 : RT == 2 ? 5 : RT == 4 ? 6 : 7;
   constexpr int NBU = MODE == KR_WIDE ? NBE : 1;     // distinct u operands
@@ -116,40 +150,40 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   const int npair = (int)(nk >> 1);
   const float* Kb = Kh + k_begin * d;
   const float* Vb = Vh + k_begin * dv;
-  // u columns: lane offsets into the key row (lk) and the value row (lv), which
-  // of the two the lane takes, and a mask for columns past the row width
-  int lk[NBU], lv[NBU];
+  // u columns: byte offsets into the key row (lk) and the value row (lv) and
+  // which of the two the lane takes (column 0 for columns past the row width)
+  unsigned lk[NBU], lv[NBU];
   bool usel[NBU];
-  float umask[NBU];
 #pragma unroll
   for (int y = 0; y < NBU; ++y) {
     const int e = MODE == KR_PAIR ? m : MODE == KR_SINGLE ? 32 * U.ct + l32 : 64 * U.ct + 32 * y + l32;
-    const bool fromk = !U.top && e < d;
-    const int col = fromk ? e : (U.top ? e : e - d);
+    const bool fromk = !TOP && e < d;
+    const int col = fromk ? e : (TOP ? e : e - d);
     const bool valid = e < U.C && (fromk || col < dv);
-    lk[y] = khalf * d + (fromk && valid ? col : 0);
-    lv[y] = khalf * dv + (!fromk && valid ? col : 0);
+    lk[y] = 4u * (unsigned)(khalf * d + (fromk && valid ? col : 0));
+    lv[y] = 4u * (unsigned)(khalf * dv + (!fromk && valid ? col : 0));
     usel[y] = fromk;
-    umask[y] = valid ? 1.f : 0.f;
   }
   float cu[NBU];
 #pragma unroll
   for (int y = 0; y < NBU; ++y) {
     const int e = MODE == KR_PAIR ? m : MODE == KR_SINGLE ? 32 * U.ct + l32 : 64 * U.ct + 32 * y + l32;
-    cu[y] = (CENTER && !U.top && e < d) ? cen[e] : 0.f;
+    cu[y] = (CENTER && !TOP && e < d) ? cen[e] : 0.f;
   }
   const int q1 = U.b1 >> 4, q2 = U.b2 >> 4;
-  const int la = khalf * d + 16 * U.rc + m;           // lane offsets of key components
-  const int l1 = khalf * d + 16 * q1 + m;
-  const int l2 = khalf * d + 16 * q2 + m;
+  // byte offsets of the key components
+  const unsigned la = 4u * (unsigned)(khalf * d + 16 * U.rc + m);
+  const unsigned l1 = 4u * (unsigned)(khalf * d + 16 * q1 + m);
+  const unsigned l2 = 4u * (unsigned)(khalf * d + 16 * q2 + m);
   const int src1 = (rowbase + ((m + (U.b1 & 15) + par) & 15)) * 4;
   const int src2 = (rowbase + ((m + (U.b2 & 15) + (MODE == KR_PAIR ? par : 0)) & 15)) * 4;
-  int fdig[NF > 0 ? NF : 1], lf[NF > 0 ? NF : 1];
+  int fdig[NF > 0 ? NF : 1];
+  unsigned lf[NF > 0 ? NF : 1];
   float cf[NF > 0 ? NF : 1];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     fdig[f] = (U.F >> (LOGD * (NF - 1 - f))) & (d - 1);
-    lf[f] = khalf * d + fdig[f];
+    lf[f] = 4u * (unsigned)(khalf * d + fdig[f]);
     cf[f] = CENTER ? cen[fdig[f]] : 0.f;
   }
   const float ca = CENTER ? cen[16 * U.rc + m] : 0.f;
@@ -157,31 +191,41 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   const float c2 = CENTER ? cen[16 * q2 + m] : 0.f;
 
   // prefetch ring (static slots)
-  float ra[KR_SLOTS], r1[KR_SLOTS], r2[KR_SLOTS], ru[KR_SLOTS][NBU], rf[KR_SLOTS][NF > 0 ? NF : 1];
-  // one step's components from the rows at kr (keys) and vr (values)
-  auto load = [&](const float* kr, const float* vr, float& va, float& v1, float& v2,
-                  float (&vu)[NBU], float (&vf)[NF > 0 ? NF : 1]) {
-    va = kr[la];
+  // (below the top level a u column comes from the key or the value row: both are
+  // loaded into the ring and the lane's choice is made when the step uses them,
+  // so that no select waits on a load just issued)
+  constexpr int NUK = TOP ? 1 : NBU;
+  float ra[KR_SLOTS], r1[KR_SLOTS], r2[KR_SLOTS], ru[KR_SLOTS][NBU], rk2[KR_SLOTS][NUK],
+      rf[KR_SLOTS][NF > 0 ? NF : 1];
+  // one step's components from the key row at byte offset sk and the value row
+  // at sv (both relative to the split's first rows), lane offsets less adjk/adjv
+  const __amdgpu_buffer_rsrc_t rk = kr_rsrc(Kb), rv = kr_rsrc(Vb);
+  auto load = [&](unsigned sk, unsigned sv, unsigned adjk, unsigned adjv, float& va, float& v1,
+                  float& v2, float (&vu)[NBU], float (&vk)[NUK], float (&vf)[NF > 0 ? NF : 1]) {
+    va = kr_ld(rk, la - adjk, sk);
     if (RT > 1) {
-      v1 = kr[l1];
-      if (MODE != KR_WIDE) v2 = kr[l2];
+      v1 = kr_ld(rk, l1 - adjk, sk);
+      if (MODE != KR_WIDE) v2 = kr_ld(rk, l2 - adjk, sk);
     }
 #pragma unroll
     for (int y = 0; y < NBU; ++y) {
-      if constexpr (MODE == KR_PAIR) vu[y] = vr[lv[y]];   // the top level: u = v
-      else vu[y] = usel[y] ? kr[lk[y]] : vr[lv[y]];
+      vu[y] = kr_ld(rv, lv[y] - adjv, sv);        // the top level: u = v
+      if constexpr (!TOP) vk[y] = kr_ld(rk, lk[y] - adjk, sk);
     }
 #pragma unroll
-    for (int f = 0; f < NF; ++f) vf[f] = kr[lf[f]];
+    for (int f = 0; f < NF; ++f) vf[f] = kr_ld(rk, lf[f] - adjk, sk);
   };
-  auto fetch = [&](int st, int sl) {      // unconditional: no merge of old and new slots
-    const int lastp = npair > 0 ? 2 * (npair - 1) : 0;
-    const int off = 2 * st < lastp ? 2 * st : lastp;       // uniform
-    load(Kb + (long long)off * d, Vb + (long long)off * dv, ra[sl], r1[sl], r2[sl], ru[sl], rf[sl]);
+  // unconditional (no merge of old and new slots); CLAMP re-reads the last full
+  // pair for steps past it, else the step must lie before it
+  const int lastp = npair > 0 ? 2 * (npair - 1) : 0;
+  auto fetch = [&](int st, int sl, auto clamp_c) {
+    const int off = !decltype(clamp_c)::value || 2 * st < lastp ? 2 * st : lastp;   // uniform
+    load((unsigned)off * (4u * d), (unsigned)off * (4u * dv), 0u, 0u, ra[sl], r1[sl], r2[sl],
+         ru[sl], rk2[sl], rf[sl]);
   };
   if (npair > 0) {
 #pragma unroll
-    for (int s = 0; s < KR_PF; ++s) fetch(s, s);
+    for (int s = 0; s < KR_PF; ++s) fetch(s, s, std::true_type{});
   }
 
   floatx16 acc[KR_NA][NBE];
@@ -228,9 +272,9 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     float B[NBE];
     if constexpr (MODE == KR_WIDE) {
 #pragma unroll
-      for (int y = 0; y < NBE; ++y) B[y] = u[y] * umask[y];
+      for (int y = 0; y < NBE; ++y) B[y] = u[y];
     } else {
-      const float pu = u[0] * umask[0] * p;
+      const float pu = NF > 0 ? u[0] * p : u[0];
       if constexpr (MODE == KR_PAIR) {
         B[0] = kr_bmul<0>(x2, pu);
         B[1] = kr_bmul<2>(x2, pu);
@@ -249,12 +293,13 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   float xr1 = 0.f, xr2 = 0.f;
   if (npair > 0) rotate(ra[0], r1[0], r2[0], xr1, xr2);
 
-  auto step = [&](int st, auto slot_c) {
+  auto step = [&](int st, auto slot_c, auto tail_c) {
     constexpr int SL = decltype(slot_c)::value;
+    constexpr bool TAIL = decltype(tail_c)::value;     // a step of the last groups
     float u[NBU], fv[NF > 0 ? NF : 1];
     const float a0v = ra[SL];
 #pragma unroll
-    for (int y = 0; y < NBU; ++y) u[y] = ru[SL][y];
+    for (int y = 0; y < NBU; ++y) u[y] = TOP || !usel[y] ? ru[SL][y] : rk2[SL][TOP ? 0 : y];
 #pragma unroll
     for (int f = 0; f < NF; ++f) fv[f] = rf[SL][f];
     const float x1 = xr1, x2 = xr2;
@@ -262,28 +307,46 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     // here, ahead of this step's work (the scheduler would otherwise sink them
     // next to their use)
     __builtin_amdgcn_sched_barrier(0);
-    fetch(st + KR_PF, (SL + KR_PF) % KR_SLOTS);
+    fetch(st + KR_PF, (SL + KR_PF) % KR_SLOTS, tail_c);
     constexpr int SN = (SL + 1) % KR_SLOTS;
     rotate(ra[SN], r1[SN], r2[SN], xr1, xr2);
     __builtin_amdgcn_sched_barrier(0);
     auto ap = compute(a0v, u, fv, x1, x2);
-    const float a = st < npair ? ap.first : 0.f;     // uniform: steps past the pairs add nothing
+    // uniform: steps past the pairs (last groups only) add nothing
+    const float a = !TAIL || st < npair ? ap.first : 0.f;
     mma(a, ap.second, u, x1, x2);
   };
   static_assert(KR_PF == 3 && KR_SLOTS == 4 && KR_NA == 4, "the step is written for these sizes");
   // whole groups of KR_SLOTS steps with no branches inside (a merge of ring slots
-  // would make the compiler wait for loads just issued)
-  for (int st0 = 0; st0 < npair; st0 += KR_SLOTS) {
-    step(st0, std::integral_constant<int, 0>{});
-    step(st0 + 1, std::integral_constant<int, 1>{});
-    step(st0 + 2, std::integral_constant<int, 2>{});
-    step(st0 + 3, std::integral_constant<int, 3>{});
+  // would make the compiler wait for loads just issued): first the groups whose
+  // steps and fetches all lie before the last pair, then (at most two) groups that
+  // clamp their fetches and zero the A operands of steps past the pairs
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  int st0 = 0;
+  for (; st0 + KR_SLOTS + KR_PF <= npair; st0 += KR_SLOTS) {
+    step(st0, S0{}, std::false_type{});
+    step(st0 + 1, S1{}, std::false_type{});
+    step(st0 + 2, S2{}, std::false_type{});
+    step(st0 + 3, S3{}, std::false_type{});
+  }
+  for (; st0 < npair; st0 += KR_SLOTS) {
+    step(st0, S0{}, std::true_type{});
+    step(st0 + 1, S1{}, std::true_type{});
+    step(st0 + 2, S2{}, std::true_type{});
+    step(st0 + 3, S3{}, std::true_type{});
   }
   if (nk & 1) {
     // the lone last key: both lane halves read its row, the second half adds nothing
     const long long lastk = nk - 1;
-    float va = 0.f, v1 = 0.f, v2 = 0.f, u[NBU], fv[NF > 0 ? NF : 1];
-    load(Kb + lastk * d - khalf * d, Vb + lastk * dv - khalf * dv, va, v1, v2, u, fv);
+    float va = 0.f, v1 = 0.f, v2 = 0.f, u[NBU], uk[NUK], fv[NF > 0 ? NF : 1];
+    load((unsigned)lastk * (4u * d), (unsigned)lastk * (4u * dv), (unsigned)khalf * (4u * d),
+         (unsigned)khalf * (4u * dv), va, v1, v2, u, uk, fv);
+#pragma unroll
+    for (int y = 0; y < NBU; ++y)
+      if (!TOP && usel[y]) u[y] = uk[TOP ? 0 : y];
     float x1, x2;
     rotate(va, v1, v2, x1, x2);
     auto ap = compute(va, u, fv, x1, x2);
@@ -316,19 +379,34 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
         *dst = accumulate ? *dst + acc[x][y][r] : acc[x][y][r];
       }
   }
+  // zeros into the unit's rows of the partial buffers its group does not reach
+  // (a plain loop over the same positions: only the lighter groups have any)
+#pragma unroll 1
+  for (int i = 0; i < nzero * NBE * KR_NA * 16; ++i) {
+    const int r = i & 15, x = (i >> 4) % KR_NA, y = (i >> 4) / KR_NA % NBE;
+    const int z = 1 + (i >> 4) / (KR_NA * NBE);
+    int e, b2;
+    if (MODE == KR_PAIR) { e = m; b2 = U.b2 + 2 * y + par; }
+    else if (MODE == KR_SINGLE) { e = 32 * U.ct + l32; b2 = U.b2 + y; }
+    else { e = 64 * U.ct + 32 * y + l32; b2 = 0; }
+    const long long hi = MODE == KR_WIDE ? 0 : (long long)U.F * d + b2;
+    const int row = 8 * (r >> 2) + 4 * khalf + (r & 3);
+    const long long a = (hi * d + U.b1 + 2 * x + (row >> 4)) * d + 16 * U.rc + (row & 15);
+    if (e < U.C) o[z * zstride + a * U.C + e] = 0.f;
+  }
 }
 
 template <int RT, bool CENTER>
 __global__ __launch_bounds__(64 * KR_WAVES, 2)
 void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ V,
                          long long n, long long hkeys, int dv,
-                         const KrUnit* __restrict__ units, int nunits,
-                         long long keys_per_split, int nsplit, int nhead,
+                         const KrUnit* __restrict__ units, KrSplits P, int nhead,
                          float* __restrict__ out, long long head_stride,
                          long long split_stride, int accumulate,
                          const float* __restrict__ center, PendingReduce red) {
   constexpr int d = 16 * RT;
-  const long long nitems = (long long)nunits * nsplit * nhead;
+  const long long per_head = P.item0[P.ngroup];
+  const long long nitems = per_head * nhead;
   const long long nwg = (nitems + KR_WAVES - 1) / KR_WAVES;
   if ((long long)blockIdx.x >= nwg) {
     pending_reduce_wg(red, (long long)blockIdx.x - nwg);
@@ -337,17 +415,35 @@ void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // workgroups of one XCD take a contiguous range of items: the items of one key
-  // split (all units) read the same key rows from that XCD's L2
+  // split (all units of a group) read the same key rows from that XCD's L2
   const long long item = xcd_remap(blockIdx.x, nwg) * KR_WAVES + wave;
   if (item >= nitems) return;
-  const int unit_id = (int)(item % nunits);
-  const long long split = (item / nunits) % nsplit;
-  const long long head = item / ((long long)nunits * nsplit);
+  const long long head = item / per_head;
+  const long long li = item - head * per_head;
+  // the item's group (scalar selects: no dynamic index into the argument block)
+  long long gbase = P.item0[0], kps = P.kps[0];
+  int u0 = P.unit0[0], gn = P.unit0[1] - P.unit0[0], gns = P.ns[0];
+#pragma unroll
+  for (int g = 1; g < KR_MAXG; ++g)
+    if (g < P.ngroup && li >= P.item0[g]) {
+      gbase = P.item0[g];
+      kps = P.kps[g];
+      u0 = P.unit0[g];
+      gn = P.unit0[g + 1] - P.unit0[g];
+      gns = P.ns[g];
+    }
+  const long long gi = li - gbase;
+  const int unit_id = u0 + (int)(gi % gn);
+  const long long split = gi / gn;
   const KrUnit U = units[unit_id];
+  // partial buffers split + gns, split + 2 gns, ... below nsplit get zeros here
+  const int nzero = accumulate ? 0 : (int)((P.nsplit - 1 - split) / gns);
+  const long long zstride = (long long)gns * split_stride;
 
-  const long long k_begin = split * keys_per_split;
-  long long k_end = k_begin + keys_per_split;
+  const long long k_begin = split * kps;
+  long long k_end = k_begin + kps;
   if (k_end > n) k_end = n;
+  if (k_end < k_begin) k_end = k_begin;
   const float* Kh = K + head * hkeys * d;
   const float* Vh = V + head * hkeys * dv;
   const float* cen = CENTER ? center + head * d : nullptr;
@@ -409,6 +505,7 @@ void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ 
         if (keep) {
           float* dst = o + (long long)c * U.C + e;
           *dst = accumulate ? *dst + acc[r][q] : acc[r][q];
+          for (int z = 1; z <= nzero; ++z) dst[z * zstride] = 0.f;
         }
       }
     return;
@@ -418,26 +515,30 @@ void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ 
   // number of blocks and number of leading digits
   const int nbe = U.mode == KR_WIDE ? (U.C - 64 * U.ct > 32 ? 2 : 1) : KR_NB;
   const int nf = U.mode == KR_WIDE ? 0 : U.j - 3;
-#define KR_CALL(MODE, NBE, NF)                                                              \
-  kr_body<RT, CENTER, MODE, NBE, NF>(U, Kh, Vh, dv, k_begin, k_end, cen, o, accumulate)
-  if (U.mode == KR_WIDE) {
-    if (nbe == 2) KR_CALL(KR_WIDE, 2, 0); else KR_CALL(KR_WIDE, 1, 0);
-  } else if (U.mode == KR_PAIR) {
-    switch (nf) {
-      case 0: KR_CALL(KR_PAIR, 2, 0); break;
-      case 1: KR_CALL(KR_PAIR, 2, 1); break;
-      case 2: KR_CALL(KR_PAIR, 2, 2); break;
-      case 3: KR_CALL(KR_PAIR, 2, 3); break;
-      default: KR_CALL(KR_PAIR, 2, 4); break;
-    }
-  } else {
-    switch (nf) {
-      case 0: KR_CALL(KR_SINGLE, 2, 0); break;
-      case 1: KR_CALL(KR_SINGLE, 2, 1); break;
-      case 2: KR_CALL(KR_SINGLE, 2, 2); break;
-      case 3: KR_CALL(KR_SINGLE, 2, 3); break;
-      default: KR_CALL(KR_SINGLE, 2, 4); break;
-    }
+#define KR_CALL(MODE, NBE, NF, TOP)                                                         \
+  kr_body<RT, CENTER, MODE, NBE, NF, TOP>(U, Kh, Vh, dv, k_begin, k_end, cen, o, accumulate, \
+                                          nzero, zstride)
+#define KR_NF(MODE, TOP)                          \
+  switch (nf) {                                   \
+    case 0: KR_CALL(MODE, 2, 0, TOP); break;      \
+    case 1: KR_CALL(MODE, 2, 1, TOP); break;      \
+    case 2: KR_CALL(MODE, 2, 2, TOP); break;      \
+    case 3: KR_CALL(MODE, 2, 3, TOP); break;      \
+    default: KR_CALL(MODE, 2, 4, TOP); break;     \
   }
+  if (U.mode == KR_WIDE) {
+    if (U.top) {
+      if (nbe == 2) KR_CALL(KR_WIDE, 2, 0, true); else KR_CALL(KR_WIDE, 1, 0, true);
+    } else {
+      if (nbe == 2) KR_CALL(KR_WIDE, 2, 0, false); else KR_CALL(KR_WIDE, 1, 0, false);
+    }
+  } else if (U.mode == KR_PAIR) {
+    KR_NF(KR_PAIR, true)                  // C <= 16 < d + dv: only the top level
+  } else if (U.top) {
+    KR_NF(KR_SINGLE, true)
+  } else {
+    KR_NF(KR_SINGLE, false)
+  }
+#undef KR_NF
 #undef KR_CALL
 }

@@ -2,7 +2,8 @@
 kernel runs by default and the tile kernel only with EXPSKETCH_UPDATE_KR=0, a
 setting read once per process, so the tile kernel runs in one child process on
 the same seeded inputs and both are checked against the float64 oracle and each
-other."""
+other.  Likewise the digit kernel's cut of long calls into several launches
+(EXPSKETCH_UPDATE_MAXKEYS lowers the cut to a few hundred keys)."""
 
 import os
 import subprocess
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# child: same workloads with the tile kernel; writes <outdir>/tiles_<key>.npz
+# child: same workloads under the environment it is given; writes <outdir>/<tag>_<key>.npz
 _CHILD = r"""
 import os, sys
 import numpy as np
@@ -32,26 +33,28 @@ from exp_density_sketching_amd.workload import run_sketch
 from synthetic import generate
 from tests.gpu_util import gpu, host
 from tests.test_gpu_parity import _small
-for key in sys.argv[3:]:
+for key in sys.argv[4:]:
     w = _small(int(key))
     K, V, Q = generate(w)
     out, Z, sk = run_sketch(w, *gpu(K, V, Q))
     S, out, Z = host(E.sketch_export(sk), out, Z)
-    np.savez(os.path.join(sys.argv[2], "tiles_%s.npz" % key), S=S, out=out, Z=Z,
+    np.savez(os.path.join(sys.argv[2], "%s_%s.npz" % (sys.argv[3], key)), S=S, out=out, Z=Z,
              path=np.array(E.sketch_update_path(sk)))
     print("child: workload", key, "done", flush=True)
     sk.destroy()
 """
 
 
-def test_tile_and_digit_kernels_agree(tmp_path):
-    keys = [2, 3]                       # d = 16 (p = 4) and d = 32 (p = 3)
-    env = dict(os.environ, EXPSKETCH_UPDATE_KR="0")
-    say("child process: tile kernel on workloads 2 and 3 (small sizes)")
-    res = subprocess.run([sys.executable, "-u", "-c", _CHILD, ROOT, str(tmp_path)] +
+def _child(tmp_path, tag, keys, **env):
+    say(f"child process ({tag}, {env}): workloads {keys} (small sizes)")
+    res = subprocess.run([sys.executable, "-u", "-c", _CHILD, ROOT, str(tmp_path), tag] +
                          [str(k) for k in keys],
-                         env=env, cwd=ROOT, capture_output=True, text=True, timeout=180)
+                         env=dict(os.environ, **env), cwd=ROOT, capture_output=True, text=True,
+                         timeout=180)
     assert res.returncode == 0, res.stderr[-2000:]
+
+
+def _compare(tmp_path, tag, keys, path):
     for key in keys:
         w = _small(key)
         K, V, Q = generate(w)
@@ -59,14 +62,28 @@ def test_tile_and_digit_kernels_agree(tmp_path):
         assert E.sketch_update_path(sk) == "digits"
         S_d, out_d, Z_d = host(E.sketch_export(sk), out_d, Z_d)
         sk.destroy()
-        c = np.load(tmp_path / f"tiles_{key}.npz")
-        assert str(c["path"]) == "tiles"
+        c = np.load(tmp_path / f"{tag}_{key}.npz")
+        assert str(c["path"]) == path
         S_t, out_t, Z_t = c["S"], c["out"], c["Z"]
         # the moments agree to fp32 summation order
         diff = np.abs(S_t - S_d).max() / np.abs(S_d).max()
-        say(f"workload {key}: tile vs digit state max rel diff {diff:.2e}")
+        say(f"workload {key}: {tag} vs default state max rel diff {diff:.2e}")
         assert diff <= 1e-5
         for hd in range(w.h):
             o_ref, z_ref = oracle.sketch_direct(K[hd], V[hd], Q[hd], w.p)
             for o, z in ((out_d[hd], Z_d[hd]), (out_t[hd], Z_t[hd])):
                 assert zrel(z, z_ref) <= SK_Z_REL and oabs(o, o_ref) <= SK_O_ABS
+
+
+def test_tile_and_digit_kernels_agree(tmp_path):
+    keys = [2, 3]                       # d = 16 (p = 4) and d = 32 (p = 3)
+    _child(tmp_path, "tiles", keys, EXPSKETCH_UPDATE_KR="0")
+    _compare(tmp_path, "tiles", keys, "tiles")
+
+
+def test_digit_kernel_long_call_cut(tmp_path):
+    # the small cases stream 4096-key calls through staging; with a 300-key cut
+    # every flush runs as several launches, the last one ragged and odd
+    keys = [2, 3]
+    _child(tmp_path, "cut", keys, EXPSKETCH_UPDATE_MAXKEYS="300")
+    _compare(tmp_path, "cut", keys, "digits")
