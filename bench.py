@@ -43,8 +43,8 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h"],
-    "sk_update_kr_kernel": ["sk_update_kr.h", "sk_common.h", "sk_elementwise.h"],
+    "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h", "sk_reduce.h"],
+    "sk_update_kr_kernel": ["sk_update_kr.h", "sk_update_kr.hip", "sk_common.h", "sk_reduce.h"],
     "sk_exact_decode": ["sk_exact.h", "sk_common.h"],
 }
 

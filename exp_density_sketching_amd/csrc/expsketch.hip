@@ -21,6 +21,17 @@
 #include "sk_update.h"
 #include "sk_update_kr.h"
 
+// the digit kernel's instantiations live in their own objects (sk_update_kr.hip)
+#define KR_EXTERN(RT, CENTER)                                                                  \
+  extern template __global__ void sk_update_kr_kernel<RT, CENTER>(                             \
+      const float*, const float*, long long, long long, int, const KrUnit*, KrSplits, int,     \
+      float*, long long, long long, int, const float*, PendingReduce);
+KR_EXTERN(1, false)
+KR_EXTERN(1, true)
+KR_EXTERN(2, false)
+KR_EXTERN(2, true)
+#undef KR_EXTERN
+
 namespace {
 
 #define SK_TRY(expr)                               \

@@ -35,7 +35,7 @@
 #pragma once
 
 #include "sk_common.h"
-#include "sk_elementwise.h"
+#include "sk_reduce.h"
 
 #include <type_traits>
 #include <utility>
