@@ -49,6 +49,15 @@ KERNEL_SOURCES = {
 }
 
 
+def exact_batched_kernel(w):
+    """The library's choice of batched exact kernel for this shape (m > 8)."""
+    if max(w.d, w.dv) < 16:
+        return "sk_exact_tiled (VALU)"
+    if w.dv == 16 and 16 <= w.d <= 64 and os.environ.get("EXPSKETCH_EXACT_MFMA16", "1") != "0":
+        return "sk_exact_mfma16"
+    return "sk_exact_mfma"
+
+
 def source_hash(kernel):
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -373,8 +382,7 @@ def main():
                           "TFLOPs": 2.0 * w.h * w.m * w.n * (w.d + w.dv) / t_ex / 1e12,
                           "mfma_frac": 2.0 * w.h * w.m * w.n * (w.d + w.dv) / t_ex /
                           PEAK_FP32_MFMA,
-                          "kernel": "sk_exact_mfma" if max(w.d, w.dv) >= 16 else
-                          "sk_exact_tiled (VALU)"},
+                          "kernel": exact_batched_kernel(w)},
         "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
                          "kv_bytes": kv_bytes,
                          "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},

@@ -159,6 +159,14 @@ UpdateKrKernel update_kr_kernel_for(bool center, int d) {
   if (d == 16) return center ? sk_update_kr_kernel<1, true> : sk_update_kr_kernel<1, false>;
   return center ? sk_update_kr_kernel<2, true> : sk_update_kr_kernel<2, false>;
 }
+// EXPSKETCH_EXACT_MFMA16=0 keeps the 32x32 batched exact kernel at dv = 16.
+bool use_exact_mfma16() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_EXACT_MFMA16");
+    return e == nullptr || std::atoi(e) != 0;
+  }();
+  return v;
+}
 // EXPSKETCH_UPDATE_KR=0 keeps the tile kernels for every key width.
 bool use_update_kr() {
   static const bool v = [] {
@@ -1447,7 +1455,8 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     const long long ns_fill = std::min(((long long)di.num_cu + hq - 1) / hq, (nn + 511) / 512);
     ns = std::max(ns_long, ns_fill);
   } else {
-    const long long lk = min_keys_env > 0 ? min_keys_env : 512;
+    // (measured: 1024-key slices for the 16x16x4 kernel at dv = 16, 512 otherwise)
+    const long long lk = min_keys_env > 0 ? min_keys_env : (dv == 16 && d >= 16 && d <= 64 ? 1024 : 512);
     ns = std::min((8LL * di.num_cu + hq - 1) / hq, ((long long)n + lk - 1) / lk);
   }
   ns = std::max(1LL, ns);
@@ -1506,14 +1515,30 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     case 2: SK_XM(DD, 2); break;      \
     default: SK_XM(DD, 4); break;     \
   }
-    switch (d) {
-      case 4: SK_XM_D(4); break;
-      case 8: SK_XM_D(8); break;
-      case 16: SK_XM_D(16); break;
-      case 32: SK_XM_D(32); break;
-      case 64: SK_XM_D(64); break;
-      default: SK_XM_D(128); break;
+    // 16 value columns: the 16x16x4 kernel (no padding of the value columns)
+    // (its buffer loads address a slice with 32-bit byte offsets)
+    const bool mfma16 = dv == 16 && d >= 16 && d <= 64 && use_exact_mfma16() &&
+                        kps * 4LL * std::max(d, dv) < (1LL << 31) - (1LL << 16);
+#define SK_XM16(DD)                                                                      \
+  hipLaunchKernelGGL((sk_exact_mfma16<DD, 16>), grid, blk, 0, st, K, V, nn, Q, mm, kps, \
+                     nsplit, parts)
+    if (mfma16) {
+      switch (d) {
+        case 16: SK_XM16(16); break;
+        case 32: SK_XM16(32); break;
+        default: SK_XM16(64); break;
+      }
+    } else {
+      switch (d) {
+        case 4: SK_XM_D(4); break;
+        case 8: SK_XM_D(8); break;
+        case 16: SK_XM_D(16); break;
+        case 32: SK_XM_D(32); break;
+        case 64: SK_XM_D(64); break;
+        default: SK_XM_D(128); break;
+      }
     }
+#undef SK_XM16
 #undef SK_XM_D
 #undef SK_XM
   }

@@ -26,6 +26,19 @@ __device__ __forceinline__ floatx4v mfma16x16x4(float a, float b, floatx4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer loads: a resource for a wave-uniform base (scalar registers), a
+// byte offset per lane in a vector register and a wave-uniform byte offset in a
+// scalar register; no per-lane 64-bit address arithmetic.  Callers keep every
+// offset in bounds (the resource's range is only an upper limit).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const float* base) {
+  // raw buffer: stride 0, the largest range, the gfx9 format word of 32-bit data
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+__device__ __forceinline__ float sk_ld(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }

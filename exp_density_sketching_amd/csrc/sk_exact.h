@@ -22,6 +22,8 @@
 
 #include "sk_common.h"
 
+#include <type_traits>
+
 #ifndef SK_EX_U
 #define SK_EX_U 8          // keys per group in flight per step (decode)
 #endif
@@ -152,6 +154,202 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
         const int c = 32 * cb + acc_row(r, lane);
         if (c < dv) P[2 + c] = acc[cb][r];
       }
+  }
+}
+
+// sk_exact_mfma16 (many queries per head, value width a multiple of 16 that is
+// not one of 32): the same online softmax with v_mfma_f32_16x16x4_f32 for both
+// products, so 16 value columns fill the instruction (the 32x32 form pads them
+// to 32).  One workgroup = 4 waves x 32 queries (two 16-query blocks per wave),
+// one key slice; per stage of 32 keys (two 16-key blocks) each wave loads its
+// operands straight from memory into registers, one stage ahead (buffer loads:
+// fixed lane offsets, the stage's offset in a scalar register; the rows of a
+// stage are shared by the workgroup's waves through L1/L2): no LDS, no barrier.
+//   S^T block (16 keys x 16 queries): D/4 instructions, A = key rows, B = the
+//       query components (registers); lane l, register r holds S[key 4 (l/16) +
+//       r][query l % 16]
+//   softmax in base 2 (queries prescaled by log2 e, p = 2^{s - ref}) against a
+//       reference ref per query that is raised, and the sums rescaled by
+//       2^{ref_old - ref}, only when a stage maximum exceeds it by more than
+//       SK_XTAU (p <= 2^SK_XTAU otherwise); the decision is per wave, so the
+//       rescale is a branch the whole wave takes or skips.  A stage maximum is
+//       the largest of the lane's 8 entries and of its 4 lane groups.
+//   O^T block (16 value columns x 16 queries): per key block 4 instructions,
+//       instruction r taking keys 4 k + r (k = lane / 16) with B = P straight
+//       from S's register r and A = those keys' value rows.
+// The partial record is the one of sk_exact_decode (mu = ref in natural-log units).
+#define SK_XTAU 8.f
+template <int D, int DV>
+__global__ __launch_bounds__(256)
+void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
+                     long long n, const float* __restrict__ Q, long long m,
+                     long long keys_per_split, int nsplit, float* __restrict__ parts) {
+  static_assert(D % 16 == 0 && DV % 16 == 0, "widths in blocks of 16");
+  constexpr int NKK = D / 4;                // k-steps of the first product
+  constexpr int NCB = DV / 16;              // value column blocks
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float LN2 = 0.6931471805599453f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const long long split = blockIdx.x % nsplit;
+  const long long qt = blockIdx.x / nsplit;
+  const long long head = blockIdx.y;
+  const long long k_begin = split * keys_per_split;
+  long long k_end = k_begin + keys_per_split;
+  if (k_end > n) k_end = n;
+  const int nkeys = (int)(k_end > k_begin ? k_end - k_begin : 0);   // < 2^31 / (4 max(D, DV))
+
+  // B operands of the first product: Q[query][4 kk + g] * log2 e
+  float qop[2][NKK];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const long long q = qt * SK_XQ + wave * 32 + qb * 16 + i16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qop[qb][kk] = q < m ? Q[(head * m + q) * D + 4 * kk + g] * LOG2E : 0.f;
+  }
+
+  // resources at the slice's first key and value rows
+  const __amdgpu_buffer_rsrc_t rk = sk_rsrc(K + (head * n + k_begin) * D);
+  const __amdgpu_buffer_rsrc_t rv = sk_rsrc(V + (head * n + k_begin) * DV);
+  // operands of one stage: key rows (A of the first product) and value rows (A of
+  // the second); in the last, partial stage rows past the slice are clamped to
+  // its last row (their p is 0)
+  float kop[2][2][NKK], vop[2][2][4][NCB];
+  auto fetch = [&](int kb0, int buf, auto part_c) {   // kb0: the stage's first key in the slice
+    constexpr bool part = decltype(part_c)::value;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int krow = 16 * kb + i16;
+      int vrow[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vrow[r] = 16 * kb + 4 * g + r;
+      if constexpr (part) {
+        const int last = nkeys - 1 - kb0;
+        krow = krow < last ? krow : last;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vrow[r] = vrow[r] < last ? vrow[r] : last;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kop[buf][kb][kk] = sk_ld(rk, 4u * (unsigned)(krow * D + 4 * kk + g), 4u * (unsigned)kb0 * D);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          vop[buf][kb][r][cb] =
+              sk_ld(rv, 4u * (unsigned)(vrow[r] * DV + 16 * cb + i16), 4u * (unsigned)kb0 * DV);
+    }
+  };
+
+  float ref[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  floatx4v acc[2][NCB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = floatx4v{0.f, 0.f, 0.f, 0.f};
+
+  auto stage = [&](int kb0, int buf, auto part_c) {
+    constexpr bool part = decltype(part_c)::value;
+    const int nk = nkeys - kb0 < SK_XK ? nkeys - kb0 : SK_XK;
+    floatx4v sc[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[qb][kb] = floatx4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          sc[qb][kb] = mfma16x16x4(kop[buf][kb][kk], qop[qb][kk], sc[qb][kb]);
+      }
+    if constexpr (part) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + 4 * g + r >= nk) sc[qb][kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[qb][kb][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      if (__any(mloc > ref[qb] + SK_XTAU)) {   // also the first stage (ref = -inf)
+        const float rnew = fmaxf(ref[qb], mloc);   // finite: every stage has a key
+        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - rnew);   // 0 the first time
+        l[qb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] *= alpha;
+        ref[qb] = rnew;
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(sc[qb][kb][r] - ref[qb]);
+          sc[qb][kb][r] = pv;
+          lsum += pv;
+        }
+      l[qb] += lsum;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[qb][cb] = mfma16x16x4(vop[buf][kb][r][cb], sc[qb][kb][r], acc[qb][cb]);
+    }
+  };
+
+  // full stages in pairs (static buffer indices), each fetching the next one
+  // ahead; the last, partial stage (if any) clamps its rows and masks its keys
+  using Full = std::false_type;
+  using Part = std::true_type;
+  const int nfull = nkeys / SK_XK;
+  const bool tail = nkeys % SK_XK != 0;
+  if (nfull > 0) fetch(0, 0, Full{});
+  else if (tail) fetch(0, 0, Part{});
+  int st = 0;
+  for (; st + 2 <= nfull; st += 2) {
+    fetch((st + 1) * SK_XK, 1, Full{});
+    stage(st * SK_XK, 0, Full{});
+    if (st + 2 < nfull) fetch((st + 2) * SK_XK, 0, Full{});
+    else if (tail) fetch((st + 2) * SK_XK, 0, Part{});
+    stage((st + 1) * SK_XK, 1, Full{});
+  }
+  if (st < nfull) {                         // one full stage left, in buffer 0
+    if (tail) fetch((st + 1) * SK_XK, 1, Part{});
+    stage(st * SK_XK, 0, Full{});
+    if (tail) stage((st + 1) * SK_XK, 1, Part{});
+  } else if (tail) {
+    stage(st * SK_XK, 0, Part{});
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = l[qb] + __shfl_xor(l[qb], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const long long q = qt * SK_XQ + wave * 32 + qb * 16 + i16;
+    if (q < m) {
+      float* P = parts + ((head * m + q) * nsplit + split) * (2 + DV);
+      if (g == 0) {
+        P[0] = ref[qb] * LN2;
+        P[1] = lt;
+      }
+      // acc[qb][cb][r] = sum_i p_i v_i[c], c = 16 cb + 4 g + r
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[2 + 16 * cb + 4 * g + r] = acc[qb][cb][r];
+    }
   }
 }
 

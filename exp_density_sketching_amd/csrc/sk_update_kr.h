@@ -105,19 +105,11 @@ __device__ __forceinline__ float kr_u(const float* __restrict__ krow, const floa
   return c < dv ? vrow[c] : 0.f;
 }
 
-// Key and value components are read with raw buffer loads: a resource at the
-// split's first row (wave-uniform, in scalar registers), the lane's byte offset
-// in a vector register and the step's row offset in a scalar one, so a load
-// costs no per-lane address arithmetic.  Offsets stay below 2^31 (the host cuts
-// longer key ranges into several launches).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t kr_rsrc(const float* base) {
-  // raw buffer: stride 0, the largest range, the gfx9 format word of 32-bit data
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff,
-                                           0x00020000);
-}
-__device__ __forceinline__ float kr_ld(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
-}
+// Key and value components are read with raw buffer loads (sk_rsrc / sk_ld): a
+// resource at the split's first row, the lane's byte offset in a vector register
+// and the step's row offset in a scalar one, so a load costs no per-lane address
+// arithmetic.  Offsets stay below 2^31 (the host cuts longer key ranges into
+// several launches).
 
 // One unit at levels >= 2 (see the layout above), specialised by mode, number
 // of blocks per b1 pair (NBE), number of leading digits (NF) and whether u is
@@ -199,21 +191,21 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
       rf[KR_SLOTS][NF > 0 ? NF : 1];
   // one step's components from the key row at byte offset sk and the value row
   // at sv (both relative to the split's first rows), lane offsets less adjk/adjv
-  const __amdgpu_buffer_rsrc_t rk = kr_rsrc(Kb), rv = kr_rsrc(Vb);
+  const __amdgpu_buffer_rsrc_t rk = sk_rsrc(Kb), rv = sk_rsrc(Vb);
   auto load = [&](unsigned sk, unsigned sv, unsigned adjk, unsigned adjv, float& va, float& v1,
                   float& v2, float (&vu)[NBU], float (&vk)[NUK], float (&vf)[NF > 0 ? NF : 1]) {
-    va = kr_ld(rk, la - adjk, sk);
+    va = sk_ld(rk, la - adjk, sk);
     if (RT > 1) {
-      v1 = kr_ld(rk, l1 - adjk, sk);
-      if (MODE != KR_WIDE) v2 = kr_ld(rk, l2 - adjk, sk);
+      v1 = sk_ld(rk, l1 - adjk, sk);
+      if (MODE != KR_WIDE) v2 = sk_ld(rk, l2 - adjk, sk);
     }
 #pragma unroll
     for (int y = 0; y < NBU; ++y) {
-      vu[y] = kr_ld(rv, lv[y] - adjv, sv);        // the top level: u = v
-      if constexpr (!TOP) vk[y] = kr_ld(rk, lk[y] - adjk, sk);
+      vu[y] = sk_ld(rv, lv[y] - adjv, sv);        // the top level: u = v
+      if constexpr (!TOP) vk[y] = sk_ld(rk, lk[y] - adjk, sk);
     }
 #pragma unroll
-    for (int f = 0; f < NF; ++f) vf[f] = kr_ld(rk, lf[f] - adjk, sk);
+    for (int f = 0; f < NF; ++f) vf[f] = sk_ld(rk, lf[f] - adjk, sk);
   };
   // unconditional (no merge of old and new slots); CLAMP re-reads the last full
   // pair for steps past it, else the step must lie before it

@@ -84,7 +84,7 @@ def test_exact_small(key):
 
 
 @pytest.mark.parametrize("ident,n,h", [(1, 999, 1), (2, 700, 1), (3, 600, 1), (4, 300, 2),
-                                       (5, 150, 1)])
+                                       (5, 150, 1), (2, 2501, 2), (3, 1601, 2)])
 def test_state_matches_oracle_moments(ident, n, h):
     """The exported [M | N] equals the oracle's moments entry by entry, within
     fp32 rounding of the sum of absolute terms (oracle run on |K|, |V|)."""
@@ -106,7 +106,8 @@ def test_state_matches_oracle_moments(ident, n, h):
 
 
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
-                                    (128, 128, 1), (4, 4, 7), (32, 8, 2)])
+                                    (128, 128, 1), (4, 4, 7), (32, 8, 2), (32, 16, 2),
+                                    (64, 16, 1), (128, 16, 1)])
 def test_other_shapes(d, dv, p):
     w = CONFIGS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
