@@ -19,7 +19,8 @@
 // and at level 2 (no b2 digit, "wide") 32 values of e.  A wave owns a unit: 4
 // b1 pairs x 2 b2 pairs (or b2 values, or 32-column chunks), one 16-chunk of c
 // and F, i.e. 8 blocks (128 accumulator registers).  Per two keys it loads the
-// key and value components it needs with 64-byte loads, rotates the key row so
+// key and value components it needs (buffer loads, 64 contiguous bytes per
+// 16-lane row), rotates the key row so
 // that the unit's b1 (b2) digits line up, and forms each operand with one
 // VALU multiply whose second factor is a DPP row broadcast (v_mul_f32_dpp
 // row_newbcast): 6 such multiplies feed 8 matrix instructions, and no feature
