@@ -1269,13 +1269,16 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   }
   hipError_t e1 = hipGetLastError();
   timing_mark(s, 1, true);
-  // queries per finishing workgroup: a power of two with qg * (d + dv) <= 256
+  // threads per (query, column) and queries per finishing workgroup (a power of
+  // two with qg * (d + dv) * lanes <= 256)
+  const int cols = s->d + s->dv;
+  const int lanes = cols <= 64 ? 4 : (cols <= 128 ? 2 : 1);
   int qg = 1;
-  while (qg < SK_TMQ && 2 * qg * (s->d + s->dv) <= 256) qg *= 2;
+  while (qg < SK_TMQ && 2 * qg * cols * lanes <= 256) qg *= 2;
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / qg) * s->h)),
                      dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
-                     s->dv, qg, (float)s->count, Q, s->center, out, Z);
+                     s->dv, qg, lanes, (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
   (void)hipFreeAsync(parts, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;

@@ -201,22 +201,26 @@ void sk_query_kernel(const float* __restrict__ Q, long long m,
 }
 
 // Sum the partials of every tile in tile order, add the count, divide.  One
-// workgroup per (head, query tile, group of qg queries), qg * (d + dv) <= 256, the
-// tile table staged in LDS once.  Thread (query, col) adds column col of its query
-// over the tiles in tile order (four running sums, tile index mod 4): a column
-// col < d of a lower level holds a share of Zhat, col >= d one of Ntilde[col - d]
-// (top-level tiles hold only the Ntilde columns, at col - d).  Zhat is then the
-// count plus the Zhat columns of the query, added in column order.
+// workgroup per (head, query tile, group of qg queries), the tile table staged in
+// LDS once.  Entry (query, col) adds column col of its query over the tiles in
+// four running sums (tile index mod 4, each in tile order), added as (s0 + s1) +
+// (s2 + s3); `lanes` (4, 2 or 1) threads share an entry, each taking residues
+// lane, lane + lanes, ..., so the tiles' loads go out in parallel.  qg * (d + dv)
+// * lanes <= 256.  A column col < d of a lower level holds a share of Zhat, col >=
+// d one of Ntilde[col - d] (top-level tiles hold only the Ntilde columns, at
+// col - d).  Zhat is then the count plus the Zhat columns of the query, added in
+// column order.
 #define SK_QFIN_LDS 1024
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
                      int ntiles, int nqt, long long PB, long long m, int d, int dv, int qg,
-                     float count, const float* __restrict__ Q,
+                     int lanes, float count, const float* __restrict__ Q,
                      const float* __restrict__ center, float* __restrict__ out,
                      float* __restrict__ Z) {
   __shared__ long long tp[SK_QFIN_LDS];
   __shared__ int tc[SK_QFIN_LDS];
   __shared__ int tt[SK_QFIN_LDS];
+  __shared__ float rs[4][256];        // residue sums per entry
   __shared__ float cs[256];
   __shared__ float zq[256];
   const int tid = threadIdx.x;
@@ -238,9 +242,11 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     }
   }
   __syncthreads();
-  const bool act = tid < qg * cols;
-  const int ql = act ? tid / cols : 0;
-  const int col = tid - ql * cols;
+  const int nent = qg * cols;
+  const int ent = tid / lanes, ln = tid - ent * lanes;
+  const bool act = ent < nent;
+  const int ql = act ? ent / cols : 0;
+  const int col = act ? ent - ql * cols : 0;
   const long long qoff = qi0 + ql;
   // one term: the partial of tile ti for (query, col), zero if the tile has no such column
   auto term = [&](int ti) -> float {
@@ -251,17 +257,14 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     return (c >= 0) ? P[pofs + qoff * C + c] : 0.f;
   };
   if (act) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int ti = 0;
-    for (; ti + 4 <= ntiles; ti += 4) {
-      const float v0 = term(ti), v1 = term(ti + 1), v2 = term(ti + 2), v3 = term(ti + 3);
-      a0 += v0; a1 += v1; a2 += v2; a3 += v3;
+    for (int r = ln; r < 4; r += lanes) {
+      float a = 0.f;
+      for (int ti = r; ti < ntiles; ti += 4) a += term(ti);
+      rs[r][ent] = a;
     }
-    if (ti < ntiles) a0 += term(ti);
-    if (ti + 1 < ntiles) a1 += term(ti + 1);
-    if (ti + 2 < ntiles) a2 += term(ti + 2);
-    cs[tid] = (a0 + a1) + (a2 + a3);
   }
+  __syncthreads();
+  for (int e = tid; e < nent; e += 256) cs[e] = (rs[0][e] + rs[1][e]) + (rs[2][e] + rs[3][e]);
   __syncthreads();
   if (tid < qg) {
     const float* row = cs + tid * cols;
@@ -273,7 +276,7 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
   }
   __syncthreads();
   const long long q = qbase + ql;
-  if (act && col >= d && q < m) out[(head * m + q) * dv + (col - d)] = cs[tid] / zq[ql];
+  if (act && ln == 0 && col >= d && q < m) out[(head * m + q) * dv + (col - d)] = cs[ent] / zq[ql];
   // with a centre c the moments are those of k - c: the returned Zhat carries
   // e^{<q,c>}, which cancels in ohat
   if (tid < qg && qbase + tid < m) {
