@@ -389,8 +389,10 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   }
 }
 
+// Three waves per SIMD at d = 16 (168 registers; measured faster than two with
+// more registers), two at d = 32 (three would spill in the main loop).
 template <int RT, bool CENTER>
-__global__ __launch_bounds__(64 * KR_WAVES, 2)
+__global__ __launch_bounds__(64 * KR_WAVES, RT == 1 ? 3 : 2)
 void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ V,
                          long long n, long long hkeys, int dv,
                          const KrUnit* __restrict__ units, KrSplits P, int nhead,
