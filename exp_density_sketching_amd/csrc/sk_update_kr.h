@@ -389,10 +389,11 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   }
 }
 
-// Three waves per SIMD at d = 16 (168 registers; measured faster than two with
-// more registers), two at d = 32 (three would spill in the main loop).
+// Three waves per SIMD (168 registers; measured faster than two with more
+// registers).  At d = 32 the loops of units with two or more leading digits
+// (levels >= 5) spill a few registers; the others do not.
 template <int RT, bool CENTER>
-__global__ __launch_bounds__(64 * KR_WAVES, RT == 1 ? 3 : 2)
+__global__ __launch_bounds__(64 * KR_WAVES, 3)
 void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ V,
                          long long n, long long hkeys, int dv,
                          const KrUnit* __restrict__ units, KrSplits P, int nhead,
