@@ -116,6 +116,22 @@ def test_other_shapes(d, dv, p):
     _check_exact(w, K, V, Q, label=f"d={d} dv={dv} p={p}")
 
 
+@pytest.mark.parametrize("d,dv,p,n", [(16, 16, 6, 1024), (32, 8, 5, 768)])
+def test_deep_levels_digit_kernel(d, dv, p, n):
+    """Levels with two and three leading digits on the digit-organised kernel
+    (d = 16 up to degree 6, d = 32 up to degree 5; the states are 1.2 GB), against
+    the oracle's direct route."""
+    w = CONFIGS[1].scaled(n=n, m=64)
+    w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
+    s = E.sketch_create(d, dv, p, 1)
+    try:
+        assert E.sketch_update_path(s) == "digits"
+    finally:
+        s.destroy()
+    K, V, Q = generate(w)
+    _check_sketch(w, K, V, Q, label=f"d={d} dv={dv} p={p}")
+
+
 def test_decode_mode_exact():
     """m = 1..8 queries per head takes the streaming kernel."""
     for m in (1, 2, 3, 5, 8):
