@@ -1136,7 +1136,7 @@ int settle(sk_sketch* s) {
   return rc;
 }
 
-// Default staging size: up to 16384 keys per head in at most 32 MB, off below
+// Default staging size: up to 32768 keys per head in at most 32 MB, off below
 // 1024 keys.
 long long default_stage_cap(const sk_sketch* s) {
   const long long per_key = (long long)sizeof(float) * (s->d + s->dv) * s->h;

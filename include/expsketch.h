@@ -141,10 +141,11 @@ int sketch_reset(sk_handle s);
  * N_j += sum k^(x)j v^T for j = 0..p).
  *   K: device [h][n][d]; V: device [h][n][dv]; n >= 0 keys per head (n == 0: no-op).
  * The inputs may be reused or freed once the stream has passed the call.
- * Small calls are staged: a call of at most half the staging size (default up
- * to 16384 keys per head, at most 32 MB; see sketch_set_staging) copies its keys
- * and values into a buffer the handle owns, and the buffer is contracted in one
- * launch when it fills or when anything reads or merges the state.  The moments
+ * Small calls are staged: a call of at most half the staging size (by default
+ * 32768 keys per head, at most 32 MB per handle; see sketch_set_staging) copies
+ * its keys and values into a buffer the handle owns, and the buffer is
+ * contracted in one launch when it fills or when anything reads or merges the
+ * state.  The moments
  * are the same sums; only the grouping of keys into launches changes, and for a
  * given sequence of calls the results are deterministic.
  * Errors: SK_EINVAL (NULL/misaligned pointer with n > 0, n < 0), SK_ENOMEM
