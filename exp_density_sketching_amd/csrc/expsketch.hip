@@ -1440,7 +1440,14 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   // one thread per query on the VALU for d, dv <= 8 (there the value columns
   // would be padded 4x and the exponentials dominate)
   const bool use_mfma = !decode && bmax >= 16;
-  const long long nqt = decode ? 1 : (m + (use_mfma ? SK_XQ : 256) - 1) / (use_mfma ? SK_XQ : 256);
+  // 16 value columns: the 16x16x4 kernel (no padding of the value columns), 64
+  // queries per wave up to d = 32 (32 at d = 64, for registers); its buffer loads
+  // address a slice with 32-bit byte offsets, so the whole KV of a head must fit
+  const bool mfma16 = use_mfma && dv == 16 && d >= 16 && d <= 64 && use_exact_mfma16() &&
+                      (long long)n * 4LL * bmax < (1LL << 31) - (1LL << 16);
+  const bool qb4 = mfma16 && d <= 32;
+  const long long per_wg = !use_mfma ? 256 : (qb4 ? 256 : SK_XQ);   // queries per workgroup
+  const long long nqt = decode ? 1 : (m + per_wg - 1) / per_wg;
   // EXPSKETCH_EXACT_MINKEYS=<k> sets the fewest keys per slice (tuning aid).
   static const long long min_keys_env = [] {
     const char* v = std::getenv("EXPSKETCH_EXACT_MINKEYS");
@@ -1458,8 +1465,9 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     const long long ns_fill = std::min(((long long)di.num_cu + hq - 1) / hq, (nn + 511) / 512);
     ns = std::max(ns_long, ns_fill);
   } else {
-    // (measured: 1024-key slices for the 16x16x4 kernel at dv = 16, 512 otherwise)
-    const long long lk = min_keys_env > 0 ? min_keys_env : (dv == 16 && d >= 16 && d <= 64 ? 1024 : 512);
+    // (measured: 1024-key slices for the 16x16x4 kernel with 32 queries per wave,
+    // 512 otherwise)
+    const long long lk = min_keys_env > 0 ? min_keys_env : (mfma16 && !qb4 ? 1024 : 512);
     ns = std::min((8LL * di.num_cu + hq - 1) / hq, ((long long)n + lk - 1) / lk);
   }
   ns = std::max(1LL, ns);
@@ -1518,18 +1526,14 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
     case 2: SK_XM(DD, 2); break;      \
     default: SK_XM(DD, 4); break;     \
   }
-    // 16 value columns: the 16x16x4 kernel (no padding of the value columns)
-    // (its buffer loads address a slice with 32-bit byte offsets)
-    const bool mfma16 = dv == 16 && d >= 16 && d <= 64 && use_exact_mfma16() &&
-                        kps * 4LL * std::max(d, dv) < (1LL << 31) - (1LL << 16);
-#define SK_XM16(DD)                                                                      \
-  hipLaunchKernelGGL((sk_exact_mfma16<DD, 16>), grid, blk, 0, st, K, V, nn, Q, mm, kps, \
+#define SK_XM16(DD, QB)                                                                    \
+  hipLaunchKernelGGL((sk_exact_mfma16<DD, 16, QB>), grid, blk, 0, st, K, V, nn, Q, mm, kps, \
                      nsplit, parts)
     if (mfma16) {
       switch (d) {
-        case 16: SK_XM16(16); break;
-        case 32: SK_XM16(32); break;
-        default: SK_XM16(64); break;
+        case 16: SK_XM16(16, 4); break;
+        case 32: SK_XM16(32, 4); break;
+        default: SK_XM16(64, 2); break;
       }
     } else {
       switch (d) {

@@ -160,8 +160,8 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
 // sk_exact_mfma16 (many queries per head, value width a multiple of 16 that is
 // not one of 32): the same online softmax with v_mfma_f32_16x16x4_f32 for both
 // products, so 16 value columns fill the instruction (the 32x32 form pads them
-// to 32).  One workgroup = 4 waves x 32 queries (two 16-query blocks per wave),
-// one key slice; per stage of 32 keys (two 16-key blocks) each wave loads its
+// to 32).  One workgroup = 4 waves x 16 QB queries (QB 16-query blocks per wave:
+// 4 up to d = 32, 2 at d = 64 for registers), one key slice; per stage of 32 keys (two 16-key blocks) each wave loads its
 // operands straight from memory into registers, one stage ahead (buffer loads:
 // fixed lane offsets, the stage's offset in a scalar register; the rows of a
 // stage are shared by the workgroup's waves through L1/L2): no LDS, no barrier.
@@ -179,12 +179,14 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
 //       from S's register r and A = those keys' value rows.
 // The partial record is the one of sk_exact_decode (mu = ref in natural-log units).
 #define SK_XTAU 8.f
-template <int D, int DV>
+template <int D, int DV, int QB>
 __global__ __launch_bounds__(256)
 void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
                      long long n, const float* __restrict__ Q, long long m,
                      long long keys_per_split, int nsplit, float* __restrict__ parts) {
   static_assert(D % 16 == 0 && DV % 16 == 0, "widths in blocks of 16");
+  constexpr int QW = 16 * QB;               // queries per wave
+  constexpr int XQ = 4 * QW;                // queries per workgroup
   constexpr int NKK = D / 4;                // k-steps of the first product
   constexpr int NCB = DV / 16;              // value column blocks
   constexpr float LOG2E = 1.4426950408889634f;
@@ -201,10 +203,10 @@ void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
   const int nkeys = (int)(k_end > k_begin ? k_end - k_begin : 0);   // < 2^31 / (4 max(D, DV))
 
   // B operands of the first product: Q[query][4 kk + g] * log2 e
-  float qop[2][NKK];
+  float qop[QB][NKK];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const long long q = qt * SK_XQ + wave * 32 + qb * 16 + i16;
+  for (int qb = 0; qb < QB; ++qb) {
+    const long long q = qt * XQ + wave * QW + qb * 16 + i16;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qop[qb][kk] = q < m ? Q[(head * m + q) * D + 4 * kk + g] * LOG2E : 0.f;
@@ -243,19 +245,24 @@ void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
     }
   };
 
-  float ref[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  floatx4v acc[2][NCB];
+  float ref[QB], l[QB];
+  floatx4v acc[QB][NCB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
+    ref[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = floatx4v{0.f, 0.f, 0.f, 0.f};
 
   auto stage = [&](int kb0, int buf, auto part_c) {
     constexpr bool part = decltype(part_c)::value;
     const int nk = nkeys - kb0 < SK_XK ? nkeys - kb0 : SK_XK;
-    floatx4v sc[2][2];
+    floatx4v sc[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sc[qb][kb] = floatx4v{0.f, 0.f, 0.f, 0.f};
@@ -265,7 +272,7 @@ void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
       }
     if constexpr (part) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -273,7 +280,7 @@ void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
             if (16 * kb + 4 * g + r >= nk) sc[qb][kb][r] = -INFINITY;
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -334,10 +341,10 @@ void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     float lt = l[qb] + __shfl_xor(l[qb], 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const long long q = qt * SK_XQ + wave * 32 + qb * 16 + i16;
+    const long long q = qt * XQ + wave * QW + qb * 16 + i16;
     if (q < m) {
       float* P = parts + ((head * m + q) * nsplit + split) * (2 + DV);
       if (g == 0) {
