@@ -30,6 +30,8 @@ KR_EXTERN(1, false)
 KR_EXTERN(1, true)
 KR_EXTERN(2, false)
 KR_EXTERN(2, true)
+KR_EXTERN(4, false)
+KR_EXTERN(4, true)
 #undef KR_EXTERN
 
 namespace {
@@ -153,12 +155,15 @@ UpdateKernel update_kernel_for(bool center, int d, int dv) {
 }
 
 // The digit-organised update kernel (sk_update_kr.h) per key width d = 16 RT.
-// It runs for d = 16 and 32, where it is the faster of the two full-layout
-// kernels; at d = 64 and 128 the tile kernel is.
+// It runs for d = 16, 32 and 64, where it is the faster of the two full-layout
+// kernels; the other widths run the tile kernel.
 UpdateKrKernel update_kr_kernel_for(bool center, int d) {
   if (d == 16) return center ? sk_update_kr_kernel<1, true> : sk_update_kr_kernel<1, false>;
-  return center ? sk_update_kr_kernel<2, true> : sk_update_kr_kernel<2, false>;
+  if (d == 32) return center ? sk_update_kr_kernel<2, true> : sk_update_kr_kernel<2, false>;
+  return center ? sk_update_kr_kernel<4, true> : sk_update_kr_kernel<4, false>;
 }
+// key widths that run the digit kernel
+bool kr_width(int d) { return d == 16 || d == 32 || d == 64; }
 // EXPSKETCH_EXACT_MFMA16=0 keeps the 32x32 batched exact kernel at dv = 16.
 bool use_exact_mfma16() {
   static const bool v = [] {
@@ -849,7 +854,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   } else {
     for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
     for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
-    if ((d == 16 || d == 32) && use_update_kr()) plan_kr_units(s);
+    if (kr_width(d) && use_update_kr()) plan_kr_units(s);
   }
 
   plan_step(s);

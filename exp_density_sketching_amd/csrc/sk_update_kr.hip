@@ -6,7 +6,7 @@
 #include "sk_update_kr.h"
 
 #if !defined(KR_RT) || !defined(KR_CENTER)
-#error "compile with -DKR_RT=<1|2> -DKR_CENTER=<0|1>"
+#error "compile with -DKR_RT=<1|2|4> -DKR_CENTER=<0|1>"
 #endif
 
 template __global__ void sk_update_kr_kernel<KR_RT, (KR_CENTER != 0)>(

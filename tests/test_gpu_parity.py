@@ -355,12 +355,13 @@ def test_staged_calls_equal_direct_calls(layout):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("d,layout,want", [(16, "full", "digits"), (32, "full", "digits"),
-                                           (64, "full", "tiles"), (8, "full", "tiles"),
-                                           (16, "sym", "multiset")])
+                                           (64, "full", "digits"), (8, "full", "tiles"),
+                                           (128, "full", "tiles"), (16, "sym", "multiset")])
 def test_update_path(d, layout, want):
-    """Key widths 16 and 32 run the digit-organised kernel, the others the tile
-    kernel (both checked against the oracle above); the multiset layout its own."""
-    s = E.sketch_create(d, d, 3, 1, layout)
+    """Key widths 16, 32 and 64 run the digit-organised kernel, the others the
+    tile kernel (both checked against the oracle above); the multiset layout its
+    own."""
+    s = E.sketch_create(d, d, 2, 1, layout)
     try:
         assert E.sketch_update_path(s) == want
     finally:

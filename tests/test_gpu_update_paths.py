@@ -1,4 +1,4 @@
-"""The two full-layout update kernels agree: at d = 16 and 32 the digit-organised
+"""The two full-layout update kernels agree: at d = 16, 32 and 64 the digit-organised
 kernel runs by default and the tile kernel only with EXPSKETCH_UPDATE_KR=0, a
 setting read once per process, so the tile kernel runs in one child process on
 the same seeded inputs and both are checked against the float64 oracle and each
@@ -76,7 +76,7 @@ def _compare(tmp_path, tag, keys, path):
 
 
 def test_tile_and_digit_kernels_agree(tmp_path):
-    keys = [2, 3]                       # d = 16 (p = 4) and d = 32 (p = 3)
+    keys = [2, 3, 4]                    # d = 16 (p = 4), 32 (p = 3), 64 (p = 2, 3 heads)
     _child(tmp_path, "tiles", keys, EXPSKETCH_UPDATE_KR="0")
     _compare(tmp_path, "tiles", keys, "tiles")
 
