@@ -20,8 +20,9 @@
 // b1 pairs x 2 b2 pairs (or b2 values, or 32-column chunks), one 16-chunk of c
 // and F, i.e. 8 blocks (128 accumulator registers).  Per two keys it loads the
 // key and value components it needs (buffer loads, 64 contiguous bytes per
-// 16-lane row), rotates the key row so
-// that the unit's b1 (b2) digits line up, and forms each operand with one
+// 16-lane row) with the unit's b1 (b2) digits lined up in the row (at d = 16 by
+// rotating the row of c components, ds_bpermute; at d >= 32 by loading them
+// rotated), and forms each operand with one
 // VALU multiply whose second factor is a DPP row broadcast (v_mul_f32_dpp
 // row_newbcast): 6 such multiplies feed 8 matrix instructions, and no feature
 // tile passes through LDS.  Levels 0 and 1 (no b1 digit) run a small 16x16x4
@@ -166,10 +167,18 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   const int q1 = U.b1 >> 4, q2 = U.b2 >> 4;
   // byte offsets of the key components
   const unsigned la = 4u * (unsigned)(khalf * d + 16 * U.rc + m);
-  const unsigned l1 = 4u * (unsigned)(khalf * d + 16 * q1 + m);
-  const unsigned l2 = 4u * (unsigned)(khalf * d + 16 * q2 + m);
   const int src1 = (rowbase + ((m + (U.b1 & 15) + par) & 15)) * 4;
   const int src2 = (rowbase + ((m + (U.b2 & 15) + (MODE == KR_PAIR ? par : 0)) & 15)) * 4;
+  // d >= 32: the b1 and b2 components are loaded already rotated (lane m of the
+  // row gets the component the rotation would bring it; measured faster there),
+  // at d = 16 they come from the c components by a row rotation
+  constexpr bool ROTL = RT > 1;
+  const int rot1 = 16 * q1 + ((m + (U.b1 & 15) + par) & 15);
+  const int rot2 = 16 * q2 + ((m + (U.b2 & 15) + (MODE == KR_PAIR ? par : 0)) & 15);
+  const unsigned lx1 = 4u * (unsigned)(khalf * d + rot1);
+  const unsigned lx2 = 4u * (unsigned)(khalf * d + rot2);
+  const float cx1 = CENTER ? cen[rot1] : 0.f;
+  const float cx2 = CENTER ? cen[rot2] : 0.f;
   int fdig[NF > 0 ? NF : 1];
   unsigned lf[NF > 0 ? NF : 1];
   float cf[NF > 0 ? NF : 1];
@@ -180,8 +189,6 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
     cf[f] = CENTER ? cen[fdig[f]] : 0.f;
   }
   const float ca = CENTER ? cen[16 * U.rc + m] : 0.f;
-  const float c1 = CENTER ? cen[16 * q1 + m] : 0.f;
-  const float c2 = CENTER ? cen[16 * q2 + m] : 0.f;
 
   // prefetch ring (static slots)
   // (below the top level a u column comes from the key or the value row: both are
@@ -196,9 +203,9 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   auto load = [&](unsigned sk, unsigned sv, unsigned adjk, unsigned adjv, float& va, float& v1,
                   float& v2, float (&vu)[NBU], float (&vk)[NUK], float (&vf)[NF > 0 ? NF : 1]) {
     va = sk_ld(rk, la - adjk, sk);
-    if (RT > 1) {
-      v1 = sk_ld(rk, l1 - adjk, sk);
-      if (MODE != KR_WIDE) v2 = sk_ld(rk, l2 - adjk, sk);
+    if constexpr (ROTL) {
+      v1 = sk_ld(rk, lx1 - adjk, sk);
+      if (MODE != KR_WIDE) v2 = sk_ld(rk, lx2 - adjk, sk);
     }
 #pragma unroll
     for (int y = 0; y < NBU; ++y) {
@@ -231,12 +238,13 @@ void kr_body(const KrUnit& U, const float* __restrict__ Kh, const float* __restr
   // lane 2 x of row parity x' gets k[b1 + 2 x + x'], and lane 2 y of parity y'
   // k[b2 + 2 y + y'] (pair) or lane y k[b2 + y] (single)
   auto rotate = [&](float va, float v1, float v2, float& x1, float& x2) {
-    float k1 = RT > 1 ? v1 : va;
-    float k2 = RT > 1 ? (MODE != KR_WIDE ? v2 : 0.f) : va;
-    if (CENTER) {
-      k1 -= RT > 1 ? c1 : ca;
-      k2 -= RT > 1 ? c2 : ca;
+    if constexpr (ROTL) {
+      x1 = CENTER ? v1 - cx1 : v1;
+      x2 = MODE == KR_WIDE ? 0.f : (CENTER ? v2 - cx2 : v2);
+      return;
     }
+    const float k = CENTER ? va - ca : va;         // d = 16: b1, b2 and c share a row
+    const float k1 = k, k2 = k;
     x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src1, __builtin_bit_cast(int, k1)));
     x2 = MODE == KR_WIDE ? 0.f
          : __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src2, __builtin_bit_cast(int, k2)));
