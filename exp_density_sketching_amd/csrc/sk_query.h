@@ -180,8 +180,12 @@ void sk_query_kernel(const float* __restrict__ Q, long long m,
           float w = 0.f;
           if (valid) {
             w = zcol ? Qs[e * LDQ + q] * T.wz : T.wn;
-            for (int c = 0; c < t; ++c)
-              w *= Qs[((alo >> (LOGD * (t - 1 - c))) & dmask) * LDQ + q];
+            if (t == 1) {                     // the common case, without the loop
+              w *= Qs[(alo & dmask) * LDQ + q];
+            } else {
+              for (int c = 0; c < t; ++c)
+                w *= Qs[((alo >> (LOGD * (t - 1 - c))) & dmask) * LDQ + q];
+            }
           }
           Ys[ql * LDY + cl] = a[r] * w;
         }
