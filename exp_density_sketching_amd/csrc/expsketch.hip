@@ -700,10 +700,9 @@ KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
     const KrSplits P = kr_splits_for(s, n, ns);
     const long long waves = P.item0[P.ngroup] * s->h;
     const long long per_simd = (waves + simds - 1) / simds;   // they share its matrix core
-    // measured on MI355X: one wave per SIMD runs about 20% slower (no other wave
-    // covers its waits), and exactly two resident waves that all finish together
-    // about 5% slower than three or more, where the workgroups dispatched last fill
-    // the slots that free up first
+    // measured on MI355X (a SIMD holds three of this kernel's waves): with one
+    // wave per SIMD a launch runs about 20% slower than with three (no other wave
+    // covers its waits), with two about 5% slower
     const double shape = per_simd == 1 ? 1.2 : per_simd == 2 ? 1.05 : 1.0;
     const double cost = (double)per_simd * (double)P.kps[0] * (1.0 + 0.003 * P.nsplit) * shape;
     if (best_cost < 0.0 || cost < best_cost - 1e-9) {
