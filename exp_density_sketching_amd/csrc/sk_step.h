@@ -151,26 +151,39 @@ void sk_step_kernel(float* __restrict__ X, long long head_stride,
   for (int c = tid; c < dv; c += 256) rec[1 + c] = red[T.top ? c : d + c];
 }
 
-// Per head: Zhat = count + the tiles' Zhat parts in tile order, Ntilde likewise,
+// Per head: Zhat = count + the sum of the tiles' Zhat parts, Ntilde likewise (a
+// fixed order: interleaved running sums, each in tile order, added in order),
 // ohat = Ntilde / Zhat; with a centre c the moments are those of k - c and the
 // returned Zhat carries the factor e^{<q,c>} (which cancels in ohat).
 __global__ __launch_bounds__(256)
 void sk_step_finish(const float* __restrict__ parts, int ntiles, int d, int dv, float count,
                     const float* __restrict__ qin, const float* __restrict__ center,
                     float* __restrict__ out, float* __restrict__ Z) {
+  __shared__ float ps[256];
   __shared__ float zs;
   const int tid = threadIdx.x;
   const long long head = blockIdx.x;
-  const float* P = parts + head * ntiles * (long long)(1 + dv);
+  const int cols = 1 + dv;
+  // L threads per record column (a power of two, L * cols <= 256): thread j of
+  // column c adds the tiles j, j + L, ... in tile order; the column's L sums are
+  // then added in thread order
+  int L = 1;
+  while (2 * L * cols <= 256 && L < 64) L *= 2;
+  const int c = tid / L, j = tid - c * L;
+  const float* P = parts + head * ntiles * (long long)cols;
+  float a = 0.f;
+  if (c < cols)
+    for (int t = j; t < ntiles; t += L) a += P[(long long)t * cols + c];
+  ps[tid] = a;
+  __syncthreads();
+  float sum = 0.f;
+  if (c < cols && j == 0)
+    for (int i = 0; i < L; ++i) sum += ps[tid + i];
+  __syncthreads();
+  if (c < cols && j == 0) ps[c] = sum;
+  __syncthreads();
   if (tid == 0) {
-    float z0 = 0.f, z1 = 0.f;
-    int t = 0;
-    for (; t + 2 <= ntiles; t += 2) {
-      z0 += P[(long long)t * (1 + dv)];
-      z1 += P[(long long)(t + 1) * (1 + dv)];
-    }
-    if (t < ntiles) z0 += P[(long long)t * (1 + dv)];
-    zs = (z0 + z1) + count;
+    zs = ps[0] + count;
     float f = 1.f;
     if (center != nullptr) {
       float dot = 0.f;
@@ -180,14 +193,5 @@ void sk_step_finish(const float* __restrict__ parts, int ntiles, int d, int dv, 
     Z[head] = zs * f;
   }
   __syncthreads();
-  for (int c = tid; c < dv; c += 256) {
-    float n0 = 0.f, n1 = 0.f;
-    int t = 0;
-    for (; t + 2 <= ntiles; t += 2) {
-      n0 += P[(long long)t * (1 + dv) + 1 + c];
-      n1 += P[(long long)(t + 1) * (1 + dv) + 1 + c];
-    }
-    if (t < ntiles) n0 += P[(long long)t * (1 + dv) + 1 + c];
-    out[head * dv + c] = (n0 + n1) / zs;
-  }
+  for (int cc = tid; cc < dv; cc += 256) out[head * dv + cc] = ps[1 + cc] / zs;
 }
