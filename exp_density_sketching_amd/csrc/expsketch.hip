@@ -610,10 +610,10 @@ int build_sym(sk_sketch* s) {
 }
 
 // Decode-step tiles: every block of the state cut into row ranges of at most
-// ST_FLOATS floats (and ST_ROWS rows).
+// fpt floats (and ST_ROWS rows).
 void plan_step_block(sk_sketch* s, long long xoff, long long rows, int C, int top, int level,
-                     int rc0, int j) {
-  const long long rpt = std::max(1LL, std::min<long long>(ST_ROWS, ST_FLOATS / C));
+                     int rc0, int j, long long fpt) {
+  const long long rpt = std::max(1LL, std::min<long long>(ST_ROWS, fpt / C));
   double fj = 1.0;
   for (int i = 2; i <= j; ++i) fj *= i;
   for (long long r0 = 0; r0 < rows; r0 += rpt) {
@@ -632,13 +632,18 @@ void plan_step_block(sk_sketch* s, long long xoff, long long rows, int C, int to
 }
 
 void plan_step(sk_sketch* s) {
+  // floats per tile: ST_FLOATS, halved (down to 2048) while the launch (tiles
+  // times heads) would have fewer than two workgroups per CU
+  const long long total = (long long)s->XS * s->h;
+  long long fpt = ST_FLOATS;
+  while (fpt > 2048 && total / fpt < 2LL * std::max(1, s->dev.num_cu)) fpt /= 2;
   if (s->layout == SK_LAYOUT_SYM) {
     const int Cl = s->d + s->dv;
-    if (s->Rlo > 0) plan_step_block(s, 0, s->Rlo, Cl, 0, -1, 0, 0);
-    plan_step_block(s, s->Rlo * Cl, s->Rtop, s->dv, 1, -1, (int)s->Rlo, 0);
+    if (s->Rlo > 0) plan_step_block(s, 0, s->Rlo, Cl, 0, -1, 0, 0, fpt);
+    plan_step_block(s, s->Rlo * Cl, s->Rtop, s->dv, 1, -1, (int)s->Rlo, 0, fpt);
   } else {
     for (int j = 0; j <= s->p; ++j)
-      plan_step_block(s, s->xoff[j], s->rows[j], s->C[j], j == s->p, j, 0, j);
+      plan_step_block(s, s->xoff[j], s->rows[j], s->C[j], j == s->p, j, 0, j, fpt);
   }
 }
 

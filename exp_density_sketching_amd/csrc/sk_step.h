@@ -21,7 +21,7 @@
 #include "sk_common.h"
 #include "sk_sym.h"
 
-#define ST_FLOATS 8192    // state floats per workgroup (32 KB)
+#define ST_FLOATS 8192    // state floats per workgroup at most (32 KB)
 #define ST_ROWS 1024      // rows per workgroup at most
 
 // One row range of one block (full layout: a level j; multiset layout: the lower
