@@ -164,16 +164,26 @@ void sk_step_finish(const float* __restrict__ parts, int ntiles, int d, int dv, 
   const int tid = threadIdx.x;
   const long long head = blockIdx.x;
   const int cols = 1 + dv;
-  // L threads per record column (a power of two, L * cols <= 256): thread j of
-  // column c adds the tiles j, j + L, ... in tile order; the column's L sums are
-  // then added in thread order
-  int L = 1;
-  while (2 * L * cols <= 256 && L < 64) L *= 2;
+  // L threads per record column (L * cols <= 256): thread j of column c adds the
+  // tiles j, j + L, ... in tile order, 16 loads in flight at a time (the records
+  // come from other XCDs' writes, so each load is a long round trip); the
+  // column's L sums are then added in thread order
+  const int L = std::max(1, std::min(64, 256 / cols));
   const int c = tid / L, j = tid - c * L;
   const float* P = parts + head * ntiles * (long long)cols;
   float a = 0.f;
-  if (c < cols)
-    for (int t = j; t < ntiles; t += L) a += P[(long long)t * cols + c];
+  if (c < cols) {
+    const float* Pc = P + c;
+    int t = j;
+    for (; t + 15 * L < ntiles; t += 16 * L) {
+      float r[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) r[u] = Pc[(long long)(t + u * L) * cols];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a += r[u];
+    }
+    for (; t < ntiles; t += L) a += Pc[(long long)t * cols];
+  }
   ps[tid] = a;
   __syncthreads();
   float sum = 0.f;
