@@ -272,9 +272,9 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import exp_density_sketching_amd as E
     from exp_density_sketching_amd.workload import ingest
-    from synthetic import CONFIGS, generate
+    from synthetic import WORKLOADS, generate
 
-    w = CONFIGS[args.workload]
+    w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     if args.counters:
         return counters_pass(w, E, torch, generate, args.layout)
@@ -465,7 +465,7 @@ def main():
     if kv_bytes <= 256e6:
         # this workload's KV stays in the Infinity Cache: the exact path's HBM
         # figure comes from the 32-head workload's decode
-        line["exact_decode_hbm"] = exact_decode_hbm(CONFIGS[4], E, torch, args.decode_steps)
+        line["exact_decode_hbm"] = exact_decode_hbm(WORKLOADS[4], E, torch, args.decode_steps)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, K, V, Q, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -12,8 +12,8 @@ q) is the one stated in "Rumo a Limites Estritos para Atenção em Streaming"
 queries is how those pages set the temperature regime (same page, regimes 1 and 2).
 """
 
-from .configs import CONFIGS, Workload, workload
+from .configs import WORKLOADS, Workload, workload
 from .generate import generate, generate_head, vectors, values
 
-__all__ = ["CONFIGS", "Workload", "workload", "generate", "generate_head",
+__all__ = ["WORKLOADS", "Workload", "workload", "generate", "generate_head",
            "vectors", "values"]

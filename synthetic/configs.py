@@ -52,7 +52,7 @@ class Workload:
         return replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "tiny_high_temp_d4_p3", d=4, dv=4, p=3, n=4096, m=64, h=1,
                 key_dist="sphere", key_r=1.0, val_dist="uniform",
                 chunk=0, substreams=1),
@@ -72,4 +72,4 @@ CONFIGS = {
 
 
 def workload(ident: int) -> Workload:
-    return CONFIGS[int(ident)]
+    return WORKLOADS[int(ident)]

@@ -17,8 +17,8 @@ def test_more_than_one_gpu_is_refused():
 def test_exact_kernel_names_follow_the_library_rule():
     sys.path.insert(0, ROOT)
     import bench
-    from synthetic import CONFIGS
-    names = {i: bench.exact_batched_kernel(CONFIGS[i]) for i in CONFIGS}
+    from synthetic import WORKLOADS
+    names = {i: bench.exact_batched_kernel(WORKLOADS[i]) for i in WORKLOADS}
     assert names[1] == "sk_exact_tiled (VALU)"          # d = dv = 4
     assert names[2] == "sk_exact_mfma16"                # dv = 16
     assert names[3] == names[4] == "sk_exact_mfma"      # dv = 32, 64

@@ -14,7 +14,7 @@ import torch
 import oracle
 import exp_density_sketching_amd as E
 from exp_density_sketching_amd.workload import ingest, run_sketch
-from synthetic import CONFIGS, generate
+from synthetic import WORKLOADS, generate
 from tests.gpu_util import (SK_Z_REL, SK_O_ABS, EX_Z_REL, EX_O_ABS, gpu, host, zrel,
                             oabs, say)
 
@@ -66,7 +66,7 @@ SMALL = {
 
 def _small(key):
     ident = key if isinstance(key, int) else int(str(key)[0])
-    return CONFIGS[ident].scaled(**SMALL[key])
+    return WORKLOADS[ident].scaled(**SMALL[key])
 
 
 @pytest.mark.parametrize("key", list(SMALL))
@@ -88,7 +88,7 @@ def test_exact_small(key):
 def test_state_matches_oracle_moments(ident, n, h):
     """The exported [M | N] equals the oracle's moments entry by entry, within
     fp32 rounding of the sum of absolute terms (oracle run on |K|, |V|)."""
-    w = CONFIGS[ident].scaled(n=n, m=1, h=h, chunk=256 if ident in (2, 3) else 0,
+    w = WORKLOADS[ident].scaled(n=n, m=1, h=h, chunk=256 if ident in (2, 3) else 0,
                               substreams=2 if ident == 3 else 1)
     K, V, Q = generate(w)
     Kg, Vg = gpu(K, V)
@@ -109,7 +109,7 @@ def test_state_matches_oracle_moments(ident, n, h):
                                     (128, 128, 1), (4, 4, 7), (32, 8, 2), (32, 16, 2),
                                     (64, 16, 1), (128, 16, 1)])
 def test_other_shapes(d, dv, p):
-    w = CONFIGS[1].scaled(n=1537, m=129)
+    w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
     K, V, Q = generate(w)
     _check_sketch(w, K, V, Q, label=f"d={d} dv={dv} p={p}")
@@ -121,7 +121,7 @@ def test_deep_levels_digit_kernel(d, dv, p, n):
     """Levels with two and three leading digits on the digit-organised kernel
     (d = 16 up to degree 6, d = 32 up to degree 5; the states are 1.2 GB), against
     the oracle's direct route."""
-    w = CONFIGS[1].scaled(n=n, m=64)
+    w = WORKLOADS[1].scaled(n=n, m=64)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
     s = E.sketch_create(d, dv, p, 1)
     try:
@@ -135,7 +135,7 @@ def test_deep_levels_digit_kernel(d, dv, p, n):
 def test_decode_mode_exact():
     """m = 1..8 queries per head takes the streaming kernel."""
     for m in (1, 2, 3, 5, 8):
-        w = CONFIGS[4].scaled(n=9001, m=m, h=4)
+        w = WORKLOADS[4].scaled(n=9001, m=m, h=4)
         K, V, Q = generate(w)
         _check_exact(w, K, V, Q, label=f"decode m={m}")
 
@@ -178,7 +178,7 @@ def test_merge_mismatch_and_determinism():
     with pytest.raises(E.SketchError) as ei:
         E.sketch_merge(a, b)
     assert ei.value.code == -3
-    w = CONFIGS[5].scaled(n=20000, m=100)
+    w = WORKLOADS[5].scaled(n=20000, m=100)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     outs = []
@@ -193,7 +193,7 @@ def test_merge_mismatch_and_determinism():
 
 
 def test_merge_equals_single_stream():
-    w = CONFIGS[2].scaled(n=9000, m=64, chunk=1024)
+    w = WORKLOADS[2].scaled(n=9000, m=64, chunk=1024)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     whole, _ = ingest(w, Kg, Vg)
@@ -207,7 +207,7 @@ def test_merge_equals_single_stream():
 # Full-size workloads, run as the benchmark runs them; sampled queries checked.
 @pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
 def test_full_size_sampled(ident):
-    w = CONFIGS[ident]
+    w = WORKLOADS[ident]
     say(f"full workload {ident}: {w.name} generating inputs")
     K, V, Q = generate(w)
     rng = np.random.default_rng(1234 + ident)
@@ -221,7 +221,7 @@ def test_full_size_sampled(ident):
 
 def test_full_size_decode_exact():
     """Decode shape of the 32-head workload: one query per head over 128K keys."""
-    w = CONFIGS[4].scaled(m=1)
+    w = WORKLOADS[4].scaled(m=1)
     K, V, Q = generate(w)
     _check_exact(w, K, V, Q, label="decode 32x128K")
 
@@ -230,7 +230,7 @@ def test_sketch_error_within_bound():
     """GPU sketch against GPU exact, against the truncation bound (high-temperature
     workloads, where the bound is informative)."""
     for ident in (1, 2, 4):
-        w = CONFIGS[ident].scaled(n=16384, m=128, h=min(CONFIGS[ident].h, 2))
+        w = WORKLOADS[ident].scaled(n=16384, m=128, h=min(WORKLOADS[ident].h, 2))
         K, V, Q = generate(w)
         Kg, Vg, Qg = gpu(K, V, Q)
         o_s, z_s, sk = run_sketch(w, Kg, Vg, Qg)
@@ -248,7 +248,7 @@ def test_sketch_error_within_bound():
 
 def test_kernel_timing_events():
     """sketch_timing records one event pair per update/query kernel launch."""
-    w = CONFIGS[2].scaled(n=3 * 4096, m=200)
+    w = WORKLOADS[2].scaled(n=3 * 4096, m=200)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     sk = E.sketch_create(w.d, w.dv, w.p)
@@ -276,7 +276,7 @@ def test_pending_partials_are_always_added(layout, staging):
     4096 keys (split) alternate with calls of 100 keys (one split, added in
     place); a reset drops what is pending; a merge takes pending partials of
     both sides."""
-    w = CONFIGS[2].scaled(n=25000, m=8)
+    w = WORKLOADS[2].scaled(n=25000, m=8)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     sizes = [4096, 4096, 100, 4096, 257, 4096, 4096]
@@ -317,7 +317,7 @@ def test_staged_calls_equal_direct_calls(layout):
     """Staged small calls (default staging) give the moments of the same keys as
     one direct call; staged keys are contracted before every reader, dropped by
     reset, and kept in order around a large call and a staging change."""
-    w = CONFIGS[2].scaled(n=40000, m=16, h=2)
+    w = WORKLOADS[2].scaled(n=40000, m=16, h=2)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     st = E.sketch_create(w.d, w.dv, w.p, 2, layout)

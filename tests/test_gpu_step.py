@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import exp_density_sketching_amd as E
-from synthetic import CONFIGS, generate
+from synthetic import WORKLOADS, generate
 from tests.gpu_util import SK_Z_REL, SK_O_ABS, gpu, host, say
 
 pytestmark = pytest.mark.gpu
@@ -27,7 +27,7 @@ CASES = {
 
 def _case(key, steps):
     c = CASES[key]
-    w = CONFIGS[c["ident"]].scaled(n=c["n"] + steps, m=steps, h=c["h"], chunk=0,
+    w = WORKLOADS[c["ident"]].scaled(n=c["n"] + steps, m=steps, h=c["h"], chunk=0,
                                    substreams=1)
     return w, c["n"]
 

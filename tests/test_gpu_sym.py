@@ -17,7 +17,7 @@ import torch
 import oracle
 import exp_density_sketching_amd as E
 from exp_density_sketching_amd.workload import ingest, run_sketch
-from synthetic import CONFIGS, generate
+from synthetic import WORKLOADS, generate
 from tests.gpu_util import SK_Z_REL, SK_O_ABS, gpu, host, oabs, say, zrel
 from tests.test_gpu_parity import SMALL, _check_sketch, _small
 
@@ -36,7 +36,7 @@ def test_sym_sketch_small(key):
 def test_sym_state_matches_oracle(ident, n, h):
     """The exported multiset entries equal the oracle's, entry by entry, within
     fp32 rounding of the sum of absolute terms (oracle run on |K|, |V|)."""
-    w = CONFIGS[ident].scaled(n=n, m=1, h=h, chunk=256 if ident in (2, 3) else 0,
+    w = WORKLOADS[ident].scaled(n=n, m=1, h=h, chunk=256 if ident in (2, 3) else 0,
                               substreams=2 if ident == 3 else 1)
     K, V, Q = generate(w)
     Kg, Vg = gpu(K, V)
@@ -59,7 +59,7 @@ def test_sym_state_matches_oracle(ident, n, h):
                                     (128, 128, 1), (4, 4, 7), (32, 8, 2), (64, 128, 2),
                                     (128, 4, 2)])
 def test_sym_other_shapes(d, dv, p):
-    w = CONFIGS[1].scaled(n=1537, m=129)
+    w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
     K, V, Q = generate(w)
     _check_sketch(w, K, V, Q, label=f"d={d} dv={dv} p={p}", layout="sym")
@@ -67,7 +67,7 @@ def test_sym_other_shapes(d, dv, p):
 
 def test_sym_equals_full_layout():
     """Both layouts answer the same queries to fp32 rounding."""
-    w = CONFIGS[2].scaled(n=3 * 4096 + 11, m=300)
+    w = WORKLOADS[2].scaled(n=3 * 4096 + 11, m=300)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     of, zf, a = run_sketch(w, Kg, Vg, Qg, layout="full")
@@ -115,7 +115,7 @@ def test_sym_empty_degenerate_and_merge():
 
 
 def test_sym_deterministic():
-    w = CONFIGS[5].scaled(n=20000, m=100)
+    w = WORKLOADS[5].scaled(n=20000, m=100)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     outs = []
@@ -129,7 +129,7 @@ def test_sym_deterministic():
 
 @pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
 def test_sym_full_size_sampled(ident):
-    w = CONFIGS[ident]
+    w = WORKLOADS[ident]
     say(f"full workload {ident}: {w.name} (multiset layout) generating inputs")
     K, V, Q = generate(w)
     rng = np.random.default_rng(4321 + ident)
@@ -141,7 +141,7 @@ def test_sym_full_size_sampled(ident):
 
 
 def test_sym_kernel_timing_events():
-    w = CONFIGS[2].scaled(n=3 * 4096, m=200)
+    w = WORKLOADS[2].scaled(n=3 * 4096, m=200)
     K, V, Q = generate(w)
     Kg, Vg, Qg = gpu(K, V, Q)
     sk = E.sketch_create(w.d, w.dv, w.p, layout="sym")
@@ -167,7 +167,7 @@ def test_sym_kernel_timing_events():
     (8, 8, 3, 1, 2500, 129, 0),          # one query past a tile
 ])
 def test_edge_shapes(layout, d, dv, p, h, n, m, chunk):
-    w = CONFIGS[1].scaled(n=n, m=m, h=h, chunk=chunk)
+    w = WORKLOADS[1].scaled(n=n, m=m, h=h, chunk=chunk)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
     K, V, Q = generate(w)
     _check_sketch(w, K, V, Q, label=f"edge d={d} dv={dv} p={p} h={h} n={n} m={m}",

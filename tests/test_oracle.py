@@ -25,7 +25,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import CONFIGS, generate
+from synthetic import WORKLOADS, generate
 from tests import oracle_pins as pins
 
 TIGHT = 1e-12
@@ -40,7 +40,7 @@ def test_p1_bruteforce(d, p):
                                             (3, 384, 24, 128), (4, 384, 24, 128),
                                             (5, 96, 12, 16)])
 def test_p2_moment_equals_direct(ident, n, m, chunk):
-    w = CONFIGS[ident].scaled(n=n, m=m, h=1)
+    w = WORKLOADS[ident].scaled(n=n, m=m, h=1)
     K, V, Q = generate(w)
     assert pins.pin_moment_equals_direct(oracle, K[0], V[0], Q[0], w.p, chunk) < 1e-11
 
@@ -72,7 +72,7 @@ def test_p7_convergence():
 
 @pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
 def test_p8_truncation_bound(ident):
-    w = CONFIGS[ident].scaled(n=2048, m=48, h=1)
+    w = WORKLOADS[ident].scaled(n=2048, m=48, h=1)
     K, V, Q = generate(w)
     K, V, Q = K[0], V[0], Q[0]
     rho = oracle.measured_radius(K, Q)

@@ -11,7 +11,7 @@
 import pytest
 
 import oracle
-from synthetic import CONFIGS, generate
+from synthetic import WORKLOADS, generate
 from tests import oracle_pins as pins
 
 TIGHT = 1e-12
@@ -31,7 +31,7 @@ def test_s2_bruteforce(d, p):
                                             (3, 384, 24, 128), (4, 384, 24, 128),
                                             (5, 200, 12, 64)])
 def test_s3_equals_direct(ident, n, m, chunk):
-    w = CONFIGS[ident].scaled(n=n, m=m, h=1)
+    w = WORKLOADS[ident].scaled(n=n, m=m, h=1)
     K, V, Q = generate(w)
     assert pins.pin_sym_equals_direct(oracle, K[0], V[0], Q[0], w.p, chunk) < 1e-11
 
