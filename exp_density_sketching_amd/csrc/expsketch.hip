@@ -52,6 +52,17 @@ long long query_rows_per_tile() {
   return v;
 }
 
+// a level's query split keeps the fewest trailing digits whose columns (d^t C)
+// reach this count (EXPSKETCH_QUERY_MINCOLS overrides, tuning aid)
+long long query_min_cols() {
+  static const long long v = [] {
+    const char* e = std::getenv("EXPSKETCH_QUERY_MINCOLS");
+    const long long r = e ? std::atoll(e) : 0;
+    return r >= 1 ? r : (long long)SK_TNQ;
+  }();
+  return v;
+}
+
 bool is_pow2_in(int x, int lo, int hi) {
   return x >= lo && x <= hi && (x & (x - 1)) == 0;
 }
@@ -406,9 +417,15 @@ bool plan_kr_units(sk_sketch* s) {
 // least SK_TNQ columns), 128-column tiles, a_hi ranges of query_rows_per_tile().
 void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long* pb) {
   const int d = s->d, C = s->C[j];
+  // t trailing digits go to the epilogue (folded with the weights q^(x)t): the
+  // fewest whose d^t C columns fill a column tile.  A level whose own C columns
+  // fill half a tile takes none: the half-empty tile, with its deeper rows and
+  // half the partials, costs less than folding a digit (measured at C = 64 and
+  // 128 against one folded digit; at C = 8 a half-filled tile cost more).
   int t = j;
   for (int tt = 0; tt <= j; ++tt) {
-    if (std::pow((double)d, tt) * C >= SK_TNQ) { t = tt; break; }
+    const double cols = std::pow((double)d, tt) * C;
+    if (cols >= query_min_cols() || (tt == 0 && 2 * C >= SK_TNQ)) { t = tt; break; }
   }
   while (t > SK_MAXDIG) --t;
   const int sd = j - t;

@@ -598,7 +598,21 @@ void sk_exact_combine(const float* __restrict__ parts, int nsplit, long long m, 
   const int g = tid / slots, slot = tid - g * slots;
   float acc = 0.f;
   if (g < groups && ms != -INFINITY) {
-    for (int sp = g; sp < nsplit; sp += groups) {
+    int sp = g;
+    // eight slice records in flight per thread (each load is a long round trip:
+    // the records were written on other XCDs), added in slice order
+    for (; sp + 7 * groups < nsplit; sp += 8 * groups) {
+      float mu[8], x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* r = P + (long long)(sp + u * groups) * rec;
+        mu[u] = r[0];
+        x[u] = r[1 + slot];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += x[u] * expf(mu[u] - ms);
+    }
+    for (; sp < nsplit; sp += groups) {
       const float* r = P + (long long)sp * rec;
       acc += r[1 + slot] * expf(r[0] - ms);
     }
