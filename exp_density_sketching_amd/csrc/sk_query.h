@@ -11,7 +11,8 @@
 // a_hi and t trailing digits a_lo, q^(x)j[a] = q^(x)s[a_hi] q^(x)t[a_lo], so
 //     Y_j[q][e] = sum_{a_lo} q^(x)t[a_lo] * sum_{a_hi} q^(x)s[a_hi] X_j[a_hi][(a_lo, e)].
 // The inner sum is a GEMM whose columns (a_lo, e) are rows of X_j read as they lie
-// in memory; t is chosen so that it has at least 128 columns.  One workgroup owns
+// in memory; t is the fewest digits that give it at least 128 columns, or none
+// when the level's own columns fill half of them.  One workgroup owns
 // 128 queries x 128 columns x a range of a_hi: per stage of 32 rows it forms the
 // query features q^(x)s in LDS, stages the state rows through LDS (fetched one
 // stage ahead into registers) and runs the same 2x2 v_mfma_f32_32x32x2_f32 register
