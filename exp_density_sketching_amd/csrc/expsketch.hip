@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -228,6 +229,77 @@ QueryKernel query_kernel_for(int logd) {
   }
 }
 
+// Per-call partials (query, exact path).  A hipMallocAsync that follows a
+// hipFreeAsync on the same stream makes the host wait here until that stream has
+// drained (measured: back-to-back calls then return only as each previous call's
+// kernels finish), so the partials live in a buffer kept across calls: the
+// event recorded after each use orders the next user behind it.  Requests above
+// kKeepBytes take a stream-ordered allocation of their own (their kernels run
+// longer than that wait).
+constexpr size_t kKeepBytes = size_t(256) << 20;
+
+struct Workspace {
+  float* ptr = nullptr;
+  size_t cap = 0;                          // bytes
+  hipEvent_t done = nullptr;               // recorded after the last use
+};
+
+// Points *out at `bytes` of device memory for one call on stream st: the kept
+// buffer (grown, once the work that last used it has finished, when too small)
+// or, beyond kKeepBytes, its own stream-ordered allocation (*own = true).
+// `ordered`: every use of ws is on st (stream order alone serialises them);
+// otherwise st first waits for the last use.
+int take_workspace(Workspace* ws, size_t bytes, hipStream_t st, bool ordered, float** out,
+                   bool* own) {
+  *out = nullptr;
+  *own = false;
+  if (bytes > kKeepBytes) {
+    if (hipMallocAsync((void**)out, bytes, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return SK_ENOMEM;
+    }
+    *own = true;
+    return SK_OK;
+  }
+  if (ws->done == nullptr)
+    SK_TRY(hipEventCreateWithFlags(&ws->done, hipEventDisableTiming));
+  else if (!ordered)
+    SK_TRY(hipStreamWaitEvent(st, ws->done, 0));
+  if (bytes > ws->cap) {
+    SK_TRY(hipEventSynchronize(ws->done));
+    (void)hipFree(ws->ptr);
+    ws->ptr = nullptr;
+    ws->cap = 0;
+    const size_t cap = std::min(kKeepBytes, std::max(bytes, size_t(1) << 20));
+    if (hipMalloc((void**)&ws->ptr, cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return SK_ENOMEM;
+    }
+    ws->cap = cap;
+  }
+  *out = ws->ptr;
+  return SK_OK;
+}
+
+// Ends the call's use of what take_workspace gave it (work already enqueued).
+void release_workspace(Workspace* ws, float* p, bool own, hipStream_t st) {
+  if (own)
+    (void)hipFreeAsync(p, st);
+  else if (p != nullptr)
+    (void)hipEventRecord(ws->done, st);
+}
+
+void free_workspace(Workspace* ws) {
+  if (ws->done != nullptr) (void)hipEventSynchronize(ws->done);
+  (void)hipFree(ws->ptr);
+  if (ws->done != nullptr) (void)hipEventDestroy(ws->done);
+  *ws = Workspace{};
+}
+
+// exact_attend's kept partials, per (device, stream)
+std::mutex g_xws_mutex;
+std::map<std::pair<int, void*>, Workspace> g_xws;
+
 }  // namespace
 
 struct sk_sketch {
@@ -287,6 +359,7 @@ struct sk_sketch {
   float* stage_v = nullptr;                // [h][stage_cap][dv]
   long long stage_cap = -1;                // keys per head; 0 = off, -1 = default
   long long stage_n = 0;                   // keys per head staged
+  Workspace qws;                           // query partials, kept across calls
 };
 
 namespace {
@@ -970,6 +1043,7 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->stage_k);
   (void)hipFree(s->stage_v);
   if (s->flush_ev != nullptr) (void)hipEventDestroy(s->flush_ev);
+  free_workspace(&s->qws);
   (void)hipFree(s->view);
   for (int k = 0; k < 3; ++k)
     for (int w = 0; w < 2; ++w)
@@ -1278,9 +1352,10 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   if (nqt * nlaunch * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
   float* parts = nullptr;
-  if (hipMallocAsync((void**)&parts, pbytes, s->stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return SK_ENOMEM;
+  bool own = false;
+  {
+    const int rc = take_workspace(&s->qws, pbytes, s->stream, true, &parts, &own);
+    if (rc != SK_OK) return rc;
   }
   timing_mark(s, 1, false);
   if (s->layout == SK_LAYOUT_SYM) {
@@ -1306,7 +1381,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
                      s->dv, qg, lanes, (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
-  (void)hipFreeAsync(parts, s->stream);
+  release_workspace(&s->qws, parts, own, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   return SK_OK;
 }
@@ -1501,11 +1576,17 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   kps = (kps + 31) / 32 * 32;
   const int nsplit = kps > 0 ? (int)((n + kps - 1) / kps) : 1;
   const size_t pbytes = sizeof(float) * (size_t)h * m * nsplit * (2 + dv);
+  // one kept partials buffer per (device, stream), held until the process ends;
+  // the lock covers the whole call, so calls from several threads on one stream
+  // do not interleave their kernels on it.  The stream still waits for the
+  // buffer's last use: a destroyed stream's handle value can come back as a new
+  // stream while the old one's kernels run.
+  std::lock_guard<std::mutex> ws_lock(g_xws_mutex);
+  Workspace& ws = g_xws[std::make_pair(dev, reinterpret_cast<void*>(st))];
   float* parts = nullptr;
-  if (hipMallocAsync((void**)&parts, pbytes, st) != hipSuccess) {
-    (void)hipGetLastError();
-    return SK_ENOMEM;
-  }
+  bool own = false;
+  rc = take_workspace(&ws, pbytes, st, false, &parts, &own);
+  if (rc != SK_OK) return rc;
   const long long nn = n;
   const long long mm = m;
   if (decode) {
@@ -1579,7 +1660,7 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
-  (void)hipFreeAsync(parts, st);
+  release_workspace(&ws, parts, own, st);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   return SK_OK;
 }

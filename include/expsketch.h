@@ -177,6 +177,9 @@ int sketch_merge(sk_handle dst, sk_handle src);
  * ("O Método Polinomial", query of the truncated expansion).  No clamping: an
  * empty sketch gives Z = 0 and out = NaN (0/0), as IEEE division does.
  *   Q: device [h][m][d]; out: device [h][m][dv]; Z: device [h][m]; m >= 0.
+ * The per-tile partials live in a buffer the handle keeps (freed by
+ * sketch_destroy), grown on demand up to 256 MB; larger ones are taken from the
+ * stream-ordered allocator for the call.
  * Errors: SK_EINVAL, SK_ENOMEM (partials workspace), SK_EHIP.
  */
 int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z);
@@ -206,8 +209,11 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
  * fixed-order combine of the slices.  n == 0 gives Z = 0, out = NaN.
  *   K [h][n][d], V [h][n][dv], Q [h][m][d], out [h][m][dv], Z [h][m]: device.
  *   hip_stream: hipStream_t to run on (NULL = default stream).
- * Temporary partials are taken from the stream-ordered allocator
- * (hipMallocAsync) and released on the same stream.
+ * The per-slice partials (h * m * slices * (2 + dv) floats) live in a buffer
+ * the library keeps per (device, stream) until the process ends, grown on
+ * demand up to 256 MB; larger ones are taken from the stream-ordered allocator
+ * (hipMallocAsync) for the call.  Calls from several host threads are
+ * serialised while they enqueue their kernels.
  * Errors: SK_EINVAL (shapes, NULL/misaligned pointers, n or m < 0), SK_ENOMEM,
  * SK_EHIP.
  */
