@@ -105,9 +105,12 @@ def test_state_matches_oracle_moments(ident, n, h):
     assert ptr and D == w.D and cols == 1 + w.dv and cnt == n
 
 
+# the last four put 64 or more columns (d + dv, or dv at the top) on levels j >= 1,
+# where the query contracts the whole level without folding a digit
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
                                     (128, 128, 1), (4, 4, 7), (32, 8, 2), (32, 16, 2),
-                                    (64, 16, 1), (128, 16, 1)])
+                                    (64, 16, 1), (128, 16, 1),
+                                    (16, 64, 3), (8, 64, 3), (4, 64, 4), (32, 32, 2)])
 def test_other_shapes(d, dv, p):
     w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
