@@ -724,8 +724,14 @@ void plan_step_block(sk_sketch* s, long long xoff, long long rows, int C, int to
 void plan_step(sk_sketch* s) {
   // floats per tile: ST_FLOATS, halved (down to 2048) while the launch (tiles
   // times heads) would have fewer than two workgroups per CU
+  // (EXPSKETCH_STEP_FLOATS lowers the largest tile, tuning aid)
+  static const long long cap = [] {
+    const char* e = std::getenv("EXPSKETCH_STEP_FLOATS");
+    const long long v = e ? std::atoll(e) : 0;
+    return (v >= 256 && v <= ST_FLOATS) ? v : (long long)ST_FLOATS;
+  }();
   const long long total = (long long)s->XS * s->h;
-  long long fpt = ST_FLOATS;
+  long long fpt = cap;
   while (fpt > 2048 && total / fpt < 2LL * std::max(1, s->dev.num_cu)) fpt /= 2;
   if (s->layout == SK_LAYOUT_SYM) {
     const int Cl = s->d + s->dv;
