@@ -460,3 +460,88 @@ def pin_centered_moments(impl, p=3, seed=35):
     o, Z = sk.query(Q)
     od, Zd = impl.sketch_direct_centered(K, V, Q, p, mu)
     return max(relmax(Z * np.exp(Q @ mu), Zd), absmax(o, od))
+
+
+# Bounds (oracle/bounds.py) -------------------------------------------------------------
+#
+# Each pin returns a violation measure: 0.0 when the bound function behaves, a
+# positive number (the relative miss) otherwise.
+
+# Closed-form value of the relative truncation bound rho^(p+1)/(p+1)! e^(2 rho) at
+# rho = r^2 for the five workloads (p, r^2), evaluated by hand to five
+# significant digits: e^2/24, e^2/120, 2.25^4/24 e^4.5, 0.5625^3/6 e^1.125,
+# 4^7/5040 e^8.
+KDE_BOUND_TABLE = [(3, 1.0, 0.30788), (4, 1.0, 0.061575), (3, 2.25, 96.127),
+                   (2, 0.5625, 0.091369), (6, 4.0, 9690.5)]
+
+
+def pin_bound_table(impl):
+    """kde_relative_bound against the tabulated closed-form values (5 digits)."""
+    worst = 0.0
+    for p, rho, want in KDE_BOUND_TABLE:
+        got = impl.kde_relative_bound(p, rho)
+        worst = max(worst, abs(got - want) / want)
+    return max(0.0, worst - 1e-4)        # five significant digits
+
+
+def pin_term_bound_tight(impl):
+    """taylor_term_bound is the Lagrange remainder bound: at x = +rho the true
+    remainder e^x - T_p(x) = rho^(p+1)/(p+1)! e^xi with 0 < xi < rho, so
+    remainder / bound lies in [e^-rho, 1].  Checked with mpmath at 50 digits."""
+    worst = 0.0
+    mpmath.mp.dps = 50
+    for p in range(0, 7):
+        for rho in (0.05, 0.3, 1.0):
+            x = mpmath.mpf(rho)
+            rem = mpmath.exp(x) - mpmath.fsum(x ** j / mpmath.factorial(j) for j in range(p + 1))
+            ratio = float(rem) / impl.taylor_term_bound(p, rho)
+            lo = math.exp(-rho)
+            worst = max(worst, lo - ratio, ratio - 1.0)
+    mpmath.mp.dps = 15
+    return max(0.0, worst)
+
+
+def pin_measured_radius(impl):
+    """Hand example: the largest key norm and the largest query norm come from
+    different rows (key norms 3 and 1, query norms 0.5 and 2): rho = 3 * 2 = 6.
+    Also the empty stream (0) and a 3-4-5 key with a unit query (5)."""
+    K = np.array([[3.0, 0.0], [0.0, 1.0]])
+    Q = np.array([[0.0, 0.5], [-2.0, 0.0]])
+    K2 = np.array([[3.0, 4.0]])
+    Q2 = np.array([[0.0, -1.0]])
+    errs = [abs(impl.measured_radius(K, Q) - 6.0) / 6.0,
+            abs(impl.measured_radius(K2, Q2) - 5.0) / 5.0,
+            abs(impl.measured_radius(np.zeros((0, 2)), Q) - 0.0)]
+    return max(errs)
+
+
+def _two_group_case(rho, a, vscale, n=1000):
+    """d = 1, q = 1, p = 0: a fraction a of the keys at -rho with value +vscale,
+    the rest at +rho with value -vscale.  Returns (observed |ohat - o|, V)."""
+    na = int(round(a * n))
+    nb = n - na
+    ea, eb = math.exp(-rho), math.exp(rho)
+    # exact o (softmax weights) and the p = 0 sketch's ohat (all weights 1)
+    o = (na * ea * vscale - nb * eb * vscale) / (na * ea + nb * eb)
+    ohat = (na * vscale - nb * vscale) / n
+    V = np.array([[vscale]] * na + [[-vscale]] * nb)
+    return abs(ohat - o), V
+
+
+def pin_attention_bound_near_tight(impl):
+    """attention_abs_bound on a near-tight d = 1, p = 0 construction: keys at
+    +-rho with values at the two ends of the range (derived by hand: with rho
+    small the best split gives |ohat - o| ~ rho while the bound is ~ 2 rho, so the
+    observed error must sit within [0.45, 1] of the bound).  Values scaled by 10
+    (the bound scales with the range).  The observed errors here are computed by
+    hand from the two groups' softmax weights, not by the oracle's sketch."""
+    worst = 0.0
+    for rho in (1e-3, 1e-2):
+        for vscale in (1.0, 10.0):
+            best = 0.0
+            for a in np.linspace(0.3, 0.7, 41):
+                obs, V = _two_group_case(rho, a, vscale)
+                bound = float(impl.attention_abs_bound(0, rho, V)[0])
+                best = max(best, obs / bound)
+            worst = max(worst, best - 1.0, 0.45 - best)
+    return max(0.0, worst)

@@ -175,3 +175,19 @@ def test_truncation_bound_values():
             xs = np.linspace(-rho, rho, 201)
             rem = np.abs(np.exp(xs) - oracle.taylor_exp(xs, p)).max()
             assert rem <= oracle.taylor_term_bound(p, rho) * (1 + 1e-12)
+
+
+def test_bound_closed_form_values():
+    assert pins.pin_bound_table(oracle) == 0.0
+
+
+def test_term_bound_is_lagrange_tight():
+    assert pins.pin_term_bound_tight(oracle) == 0.0
+
+
+def test_measured_radius_hand_example():
+    assert pins.pin_measured_radius(oracle) < 1e-15
+
+
+def test_attention_bound_near_tight():
+    assert pins.pin_attention_bound_near_tight(oracle) == 0.0

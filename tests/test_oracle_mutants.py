@@ -292,3 +292,76 @@ def test_centred_pins_pass_on_oracle():
                                  exact_attention=oracle.exact_attention,
                                  MomentSketch=oracle.MomentSketch)
     assert _centred_pins(impl) < 1e-11
+
+
+# Bound mutants -------------------------------------------------------------------------
+
+from oracle import bounds as obd
+
+
+def _bounds_impl(**over):
+    base = dict(taylor_term_bound=obd.taylor_term_bound,
+                kde_relative_bound=obd.kde_relative_bound,
+                attention_abs_bound=obd.attention_abs_bound,
+                measured_radius=obd.measured_radius)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+def _kde_missing_exp(p, rho):
+    """Drops the e^rho that the lower bound Z >= n e^-rho brings in."""
+    return obd.taylor_term_bound(p, rho)
+
+
+def _attention_no_range(p, rho, V):
+    """Drops the per-coordinate range of the values."""
+    V = np.asarray(V, dtype=np.float64)
+    eps1 = obd.taylor_term_bound(p, rho)
+    denom = math.exp(-rho) - eps1
+    if denom <= 0:
+        return np.full(V.shape[1], np.inf)
+    return np.full(V.shape[1], eps1 / denom)
+
+
+def _radius_key_squared(K, Q):
+    """max |k|^2 instead of max |k| * max |q|."""
+    K = np.asarray(K, dtype=np.float64)
+    if K.shape[0] == 0 or np.asarray(Q).shape[0] == 0:
+        return 0.0
+    return float(np.linalg.norm(K, axis=1).max() ** 2)
+
+
+def _radius_paired_rows(K, Q):
+    """max over rows i of |k_i| |q_i| (pairs rows instead of taking each maximum)."""
+    K = np.asarray(K, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    if K.shape[0] == 0 or Q.shape[0] == 0:
+        return 0.0
+    r = min(K.shape[0], Q.shape[0])
+    return float((np.linalg.norm(K[:r], axis=1) * np.linalg.norm(Q[:r], axis=1)).max())
+
+
+def _term_next_factorial(p, rho):
+    """(p+2)! in place of (p+1)!."""
+    return rho ** (p + 1) / math.factorial(p + 2) * math.exp(rho)
+
+
+def _bound_pins(impl):
+    return max(pins.pin_bound_table(impl), pins.pin_term_bound_tight(impl),
+               pins.pin_measured_radius(impl), pins.pin_attention_bound_near_tight(impl))
+
+
+@pytest.mark.parametrize("impl", [
+    _bounds_impl(kde_relative_bound=_kde_missing_exp),
+    _bounds_impl(attention_abs_bound=_attention_no_range),
+    _bounds_impl(measured_radius=_radius_key_squared),
+    _bounds_impl(measured_radius=_radius_paired_rows),
+    _bounds_impl(taylor_term_bound=_term_next_factorial),
+], ids=["kde_missing_exp_rho", "attention_no_range", "radius_key_squared",
+        "radius_paired_rows", "term_next_factorial"])
+def test_bound_mutant_caught(impl):
+    assert _bound_pins(impl) > 1e-6
+
+
+def test_bound_pins_pass_on_oracle():
+    assert _bound_pins(_bounds_impl()) < 1e-15
