@@ -29,8 +29,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", type=int, default=2,
-                    help="workload id 1..5 (default 2: d=16, p=4, 64K keys)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="workload id 1..5 (default 4: 32 heads, d=64, p=2, 128K keys each)")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the chosen workload (no workload-3 sub-object, no "
+                         "per-configuration errors)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--decode-steps", type=int, default=20)
@@ -260,25 +263,12 @@ def counters_pass(w, E, torch, generate, layout="full"):
     return 0
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sketch shards by sub-stream with one sum all-reduce; see the design "
-              "notes)", file=sys.stderr)
-        return 2
+def measure_workload(w, E, torch, K, V, Q, args, full_line=True):
+    """Warm-up and timed steps of workload w (full layout), the per-call update
+    time, the exact path in decode mode and the sketch-vs-exact error.  With
+    full_line, also the multiset layout and the decode step."""
     import numpy as np
-    import torch
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import exp_density_sketching_amd as E
     from exp_density_sketching_amd.workload import ingest
-    from synthetic import WORKLOADS, generate
-
-    w = WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    if args.counters:
-        return counters_pass(w, E, torch, generate, args.layout)
-    K, V, Q = generate(w)
     Kg = torch.from_numpy(K).cuda()
     Vg = torch.from_numpy(V).cuda()
     Qg = torch.from_numpy(Q).cuda()
@@ -342,17 +332,7 @@ def main():
     full = measure("full")
     sketches = full["sketches"]
     ukern = E.UPDATE_KERNELS[E.sketch_update_path(sketches[0])]
-    # the last timed step's sketch answers against its exact answers, and the
-    # truncation bound rho^(p+1)/(p+1)! e^(2 rho), rho = max|q| max|k| per head
-    zs, ze = z_s.cpu().double().numpy(), z_e.cpu().double().numpy()
-    os_, oe = out_s.cpu().double().numpy(), out_e.cpu().double().numpy()
-    rho = max(float(np.linalg.norm(K[hd].astype(np.float64), axis=1).max() *
-                    np.linalg.norm(Q[hd].astype(np.float64), axis=1).max())
-              for hd in range(w.h))
-    sketch_error = {"z_rel_max": float(np.max(np.abs(zs - ze) / ze)),
-                    "o_abs_max": float(np.max(np.abs(os_ - oe))),
-                    "z_rel_bound": rho ** (w.p + 1) / math.factorial(w.p + 1) * math.exp(2 * rho),
-                    "rho": rho}
+    sketch_error = sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e)
     t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
     dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
@@ -377,35 +357,12 @@ def main():
     b.record()
     torch.cuda.synchronize()
     call_dur = a.elapsed_time(b) / 1e3 / len(calls)
+    del view
 
-    # exact path in decode mode (one query per head), streaming the whole KV
-    dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
-    dec_z = torch.empty((w.h, 1), device="cuda")
-    q1 = Qg[:, :1].contiguous()
-    for _ in range(2):
-        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
-    a, b = ev(), ev()
-    a.record()
-    for _ in range(args.decode_steps):
-        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
-    b.record()
-    torch.cuda.synchronize()
-    t_dec = a.elapsed_time(b) / 1e3 / args.decode_steps
-    kv_bytes = 4.0 * w.h * w.n * (w.d + w.dv)
-
-    line = {
-        "metric": METRIC,
+    res = {
         "value": w.h * (w.n + w.m) / t_step,
         "unit": "keys+queries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": t_step * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
         "config": {"workload": w.name, "d": w.d, "dv": w.dv, "p": w.p, "D": w.D,
                    "n": w.n, "m": w.m, "heads": w.h, "chunk": w.chunk,
                    "substreams": w.substreams, "update_calls": n_calls},
@@ -416,6 +373,7 @@ def main():
         "exact_ms": t_ex * 1e3,
         "query_mfma_frac": flop_per_key * w.h * w.m / t_qry / PEAK_FP32_MFMA,
         "query_kernel_mfma_frac": flop_per_key * w.h * w.m / t_qk / PEAK_FP32_MFMA,
+        "query_kernel_us": t_qk * 1e6,
         "update_call_us": call_dur * 1e6,
         "update_call_mfma_frac": flop_per_key * keys_per_call * w.h / call_dur / PEAK_FP32_MFMA,
         "exact_batched": {"ms": t_ex * 1e3, "flop": 2.0 * w.h * w.m * w.n * (w.d + w.dv),
@@ -423,9 +381,7 @@ def main():
                           "mfma_frac": 2.0 * w.h * w.m * w.n * (w.d + w.dv) / t_ex /
                           PEAK_FP32_MFMA,
                           "kernel": exact_batched_kernel(w)},
-        "exact_decode": {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
-                         "kv_bytes": kv_bytes,
-                         "resident": "HBM" if kv_bytes > 256e6 else "cache (<= 256 MB)"},
+        "exact_decode": exact_decode(w, E, torch, Kg, Vg, Qg, args.decode_steps),
         "sketch_error": sketch_error,
         "roofline": {"kernel": ukern, "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
@@ -436,6 +392,8 @@ def main():
     }
     for s_ in sketches:
         s_.destroy()
+    if not full_line:
+        return res
     # the same step with multiset storage of the moments (identical answers,
     # C(d + p, p) rows instead of D); priced at its own algorithmic work
     sym = measure("sym")
@@ -444,7 +402,7 @@ def main():
     rows = math.comb(w.d + w.p, w.p)
     sflop = 2.0 * rows * (1 + w.dv)
     s_ach = sflop * keys_timed / sym["ktime"]
-    line["sym_layout"] = {
+    res["sym_layout"] = {
         "value": w.h * (w.n + w.m) / sym["t_step"],
         "ms_per_step": sym["t_step"] * 1e3,
         "rows": rows,
@@ -460,14 +418,126 @@ def main():
                      "flop_per_launch": sflop * keys_timed / sym["launches"],
                      "launch_us": sym["dur"] * 1e6, "launches": sym["launches"]},
     }
-    line["decode_step"] = decode_steps(w, E, torch, Kg, Vg, Qg, args.decode_steps,
-                                       line["exact_decode"]["us_per_step"])
-    if kv_bytes <= 256e6:
+    res["decode_step"] = decode_steps(w, E, torch, Kg, Vg, Qg, args.decode_steps,
+                                      res["exact_decode"]["us_per_step"])
+    return res
+
+
+def sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e):
+    """The sketch's answers against the exact path's on the same queries, and
+    the truncation bound rho^(p+1)/(p+1)! e^(2 rho), rho = max|q| max|k| per head."""
+    import numpy as np
+    zs, ze = z_s.cpu().double().numpy(), z_e.cpu().double().numpy()
+    os_, oe = out_s.cpu().double().numpy(), out_e.cpu().double().numpy()
+    rho = max(float(np.linalg.norm(K[hd].astype(np.float64), axis=1).max() *
+                    np.linalg.norm(Q[hd].astype(np.float64), axis=1).max())
+              for hd in range(w.h))
+    return {"z_rel_max": float(np.max(np.abs(zs - ze) / ze)),
+            "o_abs_max": float(np.max(np.abs(os_ - oe))),
+            "z_rel_bound": rho ** (w.p + 1) / math.factorial(w.p + 1) * math.exp(2 * rho),
+            "rho": rho}
+
+
+def exact_decode(w, E, torch, Kg, Vg, Qg, steps):
+    """The exact path in decode mode (one query per head), streaming the whole KV:
+    algorithmic bytes (d + dv) * 4 per key / time per call."""
+    dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
+    dec_z = torch.empty((w.h, 1), device="cuda")
+    q1 = Qg[:, :1].contiguous()
+    for _ in range(2):
+        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
+    b.record()
+    torch.cuda.synchronize()
+    t_dec = a.elapsed_time(b) / 1e3 / steps
+    kv_bytes = 4.0 * w.h * w.n * (w.d + w.dv)
+    hbm = kv_bytes > 256e6
+    return {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
+            "kv_bytes": kv_bytes,
+            "frac_of_hbm_peak": kv_bytes / t_dec / PEAK_HBM if hbm else None,
+            "resident": "HBM" if hbm else "cache (<= 256 MB): effective GB/s"}
+
+
+def error_of_config(w, E, torch, generate, decode_steps_n):
+    """One pass of workload w as the bench runs it (ingest, query, exact path):
+    the sketch-vs-exact error and the exact decode rate."""
+    from exp_density_sketching_amd.workload import run_sketch
+    K, V, Q = generate(w)
+    Kg, Vg, Qg = (torch.from_numpy(a).cuda() for a in (K, V, Q))
+    out_s, z_s, sk = run_sketch(w, Kg, Vg, Qg)
+    out_e, z_e = E.exact_attend(Kg, Vg, Qg)
+    torch.cuda.synchronize()
+    sk.destroy()
+    r = {"sketch_error": sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e),
+         "exact_decode": exact_decode(w, E, torch, Kg, Vg, Qg, decode_steps_n)}
+    del Kg, Vg, Qg
+    torch.cuda.empty_cache()
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sketch shards by sub-stream with one sum all-reduce; see the design "
+              "notes)", file=sys.stderr)
+        return 2
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import exp_density_sketching_amd as E
+    from synthetic import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    if args.counters:
+        return counters_pass(w, E, torch, generate, args.layout)
+    print(f"bench: workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    K, V, Q = generate(w)
+    res = measure_workload(w, E, torch, K, V, Q, args, full_line=True)
+    line = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": res.pop("config")}
+    line.update(res)
+    print(f"bench: workload {w.name} measured", file=sys.stderr, flush=True)
+    if line["exact_decode"]["resident"] != "HBM":
         # this workload's KV stays in the Infinity Cache: the exact path's HBM
         # figure comes from the 32-head workload's decode
         line["exact_decode_hbm"] = exact_decode_hbm(WORKLOADS[4], E, torch, args.decode_steps)
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, K, V, Q, args.cpu_seconds)
+    del K, V, Q
+    if not args.quick:
+        # the largest update (workload 3: 1M keys, 2.34 TFLOP, four sub-streams
+        # merged) with its own roofline and CPU baseline
+        w3 = WORKLOADS[3]
+        if w3.ident != w.ident:
+            print(f"bench: workload {w3.name}", file=sys.stderr, flush=True)
+            K3, V3, Q3 = generate(w3)
+            sub = measure_workload(w3, E, torch, K3, V3, Q3, args, full_line=False)
+            if args.cpu_seconds > 0:
+                sub["cpu_baseline"] = cpu_baseline(w3, K3, V3, Q3, args.cpu_seconds)
+            line["workload3"] = sub
+            del K3, V3, Q3
+            torch.cuda.empty_cache()
+        # the sketch-vs-exact error and the exact decode rate of every configuration
+        errs = {}
+        for i in sorted(WORKLOADS):
+            wi = WORKLOADS[i]
+            if wi.ident == w.ident:
+                r = {"sketch_error": line["sketch_error"], "exact_decode": line["exact_decode"]}
+            elif "workload3" in line and wi.ident == 3:
+                r = {"sketch_error": line["workload3"]["sketch_error"],
+                     "exact_decode": line["workload3"]["exact_decode"]}
+            else:
+                print(f"bench: error of {wi.name}", file=sys.stderr, flush=True)
+                r = error_of_config(wi, E, torch, generate, args.decode_steps)
+            errs[wi.name] = r
+        line["by_config"] = errs
     print(json.dumps(line), flush=True)
     return 0
 

@@ -21,7 +21,7 @@ EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_update
             "sketch_destroy",
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
             "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
-            "exact_attend",
+            "exact_attend", "exact_release_workspaces",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
 
@@ -62,6 +62,7 @@ def _lib():
             "sketch_set_staging": (c_int, [vp, c_i64]),
             "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
                                      vp, vp]),
+            "exact_release_workspaces": (c_int, []),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
                                      ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
             "sketch_export": (c_int, [vp, vp]),
@@ -206,7 +207,7 @@ def sketch_update(s, K, V):
 
 
 def sketch_merge(dst, src):
-    _check(_lib().sketch_merge(dst._handle(), src._h), "sketch_merge")
+    _check(_lib().sketch_merge(dst._handle(), src._handle()), "sketch_merge")
 
 
 def sketch_query(s, Q, out=None, Z=None):
@@ -319,6 +320,11 @@ def exact_attend(K, V, Q, out=None, Z=None):
                                _dev(Q, "Q", 3), m, _dev(out, "out", 3), _dev(Z, "Z", 2),
                                _stream()), "exact_attend")
     return (out[0], Z[0]) if squeeze else (out, Z)
+
+
+def exact_release_workspaces():
+    """Free the partials buffers exact_attend keeps per (device, stream)."""
+    _check(_lib().exact_release_workspaces(), "exact_release_workspaces")
 
 
 def raw():

@@ -296,9 +296,39 @@ void free_workspace(Workspace* ws) {
   *ws = Workspace{};
 }
 
-// exact_attend's kept partials, per (device, stream)
+// exact_attend's kept partials, per (device, stream): at most kMaxXws buffers;
+// a new (device, stream) pair beyond that takes the place of the one used least
+// recently, once that buffer's last use has finished
+constexpr size_t kMaxXws = 8;
+struct XwsEntry {
+  Workspace ws;
+  unsigned long long last_use = 0;
+};
 std::mutex g_xws_mutex;
-std::map<std::pair<int, void*>, Workspace> g_xws;
+std::map<std::pair<int, void*>, XwsEntry> g_xws;
+unsigned long long g_xws_clock = 0;
+
+// The kept partials buffer of (dev, stream); the caller holds g_xws_mutex.
+Workspace* xws_for(int dev, void* stream) {
+  const auto key = std::make_pair(dev, stream);
+  auto it = g_xws.find(key);
+  if (it == g_xws.end()) {
+    if (g_xws.size() >= kMaxXws) {
+      auto old = g_xws.begin();
+      for (auto i = g_xws.begin(); i != g_xws.end(); ++i)
+        if (i->second.last_use < old->second.last_use) old = i;
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      if (old->first.first != cur) (void)hipSetDevice(old->first.first);
+      free_workspace(&old->second.ws);          // waits for its last use
+      if (old->first.first != cur) (void)hipSetDevice(cur);
+      g_xws.erase(old);
+    }
+    it = g_xws.emplace(key, XwsEntry{}).first;
+  }
+  it->second.last_use = ++g_xws_clock;
+  return &it->second.ws;
+}
 
 }  // namespace
 
@@ -352,7 +382,8 @@ struct sk_sketch {
   int pcur = 0;                            // buffer the next call writes
   float* pend = nullptr;                   // partials not yet in the state
   int pend_ns = 0;
-  hipEvent_t flush_ev = nullptr;           // orders a flush before another stream
+  hipEvent_t flush_ev = nullptr;           // orders the two streams around a merge
+  hipEvent_t switch_ev = nullptr;          // orders a stream change (sketch_set_stream)
   // staging of small update calls: their keys and values are copied here and
   // contracted in one launch when the buffer fills or the state is needed
   float* stage_k = nullptr;                // [h][stage_cap][d]
@@ -500,7 +531,10 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
     const double cols = std::pow((double)d, tt) * C;
     if (cols >= query_min_cols() || (tt == 0 && 2 * C >= SK_TNQ)) { t = tt; break; }
   }
+  // both sides of the split hold at most SK_MAXDIG digits: the kernel forms
+  // q^(x)s from that many (p <= 16 keeps j - SK_MAXDIG <= t <= SK_MAXDIG feasible)
   while (t > SK_MAXDIG) --t;
+  if (t < j - SK_MAXDIG) t = j - SK_MAXDIG;
   const int sd = j - t;
   const long long N = (long long)std::llround(std::pow((double)d, t)) * C;
   const long long Kr = (long long)std::llround(std::pow((double)d, sd));
@@ -1049,6 +1083,7 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->stage_k);
   (void)hipFree(s->stage_v);
   if (s->flush_ev != nullptr) (void)hipEventDestroy(s->flush_ev);
+  if (s->switch_ev != nullptr) (void)hipEventDestroy(s->switch_ev);
   free_workspace(&s->qws);
   (void)hipFree(s->view);
   for (int k = 0; k < 3; ++k)
@@ -1060,7 +1095,16 @@ int sketch_destroy(sk_handle s) {
 
 int sketch_set_stream(sk_handle s, void* hip_stream) {
   if (s == nullptr) return SK_EINVAL;
-  s->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const hipStream_t ns = reinterpret_cast<hipStream_t>(hip_stream);
+  if (ns == s->stream) return SK_OK;
+  // the handle's buffers (state, staged keys, pending partials, query partials)
+  // are ordered by its stream alone: the new stream first waits for everything
+  // issued so far on the old one
+  if (s->switch_ev == nullptr)
+    SK_TRY(hipEventCreateWithFlags(&s->switch_ev, hipEventDisableTiming));
+  SK_TRY(hipEventRecord(s->switch_ev, s->stream));
+  SK_TRY(hipStreamWaitEvent(ns, s->switch_ev, 0));
+  s->stream = ns;
   return SK_OK;
 }
 
@@ -1322,10 +1366,9 @@ int sketch_merge(sk_handle dst, sk_handle src) {
       dst->layout != src->layout || dst->center_host != src->center_host)
     return SK_EMISMATCH;
   // src's pending partials go into its state on src's stream; dst's stream then
-  // waits for that before reading it
-  const bool src_pending = src->pend != nullptr || src->stage_n > 0;
+  // waits for everything issued on src's stream before reading its state
   int rc = settle(src);
-  if (rc == SK_OK && src_pending && src->stream != dst->stream) {
+  if (rc == SK_OK && src->stream != dst->stream) {
     if (src->flush_ev == nullptr)
       SK_TRY(hipEventCreateWithFlags(&src->flush_ev, hipEventDisableTiming));
     SK_TRY(hipEventRecord(src->flush_ev, src->stream));
@@ -1339,6 +1382,11 @@ int sketch_merge(sk_handle dst, sk_handle src) {
                      reinterpret_cast<float4*>(dst->state),
                      reinterpret_cast<const float4*>(src->state), c4);
   SK_TRY(hipGetLastError());
+  if (src->stream != dst->stream) {
+    // src's later writes wait until the add has read its state
+    SK_TRY(hipEventRecord(src->flush_ev, dst->stream));
+    SK_TRY(hipStreamWaitEvent(src->stream, src->flush_ev, 0));
+  }
   dst->count += src->count;
   return SK_OK;
 }
@@ -1527,8 +1575,14 @@ int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* col
   return SK_OK;
 }
 
-int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
-                 const float* Q, int64_t m, float* out, float* Z, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The exact path: the partials live in the kept per-(device, stream) buffer (or
+// a stream-ordered allocation).
+int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
+              const float* Q, int64_t m, float* out, float* Z, void* hip_stream) {
   if (!is_pow2_in(d, 4, 128) || !is_pow2_in(dv, 4, 128) || h < 1 || n < 0 || m < 0)
     return SK_EINVAL;
   if (m == 0) return SK_OK;
@@ -1588,10 +1642,10 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   // buffer's last use: a destroyed stream's handle value can come back as a new
   // stream while the old one's kernels run.
   std::lock_guard<std::mutex> ws_lock(g_xws_mutex);
-  Workspace& ws = g_xws[std::make_pair(dev, reinterpret_cast<void*>(st))];
+  Workspace* ws = xws_for(dev, reinterpret_cast<void*>(st));
   float* parts = nullptr;
   bool own = false;
-  rc = take_workspace(&ws, pbytes, st, false, &parts, &own);
+  rc = take_workspace(ws, pbytes, st, false, &parts, &own);
   if (rc != SK_OK) return rc;
   const long long nn = n;
   const long long mm = m;
@@ -1666,8 +1720,30 @@ int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
-  release_workspace(&ws, parts, own, st);
+  release_workspace(ws, parts, own, st);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
+  return SK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
+                 const float* Q, int64_t m, float* out, float* Z, void* hip_stream) {
+  return exact_run(K, V, n, d, dv, h, Q, m, out, Z, hip_stream);
+}
+
+int exact_release_workspaces(void) {
+  std::lock_guard<std::mutex> ws_lock(g_xws_mutex);
+  int cur = 0;
+  SK_TRY(hipGetDevice(&cur));
+  for (auto& kv : g_xws) {
+    if (kv.first.first != cur) (void)hipSetDevice(kv.first.first);
+    free_workspace(&kv.second.ws);              // waits for its last use
+  }
+  g_xws.clear();
+  SK_TRY(hipSetDevice(cur));
   return SK_OK;
 }
 

@@ -128,8 +128,12 @@ int sketch_set_center(sk_handle s, const float* c);
  * had failed (the memory is still freed). */
 int sketch_destroy(sk_handle s);
 
-/* sketch_set_stream -- issue later calls of this handle on another stream.  The
- * caller orders the two streams if work is still pending on the old one. */
+/* sketch_set_stream -- issue later calls of this handle on another stream.  When
+ * the stream changes, the library records an event on the old stream and makes
+ * the new one wait for it, so work issued later on the handle runs after
+ * everything issued before the change (the handle's own buffers are ordered by
+ * its stream alone).  Setting the current stream again costs nothing.
+ * Errors: SK_EINVAL (NULL handle), SK_EHIP. */
 int sketch_set_stream(sk_handle s, void* hip_stream);
 
 /* sketch_reset -- back to the empty sketch (all moments zero, count 0). */
@@ -164,8 +168,8 @@ int sketch_set_staging(sk_handle s, int64_t keys);
 /*
  * sketch_merge -- dst += src (Merge-and-Reduce, merge step: moments add, counts
  * add).  src is unchanged.  Both handles must have equal (d, dv, p, h), the
- * same layout and the same centre; the work
- * runs on dst's stream (the caller orders src's stream before it).
+ * same layout and the same centre; the work runs on dst's stream, which first
+ * waits for everything issued so far on src's stream when the two differ.
  * Errors: SK_EINVAL (NULL, dst == src), SK_EMISMATCH, SK_EHIP.
  */
 int sketch_merge(sk_handle dst, sk_handle src);
@@ -207,18 +211,33 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
  * pair):  Z[h][q] = sum_i exp(<q, k_i>),  out[h][q] = sum_i exp(<q,k_i>) v_i / Z.
  * Computed with a running maximum (online softmax) over key slices and a
  * fixed-order combine of the slices.  n == 0 gives Z = 0, out = NaN.
+ * Range: out is formed relative to the running maximum and stays finite for any
+ * finite scores; Z is returned as a plain fp32 sum e^mu * l (mu the largest
+ * score), so it overflows to +inf once ln Z exceeds about 88.7 (ln of the
+ * largest fp32), e.g. a largest score of 80 with more than e^8.7 ~ 6000 keys at
+ * that score.
  *   K [h][n][d], V [h][n][dv], Q [h][m][d], out [h][m][dv], Z [h][m]: device.
  *   hip_stream: hipStream_t to run on (NULL = default stream).
  * The per-slice partials (h * m * slices * (2 + dv) floats) live in a buffer
- * the library keeps per (device, stream) until the process ends, grown on
- * demand up to 256 MB; larger ones are taken from the stream-ordered allocator
- * (hipMallocAsync) for the call.  Calls from several host threads are
- * serialised while they enqueue their kernels.
+ * the library keeps per (device, stream), grown on demand up to 256 MB; larger
+ * ones are taken from the stream-ordered allocator (hipMallocAsync) for the
+ * call.  At most 8 such buffers are kept: a call on a ninth (device, stream)
+ * frees the one used least recently, after waiting for its last use.  Calls
+ * from several host threads are serialised while they enqueue their kernels.
  * Errors: SK_EINVAL (shapes, NULL/misaligned pointers, n or m < 0), SK_ENOMEM,
  * SK_EHIP.
  */
 int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
                  const float* Q, int64_t m, float* out, float* Z, void* hip_stream);
+
+/*
+ * exact_release_workspaces -- frees every partials buffer exact_attend keeps
+ * (waiting on the host for each buffer's last use first).  Later calls allocate
+ * again.  For a caller that wants the memory back, e.g. before its streams are
+ * destroyed.
+ * Errors: SK_EHIP.
+ */
+int exact_release_workspaces(void);
 
 /*
  * sketch_state -- a read-only view of the moments in the canonical layout

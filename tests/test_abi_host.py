@@ -122,3 +122,4 @@ def test_product_path_has_no_oracle_or_fallback():
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
             assert "numpy" not in src or fn == "build.py", fn
+

@@ -369,3 +369,14 @@ def test_update_path(d, layout, want):
         assert E.sketch_update_path(s) == want
     finally:
         s.destroy()
+
+
+# Levels of nine or more digits: the query's split keeps at most eight digits on
+# its row side and folds the rest in the epilogue (d = 4 with wide value rows, so
+# the plain split would put every digit on the row side).
+@pytest.mark.parametrize("d,dv,p", [(4, 64, 9), (4, 32, 10), (4, 8, 11), (4, 4, 12)])
+def test_deep_levels(d, dv, p):
+    w = WORKLOADS[1].scaled(n=333, m=45)
+    w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.9})
+    K, V, Q = generate(w)
+    _check_sketch(w, K, V, Q, label=f"deep d={d} dv={dv} p={p}")
