@@ -36,6 +36,13 @@ repository's design notes):
   -> ``sym.SymMomentSketch``.
 * ``bounds``: the Lagrange form of the Taylor remainder, carried through the sums
   (derived here; the pages state only asymptotic space bounds).
+* ``coreset``: the tail of the expansion, e^x - T_p(x), answered from a weighted
+  subset of the stream kept by Merge-and-Reduce, each reduce a discrepancy
+  halving (the self-balancing walk of Alweiss, Liu and Sawhney on consecutive
+  pairs); same section, pillar "Construções de Coreset Baseadas em Discrepância"
+  and the closing Merge-and-Reduce paragraph.  The pages name results, not a
+  procedure; the readings are in the module header.
+  -> ``coreset.MergeReduceCoreset``, ``coreset.halve``, ``coreset.tail_exp``.
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against brute
 force on tiny inputs, closed forms, identities and library routines (see the
@@ -48,9 +55,10 @@ from .sketch import (taylor_exp, sketch_direct, sketch_direct_centered, MomentSk
 from .sym import SymMomentSketch, multisets, alpha_factorial, sym_features
 from .bounds import (taylor_term_bound, kde_relative_bound, attention_abs_bound,
                      measured_radius)
+from . import coreset
 
 __all__ = ["exact_attention", "taylor_exp", "sketch_direct", "sketch_direct_centered",
            "MomentSketch",
            "feature_map", "SymMomentSketch", "multisets", "alpha_factorial",
            "sym_features", "taylor_term_bound", "kde_relative_bound",
-           "attention_abs_bound", "measured_radius"]
+           "attention_abs_bound", "measured_radius", "coreset"]

@@ -545,3 +545,232 @@ def pin_attention_bound_near_tight(impl):
                 best = max(best, obs / bound)
             worst = max(worst, best - 1.0, 0.45 - best)
     return max(0.0, worst)
+
+
+# Tail coreset (oracle/coreset.py) -------------------------------------------------------
+#
+# ``impl`` here has the attributes tail_exp, halve, uniforms, splitmix64,
+# MergeReduceCoreset, tail_direct and answer_with_tail (the oracle.coreset module).
+
+def pin_tail_exp_mpmath(impl):
+    """R_p(x) against 120-digit mpmath on a grid (relative error, with an absolute
+    floor of 1e-300 for R_p(0) = 0); 120 digits survive the cancellation of
+    e^x - T_p(x) at x = 1e-4, p = 8 (about 42 digits)."""
+    mpmath.mp.dps = 120
+    worst = 0.0
+    xs = np.concatenate([np.linspace(-12.0, 12.0, 97),
+                         [-1e-3, 1e-4, 0.0, 15.0, -14.0, 30.0, -30.0]])
+    for p in range(0, 9):
+        got = impl.tail_exp(xs, p)
+        for x, g in zip(xs, got):
+            xm = mpmath.mpf(float(x))
+            want = mpmath.exp(xm) - mpmath.fsum(xm ** j / mpmath.factorial(j)
+                                                 for j in range(p + 1))
+            w = float(want)
+            worst = max(worst, abs(g - w) / max(abs(w), 1e-300))
+    mpmath.mp.dps = 15
+    return worst
+
+
+def _tail_features(k, p, J):
+    """phi_t(k) = (k^(x)j / sqrt(j!))_{p < j <= J}, built with np.kron."""
+    return np.concatenate([kron_power(k, j) / math.sqrt(math.factorial(j))
+                           for j in range(p + 1, J + 1)])
+
+
+def _unit_vec(k, v, p, J):
+    """u(x) = phi_t(k) (x) [1; v] as an explicit vector."""
+    return np.kron(_tail_features(k, p, J), np.concatenate([[1.0], v]))
+
+
+def pin_coreset_explicit_walk(impl, p=1, n=16, d=2, dv=1, seed=41, J=16):
+    """The walk with explicit feature vectors (no kernel trick): alpha_t = <psi,
+    f_t> and the kept points must match impl.halve; the discrepancy identity
+    sum(all u) - 2 sum(kept u) = psi must hold; and the tail sums of every query
+    must obey tail(all) - 2 tail(kept) = <psi, phi_t(q) (x) e>.  Keys of norm
+    <= 0.6, so the explicit series cut at J = 16 is exact to ~1e-17."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((n, d))
+    K *= 0.6 * rng.uniform(0.2, 1.0, (n, 1)) / np.linalg.norm(K, axis=1, keepdims=True)
+    V = rng.standard_normal((n, dv))
+    U = rng.uniform(0.0, 1.0, n // 2)
+    c0 = 0.7
+    r = impl.halve(K, V, p, c0, U)
+    u = np.array([_unit_vec(K[i], V[i], p, J) for i in range(n)])
+    f = u[0::2] - u[1::2]
+    c = c0 * max(float(fi @ fi) for fi in f)
+    psi = np.zeros(u.shape[1])
+    alpha, kept = [], []
+    for t in range(n // 2):
+        a = float(psi @ f[t])
+        alpha.append(a)
+        pt = min(1.0, max(0.0, 0.5 * (1.0 - a / c)))
+        e = 1.0 if U[t] < pt else -1.0
+        psi += e * f[t]
+        kept.append(2 * t + 1 if e > 0 else 2 * t)
+    scale = max(1.0, float(np.abs(alpha).max()))
+    err = [float(np.abs(np.asarray(alpha) - r["alpha"]).max()) / scale,
+           abs(c - r["c"]) / c,
+           float(np.any(np.asarray(kept) != r["kept"]))]
+    disc = u.sum(axis=0) - 2.0 * u[kept].sum(axis=0)
+    err.append(float(np.abs(disc - psi).max()) / max(1.0, float(np.abs(psi).max())))
+    # tail sums of a few queries through the kept set against <psi, phi(q) (x) e>
+    Q = rng.standard_normal((4, d)) * 0.5
+    n_all, z_all = impl.tail_direct(K, V, Q, p)
+    n_kept, z_kept = impl.tail_direct(K[kept], V[kept], Q, p)
+    for qi in range(Q.shape[0]):
+        phq = _tail_features(Q[qi], p, J)
+        for comp in range(1 + dv):
+            e_c = np.zeros(1 + dv)
+            e_c[comp] = 1.0
+            lhs = (z_all[qi] - 2 * z_kept[qi]) if comp == 0 else \
+                (n_all[qi, comp - 1] - 2 * n_kept[qi, comp - 1])
+            rhs = float(psi @ np.kron(phq, e_c))
+            err.append(abs(lhs - rhs) / max(1e-3, abs(rhs)))
+    return max(err)
+
+
+def pin_splitmix64_known_answers(impl):
+    """The first outputs of SplitMix64 from state 0, as printed by its published
+    reference implementation (Vigna's splitmix64.c, after Steele, Lea and Flood)."""
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    got = [int(x) for x in impl.splitmix64(0, np.arange(4))]
+    return float(sum(g != w for g, w in zip(got, want)))
+
+
+def pin_coreset_no_reduce_is_exact(impl, p=3, seed=42):
+    """A block larger than the stream: no reduce happens, the coreset is the stream
+    itself (weight 1), and head (plain Taylor sums) + tail = the exact answer,
+    checked against scipy's softmax and logsumexp."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((300, 4)) * 0.4
+    V = rng.standard_normal((300, 3))
+    Q = rng.standard_normal((7, 4)) * 0.4
+    cs = impl.MergeReduceCoreset(4, 3, p, 512, 1.0, 5).update(K[:100], V[:100]).update(
+        K[100:], V[100:])
+    tN, tZ = cs.tail_query(Q)
+    S = Q @ K.T
+    Th = sum(S ** j / math.factorial(j) for j in range(p + 1))
+    o, Z = impl.answer_with_tail((Th @ V) / Th.sum(1)[:, None], Th.sum(1), tN, tZ)
+    Zref = np.exp(scipy.special.logsumexp(S, axis=1))
+    oref = scipy.special.softmax(S, axis=1) @ V
+    return max(relmax(Z, Zref), absmax(o, oref))
+
+
+def pin_coreset_fair_coin(impl, seed=43):
+    """c0 huge: every probability is 1/2, so eps_t = +1 exactly when U_t < 1/2."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((40, 3)) * 0.5
+    V = rng.standard_normal((40, 2))
+    U = rng.uniform(0, 1, 20)
+    r = impl.halve(K, V, 2, 1e300, U)
+    want = np.where(U < 0.5, 1.0, -1.0)
+    return float(np.any(r["eps"] != want))
+
+
+def pin_coreset_identical_pairs(impl, seed=44):
+    """Both points of every pair equal: f_t = 0, so the halved set answers every
+    query exactly (twice the kept tail sums = the tail sums of all points)."""
+    rng = np.random.default_rng(seed)
+    K = np.repeat(rng.standard_normal((25, 3)) * 0.6, 2, axis=0)
+    V = np.repeat(rng.standard_normal((25, 2)), 2, axis=0)
+    Q = rng.standard_normal((5, 3)) * 0.6
+    r = impl.halve(K, V, 1, 0.5, rng.uniform(0, 1, 25))
+    n_all, z_all = impl.tail_direct(K, V, Q, 1)
+    n_k, z_k = impl.tail_direct(K[r["kept"]], V[r["kept"]], Q, 1)
+    return max(relmax(2 * z_k, z_all), absmax(2 * n_k, n_all) / np.abs(n_all).max())
+
+
+def pin_coreset_levels(impl, B=16, seed=45):
+    """Merge-and-Reduce as a binary counter: after n points, level l holds a block
+    exactly when bit l of floor(n / B) is set, the buffer holds n mod B points, the
+    weights add up to n, and every kept point is one of the input rows."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((1000, 2)) * 0.5
+    V = rng.standard_normal((1000, 2))
+    cs = impl.MergeReduceCoreset(2, 2, 2, B, 1.0, 9)
+    bad = 0.0
+    rows = {tuple(np.r_[K[i], V[i]]) for i in range(1000)}
+    pos = 0
+    for step in (1, 7, 16, 33, 100, 250, 593):
+        cs.update(K[pos:pos + step], V[pos:pos + step])
+        pos += step
+        blocks = pos // B
+        for l, blk in enumerate(cs.levels):
+            bad += float((blk is not None) != bool((blocks >> l) & 1))
+        bad += float(blocks >> len(cs.levels) != 0)
+        Kp, Vp, w = cs.points()
+        bad += float(Kp.shape[0] != pos % B + B * bin(blocks).count("1"))
+        bad += abs(float(w.sum()) - pos)
+        bad += float(sum(tuple(np.r_[Kp[i], Vp[i]]) not in rows for i in range(Kp.shape[0])))
+    return bad
+
+
+def pin_coreset_beats_random(impl, trials=12, B=64, seed=46):
+    """The walk's halving errs less than a fair-coin halving of the same pairs:
+    over random queries, the RMS error of the tail sums (2 x kept against all; the
+    normaliser and the numerator) must stay below 0.7 of the fair coin's, pooled
+    over the trials (measured: 0.40 and 0.56 at c0 = 0.25; a reversed drift does
+    worse than the coin)."""
+    rng = np.random.default_rng(seed)
+    walk, coin, walkn, coinn = [], [], [], []
+    for _ in range(trials):
+        K = rng.standard_normal((2 * B, 4))
+        K *= 1.0 / np.linalg.norm(K, axis=1, keepdims=True)
+        V = rng.uniform(-1, 1, (2 * B, 2))
+        Q = rng.standard_normal((32, 4))
+        Q *= 1.0 / np.linalg.norm(Q, axis=1, keepdims=True)
+        U = rng.uniform(0, 1, B)
+        n_all, z_all = impl.tail_direct(K, V, Q, 1)
+        r = impl.halve(K, V, 1, 0.25, U)
+        nw, zw = impl.tail_direct(K[r["kept"]], V[r["kept"]], Q, 1)
+        coin_kept = np.arange(0, 2 * B, 2) + (U < 0.5)
+        nc, zc = impl.tail_direct(K[coin_kept], V[coin_kept], Q, 1)
+        walk.append(2 * zw - z_all)
+        coin.append(2 * zc - z_all)
+        walkn.append(2 * nw - n_all)
+        coinn.append(2 * nc - n_all)
+    rms = lambda a: float(np.sqrt(np.mean(np.square(a))))
+    ratio = max(rms(walk) / rms(coin), rms(walkn) / rms(coinn))
+    return max(0.0, ratio - 0.7)
+
+
+def pin_coreset_merge(impl, B=16, seed=47):
+    """Merge of two sub-stream coresets.  (1) Into an empty coreset: the same
+    points, no reduce.  (2) Blocks on different levels and empty buffers (3B and 4B
+    points): the union, no reduce, so the tail sums add exactly.  (3) Any counts:
+    the result is a binary-counter state of n1 + n2 points (level l occupied
+    exactly when bit l of floor((n1 + n2) / B) is set, (n1 + n2) mod B buffered,
+    weights adding up to n1 + n2)."""
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((600, 3)) * 0.5
+    V = rng.standard_normal((600, 2))
+    Q = rng.standard_normal((5, 3)) * 0.5
+    mk = lambda: impl.MergeReduceCoreset(3, 2, 2, B, 0.25, 3)
+    bad = 0.0
+    src = mk().update(K[:100], V[:100])
+    dst = mk().merge(src)
+    a, b = dst.points(), src.points()
+    bad += float(dst.serial != 0) + sum(float(x.shape != y.shape or np.any(x != y))
+                                        for x, y in zip(a, b))
+    d1 = mk().update(K[:3 * B], V[:3 * B])
+    d2 = mk().update(K[3 * B:7 * B], V[3 * B:7 * B])
+    n1, z1 = d1.tail_query(Q)
+    n2, z2 = d2.tail_query(Q)
+    serial = d1.serial
+    d1.merge(d2)
+    n12, z12 = d1.tail_query(Q)
+    bad += float(d1.serial != serial)
+    bad += relmax(z12, z1 + z2) + absmax(n12, n1 + n2)
+    for c1, c2 in ((5 * B + 3, 3 * B + 7), (B - 1, B - 2), (9 * B + 11, 7 * B + 9)):
+        x = mk().update(K[:c1], V[:c1])
+        y = mk().update(K[c1:c1 + c2], V[c1:c1 + c2])
+        x.merge(y)
+        tot = c1 + c2
+        blocks = tot // B
+        for l, blk in enumerate(x.levels):
+            bad += float((blk is not None) != bool((blocks >> l) & 1))
+        Kp, _, w = x.points()
+        bad += float(x.fillK.shape[0] != tot % B) + abs(float(w.sum()) - tot)
+        bad += float(x.count != tot)
+    return bad

@@ -365,3 +365,96 @@ def test_bound_mutant_caught(impl):
 
 def test_bound_pins_pass_on_oracle():
     assert _bound_pins(_bounds_impl()) < 1e-15
+
+
+# Tail coreset mutants ------------------------------------------------------------------
+
+from oracle import coreset as ocs
+
+
+def _cs_impl(**over):
+    base = dict(tail_exp=ocs.tail_exp, halve=ocs.halve, uniforms=ocs.uniforms,
+                splitmix64=ocs.splitmix64, MergeReduceCoreset=ocs.MergeReduceCoreset,
+                tail_direct=ocs.tail_direct, answer_with_tail=ocs.answer_with_tail)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+def _halve_variant(keep_flip=False, reverse=False, mean_c=False, no_values=False):
+    def halve(K, V, p, c0, U):
+        K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64)
+        B = K.shape[0] // 2
+        G = ocs.tail_exp(K @ K.T, p) * (1.0 if no_values else (1.0 + V @ V.T))
+        a = np.arange(0, 2 * B, 2)
+        b = a + 1
+        D = G[np.ix_(a, a)] - G[np.ix_(a, b)] - G[np.ix_(b, a)] + G[np.ix_(b, b)]
+        c = c0 * float(np.mean(np.diag(D)) if mean_c else np.max(np.diag(D)))
+        run = np.zeros(B)
+        alpha, eps = np.zeros(B), np.zeros(B)
+        for t in range(B):
+            alpha[t] = run[t]
+            x = -run[t] if reverse else run[t]
+            pt = min(1.0, max(0.0, 0.5 * (1.0 - x / c)))
+            e = 1.0 if U[t] < pt else -1.0
+            eps[t] = e
+            run += e * D[t]
+        kept = np.where((eps < 0) if keep_flip else (eps > 0), b, a)
+        return {"kept": kept, "eps": eps, "alpha": alpha, "c": c, "D": D}
+    return halve
+
+
+def _tail_next_degree(x, p):
+    return ocs.tail_exp(x, p + 1)
+
+
+class _NoDoubling(ocs.MergeReduceCoreset):
+    """Keeps weight 1 on every level."""
+
+    def points(self):
+        K, V, w = super().points()
+        return K, V, np.ones_like(w)
+
+
+class _MergeAtLevelZero(ocs.MergeReduceCoreset):
+    """Carries every block of the other coreset in at level 0."""
+
+    def merge(self, other):
+        self._append(other.fillK, other.fillV)
+        for blk in other.levels:
+            if blk is not None:
+                self._carry(blk[0], blk[1], 0)
+        self.count += other.count
+        return self
+
+
+def _cs_pins(impl):
+    with np.errstate(all="ignore"):
+        return max(pins.pin_tail_exp_mpmath(impl),
+                   pins.pin_coreset_explicit_walk(impl, p=1),
+                   pins.pin_coreset_explicit_walk(impl, p=0, seed=40),
+                   pins.pin_splitmix64_known_answers(impl),
+                   pins.pin_coreset_no_reduce_is_exact(impl),
+                   pins.pin_coreset_fair_coin(impl),
+                   pins.pin_coreset_identical_pairs(impl),
+                   pins.pin_coreset_levels(impl),
+                   pins.pin_coreset_beats_random(impl),
+                   pins.pin_coreset_merge(impl))
+
+
+@pytest.mark.parametrize("impl", [
+    _cs_impl(halve=_halve_variant(keep_flip=True)),
+    _cs_impl(halve=_halve_variant(reverse=True)),
+    _cs_impl(halve=_halve_variant(mean_c=True)),
+    _cs_impl(halve=_halve_variant(no_values=True)),
+    _cs_impl(tail_exp=_tail_next_degree),
+    _cs_impl(MergeReduceCoreset=_NoDoubling),
+    _cs_impl(MergeReduceCoreset=_MergeAtLevelZero),
+], ids=["kept_flipped", "drift_reversed", "threshold_from_mean", "values_dropped",
+        "tail_next_degree", "weights_not_doubled", "merge_at_level_zero"])
+def test_coreset_mutant_caught(impl):
+    assert _cs_pins(impl) > 1e-6
+
+
+def test_coreset_pins_pass_on_oracle():
+    assert _cs_pins(_cs_impl()) < 1e-10
