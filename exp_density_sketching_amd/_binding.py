@@ -14,14 +14,14 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libexpsketch.so")
 
-SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP = 0, -1, -2, -3, -4
+SK_OK, SK_EINVAL, SK_ENOMEM, SK_EMISMATCH, SK_EHIP, SK_ESCRATCH = 0, -1, -2, -3, -4, -5
 LAYOUTS = {"full": 0, "sym": 1}
 
 EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_update_path",
             "sketch_destroy",
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
             "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
-            "exact_attend", "exact_release_workspaces",
+            "exact_attend", "exact_attend_noalloc", "exact_release_workspaces",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version")
 
@@ -62,6 +62,8 @@ def _lib():
             "sketch_set_staging": (c_int, [vp, c_i64]),
             "exact_attend": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64, vp,
                                      vp, vp]),
+            "exact_attend_noalloc": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64,
+                                             vp, vp, vp]),
             "exact_release_workspaces": (c_int, []),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
                                      ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
@@ -320,6 +322,22 @@ def exact_attend(K, V, Q, out=None, Z=None):
                                _dev(Q, "Q", 3), m, _dev(out, "out", 3), _dev(Z, "Z", 2),
                                _stream()), "exact_attend")
     return (out[0], Z[0]) if squeeze else (out, Z)
+
+
+def exact_attend_noalloc(K, V, Q, out, Z):
+    """exact_attend with its partials in the library's fixed scratch array (nothing
+    allocated by the library); out [h,m,dv] and Z [h,m] are the caller's."""
+    K, V, Q = _heads(K, "K"), _heads(V, "V"), _heads(Q, "Q")
+    h, n, d = K.shape
+    dv = V.shape[2]
+    m = Q.shape[1]
+    if V.shape[:2] != (h, n) or Q.shape[0] != h or Q.shape[2] != d:
+        raise ValueError(f"shape mismatch: K {tuple(K.shape)}, V {tuple(V.shape)}, "
+                         f"Q {tuple(Q.shape)}")
+    _check(_lib().exact_attend_noalloc(_dev(K, "K", 3), _dev(V, "V", 3), n, d, dv, h,
+                                       _dev(Q, "Q", 3), m, _dev(out, "out", 3),
+                                       _dev(Z, "Z", 2), _stream()), "exact_attend_noalloc")
+    return out, Z
 
 
 def exact_release_workspaces():

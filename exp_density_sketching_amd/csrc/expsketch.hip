@@ -35,6 +35,13 @@ KR_EXTERN(4, false)
 KR_EXTERN(4, true)
 #undef KR_EXTERN
 
+// Scratch of the allocation-free exact path (exact_attend_noalloc): one array per
+// device (each GPU the library runs on holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: its device
+// address is taken once per device with hipGetSymbolAddress (scratch_on_device).
+constexpr long long kScratchFloats = 4LL << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
 
 #define SK_TRY(expr)                               \
@@ -926,6 +933,7 @@ const char* sk_strerror(int code) {
     case SK_ENOMEM: return "out of device memory";
     case SK_EMISMATCH: return "sketch shapes differ";
     case SK_EHIP: return "HIP runtime error";
+    case SK_ESCRATCH: return "request exceeds the fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -1579,10 +1587,12 @@ int sketch_state(sk_handle s, const float** dev_state, int64_t* rows_D, int* col
 
 namespace {
 
-// The exact path: the partials live in the kept per-(device, stream) buffer (or
-// a stream-ordered allocation).
+// The exact path.  fixed == nullptr: the partials live in the kept per-(device,
+// stream) buffer (or a stream-ordered allocation); otherwise in `fixed`, which
+// holds fixed_floats floats, and the slice count is lowered until they fit.
 int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
-              const float* Q, int64_t m, float* out, float* Z, void* hip_stream) {
+              const float* Q, int64_t m, float* out, float* Z, void* hip_stream,
+              float* fixed, long long fixed_floats) {
   if (!is_pow2_in(d, 4, 128) || !is_pow2_in(dv, 4, 128) || h < 1 || n < 0 || m < 0)
     return SK_EINVAL;
   if (m == 0) return SK_OK;
@@ -1632,6 +1642,11 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
     ns = std::min((8LL * di.num_cu + hq - 1) / hq, ((long long)n + lk - 1) / lk);
   }
   ns = std::max(1LL, ns);
+  if (fixed != nullptr) {
+    const long long per_slice = (long long)h * m * (2 + dv);
+    if (per_slice > fixed_floats) return SK_ESCRATCH;
+    ns = std::min(ns, fixed_floats / per_slice);
+  }
   long long kps = n > 0 ? (n + ns - 1) / ns : 0;
   kps = (kps + 31) / 32 * 32;
   const int nsplit = kps > 0 ? (int)((n + kps - 1) / kps) : 1;
@@ -1641,12 +1656,16 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   // do not interleave their kernels on it.  The stream still waits for the
   // buffer's last use: a destroyed stream's handle value can come back as a new
   // stream while the old one's kernels run.
-  std::lock_guard<std::mutex> ws_lock(g_xws_mutex);
-  Workspace* ws = xws_for(dev, reinterpret_cast<void*>(st));
-  float* parts = nullptr;
+  std::unique_lock<std::mutex> ws_lock(g_xws_mutex, std::defer_lock);
+  Workspace* ws = nullptr;
+  float* parts = fixed;
   bool own = false;
-  rc = take_workspace(ws, pbytes, st, false, &parts, &own);
-  if (rc != SK_OK) return rc;
+  if (fixed == nullptr) {
+    ws_lock.lock();
+    ws = xws_for(dev, reinterpret_cast<void*>(st));
+    rc = take_workspace(ws, pbytes, st, false, &parts, &own);
+    if (rc != SK_OK) return rc;
+  }
   const long long nn = n;
   const long long mm = m;
   if (decode) {
@@ -1720,8 +1739,31 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
-  release_workspace(ws, parts, own, st);
+  if (ws != nullptr) release_workspace(ws, parts, own, st);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
+  return SK_OK;
+}
+
+std::mutex g_scratch_mutex;
+std::vector<float*> g_scratch;
+
+// The scratch array's device address on the current device (looked up on the
+// first call on that device).
+int scratch_on_device(float** out) {
+  *out = nullptr;
+  int dev = 0;
+  SK_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return SK_EHIP;
+    }
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
   return SK_OK;
 }
 
@@ -1731,8 +1773,25 @@ extern "C" {
 
 int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
                  const float* Q, int64_t m, float* out, float* Z, void* hip_stream) {
-  return exact_run(K, V, n, d, dv, h, Q, m, out, Z, hip_stream);
+  return exact_run(K, V, n, d, dv, h, Q, m, out, Z, hip_stream, nullptr, 0);
 }
+
+int exact_attend_noalloc(const float* K, const float* V, int64_t n, int d, int dv, int h,
+                         const float* Q, int64_t m, float* out, float* Z,
+                         void* hip_stream) {
+  if (!is_pow2_in(d, 4, 128) || !is_pow2_in(dv, 4, 128) || h < 1 || n < 0 || m < 0)
+    return SK_EINVAL;
+  if (m == 0) return SK_OK;
+  if (Q == nullptr || out == nullptr || Z == nullptr || !aligned16(Q)) return SK_EINVAL;
+  if (n > 0 && (K == nullptr || V == nullptr || !aligned16(K) || !aligned16(V)))
+    return SK_EINVAL;
+  if ((long long)h * m * (2 + dv) > kScratchFloats) return SK_ESCRATCH;
+  float* buf = nullptr;
+  const int rc = scratch_on_device(&buf);
+  if (rc != SK_OK) return rc;
+  return exact_run(K, V, n, d, dv, h, Q, m, out, Z, hip_stream, buf, kScratchFloats);
+}
+
 
 int exact_release_workspaces(void) {
   std::lock_guard<std::mutex> ws_lock(g_xws_mutex);

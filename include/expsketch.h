@@ -48,6 +48,7 @@ extern "C" {
 #define SK_ENOMEM    -2  /* device memory for the state or a workspace not available */
 #define SK_EMISMATCH -3  /* merge of sketches with different (d, dv, p, h) */
 #define SK_EHIP      -4  /* a HIP runtime call or kernel launch failed */
+#define SK_ESCRATCH  -5  /* request larger than an allocation-free call's fixed scratch */
 
 typedef struct sk_sketch* sk_handle;  /* opaque; owned by the library */
 
@@ -229,6 +230,25 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
  */
 int exact_attend(const float* K, const float* V, int64_t n, int d, int dv, int h,
                  const float* Q, int64_t m, float* out, float* Z, void* hip_stream);
+
+/*
+ * exact_attend_noalloc -- exact_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and kernels, with the per-slice
+ * partials in a fixed scratch array of the library (16 MiB = 4,194,304 floats per
+ * device, held until the process ends) instead of a kept or stream-ordered
+ * allocation.  Nothing is allocated or freed.  The slice count is lowered until
+ * h * m * slices * (2 + dv) floats fit; answers then differ from exact_attend's
+ * only by summation order.  Every call on a device shares that device's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.  Every partial is written before it is read, so
+ * nothing is cleared between calls.
+ *   Arguments, layouts and results as exact_attend.
+ * Errors: SK_EINVAL (as exact_attend), SK_ESCRATCH when even one slice per
+ * query needs more than the scratch (h * m * (2 + dv) > 4,194,304), SK_EHIP.
+ */
+int exact_attend_noalloc(const float* K, const float* V, int64_t n, int d, int dv, int h,
+                         const float* Q, int64_t m, float* out, float* Z, void* hip_stream);
 
 /*
  * exact_release_workspaces -- frees every partials buffer exact_attend keeps

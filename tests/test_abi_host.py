@@ -123,3 +123,14 @@ def test_product_path_has_no_oracle_or_fallback():
             assert "import oracle" not in src and "from oracle" not in src, fn
             assert "numpy" not in src or fn == "build.py", fn
 
+
+def test_noalloc_exact_rejects_on_the_host():
+    lib = _lib()
+    fake = ctypes.c_void_p(4096)          # never dereferenced: refused before any HIP call
+    assert lib.exact_attend_noalloc(None, None, 4, 3, 4, 1, None, 1, None, None, None) == -1
+    assert lib.exact_attend_noalloc(None, None, 4, 4, 4, 1, None, 1, None, None, None) == -1
+    assert lib.exact_attend_noalloc(None, None, 4, 4, 4, 1, None, 0, None, None, None) == 0
+    # 32 heads x 2048 queries x (2 + 64) floats > 4,194,304: beyond the scratch
+    assert lib.exact_attend_noalloc(fake, fake, 32, 4, 64, 32, fake, 2048, fake, fake,
+                                    None) == -5
+    assert lib.sk_strerror(-5) == b"request exceeds the fixed scratch buffer"
