@@ -23,7 +23,10 @@ EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_update
             "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
             "exact_attend", "exact_attend_noalloc", "exact_release_workspaces",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
-            "sketch_kernel_times", "sk_strerror", "sk_version")
+            "sketch_kernel_times", "sk_strerror", "sk_version",
+            "coreset_create", "coreset_destroy", "coreset_set_stream", "coreset_reset",
+            "coreset_update", "coreset_merge", "coreset_query", "coreset_info",
+            "coreset_export")
 
 
 class SketchError(RuntimeError):
@@ -74,6 +77,17 @@ def _lib():
             "sketch_timing": (c_int, [vp, c_int]),
             "sketch_kernel_times": (c_int, [vp, c_int, ctypes.POINTER(ctypes.c_float), c_int,
                                             ctypes.POINTER(c_int)]),
+            "coreset_create": (c_int, [c_int, c_int, c_int, c_int, c_int, ctypes.c_double,
+                                       ctypes.c_uint64, vp, ctypes.POINTER(vp)]),
+            "coreset_destroy": (c_int, [vp]),
+            "coreset_set_stream": (c_int, [vp, vp]),
+            "coreset_reset": (c_int, [vp]),
+            "coreset_update": (c_int, [vp, vp, vp, c_i64]),
+            "coreset_merge": (c_int, [vp, vp]),
+            "coreset_query": (c_int, [vp, vp, c_i64, vp, vp]),
+            "coreset_info": (c_int, [vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64),
+                                     ctypes.POINTER(c_i64)]),
+            "coreset_export": (c_int, [vp, vp, vp, vp]),
             "sk_strerror": (ctypes.c_char_p, [c_int]),
             "sk_version": (c_int, []),
         }
@@ -343,6 +357,86 @@ def exact_attend_noalloc(K, V, Q, out, Z):
 def exact_release_workspaces():
     """Free the partials buffers exact_attend keeps per (device, stream)."""
     _check(_lib().exact_release_workspaces(), "exact_release_workspaces")
+
+
+class Coreset:
+    """Tail coreset handle (coreset_create ... coreset_destroy): Merge-and-Reduce
+    blocks of `block` points per head, each reduce a discrepancy halving."""
+
+    def __init__(self, d, dv, p, h=1, block=512, c0=0.25, seed=0):
+        handle = ctypes.c_void_p()
+        _check(_lib().coreset_create(d, dv, p, h, block, float(c0), int(seed) & (2**64 - 1),
+                                     _stream(), ctypes.byref(handle)), "coreset_create")
+        self._h = handle
+        self.d, self.dv, self.p, self.h, self.block = d, dv, p, h, block
+
+    def _handle(self):
+        if self._h is None:
+            raise RuntimeError("coreset destroyed")
+        _check(_lib().coreset_set_stream(self._h, _stream()), "coreset_set_stream")
+        return self._h
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            h, self._h = self._h, None
+            _check(_lib().coreset_destroy(h), "coreset_destroy")
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def info(self):
+        """(points per head, points ingested per head, reduces done)."""
+        pts, cnt, red = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(_lib().coreset_info(self._handle(), ctypes.byref(pts), ctypes.byref(cnt),
+                                   ctypes.byref(red)), "coreset_info")
+        return pts.value, cnt.value, red.value
+
+
+def coreset_create(d, dv, p, h=1, block=512, c0=0.25, seed=0):
+    return Coreset(d, dv, p, h, block, c0, seed)
+
+
+def coreset_reset(c):
+    _check(_lib().coreset_reset(c._handle()), "coreset_reset")
+
+
+def coreset_update(c, K, V):
+    """K [h, n, d] (or [n, d]), V [h, n, dv]: n more points per head."""
+    K, V = _heads(K, "K"), _heads(V, "V")
+    if K.shape[0] != c.h or K.shape[2] != c.d or V.shape[:2] != K.shape[:2] or V.shape[2] != c.dv:
+        raise ValueError(f"shape mismatch: K {tuple(K.shape)}, V {tuple(V.shape)}")
+    _check(_lib().coreset_update(c._handle(), _dev(K, "K", 3), _dev(V, "V", 3), K.shape[1]),
+           "coreset_update")
+
+
+def coreset_merge(dst, src):
+    _check(_lib().coreset_merge(dst._handle(), src._handle()), "coreset_merge")
+
+
+def coreset_query(c, Q, out, Z):
+    """Adds the tail to the head answer (out [h, m, dv], Z [h, m]) in place."""
+    Q = _heads(Q, "Q")
+    if Q.shape[0] != c.h or Q.shape[2] != c.d:
+        raise ValueError(f"Q must be [{c.h}, m, {c.d}]")
+    _check(_lib().coreset_query(c._handle(), _dev(Q, "Q", 3), Q.shape[1], _dev(out, "out", 3),
+                                _dev(Z, "Z", 2)), "coreset_query")
+    return out, Z
+
+
+def coreset_export(c):
+    """(K [h, P, d], V [h, P, dv], w [h, P]) of the coreset's points."""
+    pts = c.info()[0]
+    dev = torch.device("cuda", torch.cuda.current_device())
+    K = torch.empty((c.h, pts, c.d), dtype=torch.float32, device=dev)
+    V = torch.empty((c.h, pts, c.dv), dtype=torch.float32, device=dev)
+    w = torch.empty((c.h, pts), dtype=torch.float32, device=dev)
+    if pts > 0:
+        _check(_lib().coreset_export(c._handle(), _dev(K, "K", 3), _dev(V, "V", 3),
+                                     _dev(w, "w", 2)), "coreset_export")
+    return K, V, w
 
 
 def raw():

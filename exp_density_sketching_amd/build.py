@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libexpsketch.so")
 
 # (source, extra defines): one object each
-UNITS = [("expsketch.hip", [])] + [
+UNITS = [("expsketch.hip", []), ("coreset.hip", [])] + [
     ("sk_update_kr.hip", [f"-DKR_RT={rt}", f"-DKR_CENTER={c}"])
     for rt in (1, 2, 4) for c in (0, 1)]
 SOURCES = [os.path.join(CSRC, f) for f in sorted({u[0] for u in UNITS})]

@@ -307,6 +307,99 @@ int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D,
 int sketch_timing(sk_handle s, int enable);
 int sketch_kernel_times(sk_handle s, int kind, float* ms, int cap, int* count);
 
+/*
+ * Tail coreset -- the tail of the exp kernel's expansion answered from a weighted
+ * subset of the stream ("Metodologia" > "1. Limites Superiores Algorítmicos",
+ * pillar "Construções de Coreset Baseadas em Discrepância": small subsets built
+ * with discrepancy theory approximate the kernel density for every query and
+ * serve the tail of the expansion, while the moments serve its head; the closing
+ * paragraph assembles the stream with Merge-and-Reduce).  The pages name results,
+ * not a procedure; the readings implemented:
+ *   - e^x = T_p(x) + R_p(x): the sketch answers sum_i T_p(<q,k_i>) [1, v_i]
+ *     exactly; the coreset answers sum_i R_p(<q,k_i>) [1, v_i] by
+ *     sum_s w_s R_p(<q,k_s>) [1, v_s] over its points.
+ *   - Merge-and-Reduce as a binary counter of blocks of `block` points per head:
+ *     points fill a buffer (weight 1); a full buffer enters level 0; two blocks of
+ *     level l (older first, 2 * block points read as consecutive pairs) are halved
+ *     into one block of level l + 1 (weight 2^(l+1)).
+ *   - Halving: the self-balancing walk of Alweiss, Liu and Sawhney (STOC 2021)
+ *     over the pairs in the feature space of <u(x), u(y)> = R_p(<k_x,k_y>)
+ *     (1 + <v_x,v_y>): pair t has alpha_t = <psi, f_t> (psi the signed sum of the
+ *     pairs before it, f_t the difference of its two points), P_t = (1 -
+ *     alpha_t / c) / 2 clamped to [0, 1], c = c0 * max_t |f_t|^2; it keeps its
+ *     second point when U_t < P_t, else its first.  U_t = (SplitMix64 output >>
+ *     11) * 2^-53 (Steele, Lea and Flood, OOPSLA 2014) of counter
+ *     (r * h + head) * block + t, r = the handle's reduce number, state `seed`.
+ * The Gram matrix and the walk run in float64, so the kept points (copies of
+ * input rows, bit for bit) match a float64 reference unless a uniform falls
+ * within rounding of its threshold.
+ */
+typedef struct sk_coreset* sk_coreset_handle;  /* opaque; owned by the library */
+
+/*
+ * coreset_create -- an empty coreset of h heads (d, dv, p as sketch_create;
+ * 64 <= block <= 2048, a multiple of 64; c0 > 0 the walk's threshold factor;
+ * seed the generator's state).  The library allocates its block buffers on
+ * demand (hipMalloc) and frees them in coreset_destroy.
+ * Errors: SK_EINVAL (shapes, block, c0, out == NULL), SK_ENOMEM, SK_EHIP.
+ */
+int coreset_create(int d, int dv, int p, int h, int block, double c0, uint64_t seed,
+                   void* hip_stream, sk_coreset_handle* out);
+
+/* coreset_destroy -- synchronises the handle's stream and frees it (NULL: no-op). */
+int coreset_destroy(sk_coreset_handle c);
+
+/* coreset_set_stream -- later calls on another stream, which first waits for
+ * everything issued on the old one.  Errors: SK_EINVAL, SK_EHIP. */
+int coreset_set_stream(sk_coreset_handle c, void* hip_stream);
+
+/* coreset_reset -- back to the empty coreset (count 0, reduce number 0). */
+int coreset_reset(sk_coreset_handle c);
+
+/*
+ * coreset_update -- n more pairs per head: K [h][n][d], V [h][n][dv] (device,
+ * caller-owned; they may be reused once the stream has passed the call).  Runs
+ * every reduce the new points cause (Merge-and-Reduce).
+ * Errors: SK_EINVAL (NULL/misaligned pointer with n > 0, n < 0), SK_ENOMEM, SK_EHIP.
+ */
+int coreset_update(sk_coreset_handle c, const float* K, const float* V, int64_t n);
+
+/*
+ * coreset_merge -- dst takes src's points (Merge-and-Reduce across sub-streams):
+ * src's buffered points enter dst's buffer in order (a full buffer enters level
+ * 0), then src's blocks enter dst at their own levels, lowest first, with the
+ * reduces this causes (numbered by dst).  src is unchanged.  Equal (d, dv, p, h,
+ * block) required.  Runs on dst's stream, ordered after src's and before src's
+ * later work.
+ * Errors: SK_EINVAL, SK_EMISMATCH, SK_ENOMEM, SK_EHIP.
+ */
+int coreset_merge(sk_coreset_handle dst, sk_coreset_handle src);
+
+/*
+ * coreset_query -- adds the tail to a head answer, in place: on entry out [h][m][dv]
+ * and Z [h][m] hold (ohat, Zhat) of the moments (sketch_query) or zeros; on
+ * return Z = Zhat + tZ and out = (ohat * Zhat + tN) / Z, with tZ = sum_s w_s
+ * R_p(<q,k_s>) and tN = sum_s w_s R_p(<q,k_s>) v_s over the coreset's points (fp32;
+ * R_p by its series for |<q,k>| <= 16, else e^x - T_p(x)).  Q [h][m][d] device.
+ * With no points the head answer is left as it is.  Partials live in a buffer the
+ * handle keeps.
+ * Errors: SK_EINVAL, SK_ENOMEM, SK_EHIP.
+ */
+int coreset_query(sk_coreset_handle c, const float* Q, int64_t m, float* out, float* Z);
+
+/* coreset_info -- points per head, points ingested per head, reduces done (any
+ * pointer may be NULL).  Errors: SK_EINVAL. */
+int coreset_info(sk_coreset_handle c, int64_t* points, int64_t* count, int64_t* reduces);
+
+/*
+ * coreset_export -- the points into caller-owned device memory: K [h][points][d],
+ * V [h][points][dv], w [h][points] (points from coreset_info): the buffer first
+ * (weight 1), then the blocks by increasing level (weight 2^l), each in its row
+ * order.  Asynchronous on the handle's stream.
+ * Errors: SK_EINVAL, SK_EHIP.
+ */
+int coreset_export(sk_coreset_handle c, float* K, float* V, float* w);
+
 /* sk_strerror -- a static string for a status code. */
 const char* sk_strerror(int code);
 

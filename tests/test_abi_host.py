@@ -134,3 +134,22 @@ def test_noalloc_exact_rejects_on_the_host():
     assert lib.exact_attend_noalloc(fake, fake, 32, 4, 64, 32, fake, 2048, fake, fake,
                                     None) == -5
     assert lib.sk_strerror(-5) == b"request exceeds the fixed scratch buffer"
+
+
+def test_coreset_create_rejects_on_the_host():
+    lib = _lib()
+    out = ctypes.c_void_p(1234)
+    for args in [(3, 4, 2, 1, 64, 0.25), (4, 4, 17, 1, 64, 0.25), (4, 4, 2, 0, 64, 0.25),
+                 (4, 4, 2, 1, 100, 0.25), (4, 4, 2, 1, 32, 0.25), (4, 4, 2, 1, 4096, 0.25),
+                 (4, 4, 2, 1, 64, 0.0), (4, 4, 2, 1, 64, -1.0), (4, 4, 2, 1, 64, float("nan"))]:
+        assert lib.coreset_create(*args, 0, None, ctypes.byref(out)) == -1, args
+        assert out.value is None
+    assert lib.coreset_create(4, 4, 2, 1, 64, 0.25, 0, None, None) == -1
+    assert lib.coreset_destroy(None) == 0
+    assert lib.coreset_update(None, None, None, 3) == -1
+    assert lib.coreset_merge(None, None) == -1
+    assert lib.coreset_query(None, None, 1, None, None) == -1
+    assert lib.coreset_info(None, None, None, None) == -1
+    assert lib.coreset_export(None, None, None, None) == -1
+    assert lib.coreset_reset(None) == -1
+    assert lib.coreset_set_stream(None, None) == -1
