@@ -333,6 +333,7 @@ def measure_workload(w, E, torch, K, V, Q, args, full_line=True):
     sketches = full["sketches"]
     ukern = E.UPDATE_KERNELS[E.sketch_update_path(sketches[0])]
     sketch_error = sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e)
+    tail = coreset_leg(w, E, torch, Kg, Vg, Qg, out_s, z_s, out_e, z_e, max(1, args.steps // 2))
     t_upd, t_qry, t_ex, t_step = full["t_upd"], full["t_qry"], full["t_ex"], full["t_step"]
     dur, t_qk = full["dur"], full["t_qk"]
     flop_per_key = 2.0 * w.D * (1 + w.dv)
@@ -383,6 +384,7 @@ def measure_workload(w, E, torch, K, V, Q, args, full_line=True):
                           "kernel": exact_batched_kernel(w)},
         "exact_decode": exact_decode(w, E, torch, Kg, Vg, Qg, args.decode_steps),
         "sketch_error": sketch_error,
+        "tail_coreset": tail,
         "roofline": {"kernel": ukern, "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA,
@@ -421,6 +423,63 @@ def measure_workload(w, E, torch, K, V, Q, args, full_line=True):
     res["decode_step"] = decode_steps(w, E, torch, Kg, Vg, Qg, args.decode_steps,
                                       res["exact_decode"]["us_per_step"])
     return res
+
+
+def coreset_leg(w, E, torch, Kg, Vg, Qg, out_s, z_s, out_e, z_e, steps, block=512, c0=0.25):
+    """The tail coreset beside the sketch: Merge-and-Reduce ingest of the same
+    stream (the workload's calls and sub-stream merges), the tail added to the
+    sketch's answers, and the error of head + tail against the exact path."""
+    import numpy as np
+    S = max(1, w.substreams)
+    cs = [E.coreset_create(w.d, w.dv, w.p, w.h, block=block, c0=c0, seed=1) for _ in range(S)]
+    bounds = [w.n * i // S for i in range(S + 1)]
+    pieces = []
+    for i in range(S):
+        step = w.chunk if w.chunk > 0 else bounds[i + 1] - bounds[i]
+        for c0_ in range(bounds[i], bounds[i + 1], step):
+            c1 = min(bounds[i + 1], c0_ + step)
+            pieces.append((i, Kg[:, c0_:c1].contiguous(), Vg[:, c0_:c1].contiguous()))
+    torch.cuda.synchronize()
+
+    def ingest():
+        for c in cs:
+            E.coreset_reset(c)
+        for i, k, v in pieces:
+            E.coreset_update(cs[i], k, v)
+        for i in range(1, S):
+            E.coreset_merge(cs[0], cs[i])
+
+    ingest()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(steps):
+        ingest()
+    b.record()
+    torch.cuda.synchronize()
+    t_ing = a.elapsed_time(b) / 1e3 / steps
+    pts, cnt, red = cs[0].info()
+    out = out_s.clone()
+    Z = z_s.clone()
+    E.coreset_query(cs[0], Qg, out, Z)
+    o2, z2 = out_s.clone(), z_s.clone()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        E.coreset_query(cs[0], Qg, o2, z2)
+    b.record()
+    torch.cuda.synchronize()
+    t_q = a.elapsed_time(b) / 1e3 / steps
+    zc, zex = Z.cpu().double().numpy(), z_e.cpu().double().numpy()
+    oc, oex = out.cpu().double().numpy(), out_e.cpu().double().numpy()
+    for c in cs:
+        c.destroy()
+    return {"block": block, "c0": c0, "points_per_head": pts, "reduces": red,
+            "ingest_ms": t_ing * 1e3, "keys_per_s": w.h * w.n / t_ing,
+            "tail_query_ms": t_q * 1e3, "queries_per_s": w.h * w.m / t_q,
+            "error_with_tail": {"z_rel_max": float(np.max(np.abs(zc - zex) / zex)),
+                                "o_abs_max": float(np.max(np.abs(oc - oex)))}}
 
 
 def sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e):
@@ -471,7 +530,10 @@ def error_of_config(w, E, torch, generate, decode_steps_n):
     out_e, z_e = E.exact_attend(Kg, Vg, Qg)
     torch.cuda.synchronize()
     sk.destroy()
+    tail = coreset_leg(w, E, torch, Kg, Vg, Qg, out_s, z_s, out_e, z_e, 1)
     r = {"sketch_error": sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e),
+         "error_with_tail": tail["error_with_tail"],
+         "tail_points_per_head": tail["points_per_head"],
          "exact_decode": exact_decode(w, E, torch, Kg, Vg, Qg, decode_steps_n)}
     del Kg, Vg, Qg
     torch.cuda.empty_cache()
@@ -528,11 +590,12 @@ def main():
         errs = {}
         for i in sorted(WORKLOADS):
             wi = WORKLOADS[i]
-            if wi.ident == w.ident:
-                r = {"sketch_error": line["sketch_error"], "exact_decode": line["exact_decode"]}
-            elif "workload3" in line and wi.ident == 3:
-                r = {"sketch_error": line["workload3"]["sketch_error"],
-                     "exact_decode": line["workload3"]["exact_decode"]}
+            if wi.ident == w.ident or ("workload3" in line and wi.ident == 3):
+                src = line if wi.ident == w.ident else line["workload3"]
+                r = {"sketch_error": src["sketch_error"],
+                     "error_with_tail": src["tail_coreset"]["error_with_tail"],
+                     "tail_points_per_head": src["tail_coreset"]["points_per_head"],
+                     "exact_decode": src["exact_decode"]}
             else:
                 print(f"bench: error of {wi.name}", file=sys.stderr, flush=True)
                 r = error_of_config(wi, E, torch, generate, args.decode_steps)

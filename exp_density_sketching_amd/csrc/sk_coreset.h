@@ -107,6 +107,8 @@ __device__ inline double cs_tail_exp64(double x, int p, const double* __restrict
     t *= ax * cs_inv[i];
     hm += t;
   }
+  // (big <= hm already decides for the series without e^x: e^x > 0)
+  if (ax <= 40.0 && big <= hm) return acc;
   const double ex = exp(x);
   if (ax <= 40.0 && big <= ex + hm) return acc;
   // e^x - T_p(x), T_p by Horner from the top
