@@ -499,7 +499,9 @@ def sketch_vs_exact(w, K, Q, z_s, out_s, z_e, out_e):
 
 def exact_decode(w, E, torch, Kg, Vg, Qg, steps):
     """The exact path in decode mode (one query per head), streaming the whole KV:
-    algorithmic bytes (d + dv) * 4 per key / time per call."""
+    algorithmic bytes (d + dv) * 4 per key / time per call, and / the decode
+    kernel's own time (median of HIP event pairs around it)."""
+    import numpy as np
     dec_out = torch.empty((w.h, 1, w.dv), device="cuda")
     dec_z = torch.empty((w.h, 1), device="cuda")
     q1 = Qg[:, :1].contiguous()
@@ -512,11 +514,20 @@ def exact_decode(w, E, torch, Kg, Vg, Qg, steps):
     b.record()
     torch.cuda.synchronize()
     t_dec = a.elapsed_time(b) / 1e3 / steps
+    # the decode kernel alone (HIP events around it on the call's stream)
+    E.exact_timing(True)
+    for _ in range(steps):
+        E.exact_attend(Kg, Vg, q1, dec_out, dec_z)
+    kern = E.exact_kernel_times()
+    E.exact_timing(False)
+    t_k = float(np.median(kern)) / 1e3
     kv_bytes = 4.0 * w.h * w.n * (w.d + w.dv)
     hbm = kv_bytes > 256e6
     return {"us_per_step": t_dec * 1e6, "GBps": kv_bytes / t_dec / 1e9,
             "kv_bytes": kv_bytes,
             "frac_of_hbm_peak": kv_bytes / t_dec / PEAK_HBM if hbm else None,
+            "kernel_us": t_k * 1e6, "kernel_GBps": kv_bytes / t_k / 1e9,
+            "kernel_frac_of_hbm_peak": kv_bytes / t_k / PEAK_HBM if hbm else None,
             "resident": "HBM" if hbm else "cache (<= 256 MB): effective GB/s"}
 
 

@@ -13,7 +13,8 @@ from ._binding import (LIB_PATH, EXPORTED, LAYOUTS, Sketch, SketchError, sketch_
                        sketch_query, sketch_step, sketch_set_center, sketch_set_staging,
                        sketch_export, sketch_state, sketch_timing,
                        sketch_kernel_times, exact_attend, exact_attend_noalloc,
-                       exact_release_workspaces, raw, Coreset, coreset_create,
+                       exact_release_workspaces, exact_timing, exact_kernel_times, raw,
+                       Coreset, coreset_create,
                        coreset_reset, coreset_update, coreset_merge, coreset_query,
                        coreset_export)
 
@@ -22,6 +23,7 @@ __all__ = ["LIB_PATH", "EXPORTED", "LAYOUTS", "Sketch", "SketchError", "sketch_c
            "sketch_destroy", "sketch_reset", "sketch_update", "sketch_merge",
            "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
            "sketch_export", "sketch_state", "sketch_timing",
-           "sketch_kernel_times", "exact_attend", "exact_attend_noalloc", "exact_release_workspaces", "raw",
+           "sketch_kernel_times", "exact_attend", "exact_attend_noalloc", "exact_release_workspaces",
+           "exact_timing", "exact_kernel_times", "raw",
            "Coreset", "coreset_create", "coreset_reset", "coreset_update", "coreset_merge",
            "coreset_query", "coreset_export"]

@@ -22,6 +22,7 @@ EXPORTED = ("sketch_create", "sketch_create_ex", "sketch_layout", "sketch_update
             "sketch_set_stream", "sketch_reset", "sketch_update", "sketch_merge",
             "sketch_query", "sketch_step", "sketch_set_center", "sketch_set_staging",
             "exact_attend", "exact_attend_noalloc", "exact_release_workspaces",
+            "exact_timing", "exact_kernel_times",
             "sketch_state", "sketch_export", "sketch_info", "sketch_timing",
             "sketch_kernel_times", "sk_strerror", "sk_version",
             "coreset_create", "coreset_destroy", "coreset_set_stream", "coreset_reset",
@@ -68,6 +69,9 @@ def _lib():
             "exact_attend_noalloc": (c_int, [vp, vp, c_i64, c_int, c_int, c_int, vp, c_i64,
                                              vp, vp, vp]),
             "exact_release_workspaces": (c_int, []),
+            "exact_timing": (c_int, [c_int]),
+            "exact_kernel_times": (c_int, [ctypes.POINTER(ctypes.c_float), c_int,
+                                           ctypes.POINTER(c_int)]),
             "sketch_state": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(c_i64),
                                      ctypes.POINTER(c_int), ctypes.POINTER(c_i64)]),
             "sketch_export": (c_int, [vp, vp]),
@@ -352,6 +356,19 @@ def exact_attend_noalloc(K, V, Q, out, Z):
                                        _dev(Q, "Q", 3), m, _dev(out, "out", 3),
                                        _dev(Z, "Z", 2), _stream()), "exact_attend_noalloc")
     return out, Z
+
+
+def exact_timing(enable=True):
+    _check(_lib().exact_timing(1 if enable else 0), "exact_timing")
+
+
+def exact_kernel_times():
+    """Milliseconds of the recorded slice kernels of exact_attend calls."""
+    cap = 256
+    buf = (ctypes.c_float * cap)()
+    cnt = ctypes.c_int()
+    _check(_lib().exact_kernel_times(buf, cap, ctypes.byref(cnt)), "exact_kernel_times")
+    return [buf[i] for i in range(min(cnt.value, cap))]
 
 
 def exact_release_workspaces():

@@ -17,6 +17,7 @@
 #include "sk_elementwise.h"
 #include "sk_exact.h"
 #include "sk_query.h"
+#include "sk_query_dg.h"
 #include "sk_step.h"
 #include "sk_sym.h"
 #include "sk_update.h"
@@ -236,6 +237,52 @@ QueryKernel query_kernel_for(int logd) {
   }
 }
 
+// Query kernels by the last digit (sk_query_dg.h), per log2(d) and 32-column tiles.
+using QueryDgKernel = QueryKernel;
+// d <= 64: the register-query kernel; d = 128: the LDS-query kernel
+QueryDgKernel query_dg_kernel_for(int logd) {
+  switch (logd) {
+    case 2: return sk_query_dgr_kernel<2>;
+    case 3: return sk_query_dgr_kernel<3>;
+    case 4: return sk_query_dgr_kernel<4>;
+    case 5: return sk_query_dgr_kernel<5>;
+    case 6: return sk_query_dgr_kernel<6>;
+    default: return sk_query_dg_kernel<7>;
+  }
+}
+QueryDgKernel query_dg16_kernel_for(int logd) {
+  switch (logd) {
+    case 2: return sk_query_dg16_kernel<2>;
+    case 3: return sk_query_dg16_kernel<3>;
+    default: return sk_query_dg16_kernel<4>;
+  }
+}
+size_t query_dg_lds_bytes(int d) {
+  const size_t ldb = 32 * SK_DGNT + 32;
+  if (d <= 64) return sizeof(float) * 2 * (size_t)std::max(d, SK_DGK) * ldb;
+  return sizeof(float) * ((size_t)d * (SK_DGQ + 33) + 2 * (size_t)SK_DGK * ldb);
+}
+size_t query_dg16_lds_bytes(int d) {
+  return sizeof(float) * ((size_t)d * (SK_DGQ + 1) + 2 * (size_t)SK_DGK * (16 + 4));
+}
+// EXPSKETCH_QUERY_DG16=1 puts levels of 8 < C <= 16 columns on the 16-column
+// last-digit kernel (tuning aid).
+bool use_query_dg16() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_QUERY_DG16");
+    return e != nullptr && std::atoi(e) != 0;
+  }();
+  return v;
+}
+// EXPSKETCH_QUERY_DG=0 keeps every level on the feature-tile query kernel.
+bool use_query_dg() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_QUERY_DG");
+    return e == nullptr || std::atoi(e) != 0;
+  }();
+  return v;
+}
+
 // Per-call partials (query, exact path).  A hipMallocAsync that follows a
 // hipFreeAsync on the same stream makes the host wait here until that stream has
 // drained (measured: back-to-back calls then return only as each previous call's
@@ -315,6 +362,14 @@ std::mutex g_xws_mutex;
 std::map<std::pair<int, void*>, XwsEntry> g_xws;
 unsigned long long g_xws_clock = 0;
 
+// Kernel timing of the exact path (exact_timing): pairs of events around the
+// slice kernel of each exact_attend call, up to kTimingPairsX; guarded by
+// g_xws_mutex.
+constexpr int kTimingPairsX = 256;
+bool g_xtiming = false;
+std::vector<hipEvent_t> g_xev[2];
+int g_xrec = 0;
+
 // The kept partials buffer of (dev, stream); the caller holds g_xws_mutex.
 Workspace* xws_for(int dev, void* stream) {
   const auto key = std::make_pair(dev, stream);
@@ -358,6 +413,14 @@ struct sk_sketch {
   KrUnit* d_kunits = nullptr;
   QryTile* d_qtiles = nullptr;
   long long qpb = 0;        // floats of query partials per (head, query tile)
+  // query launches of the full layout: tiles grouped by kernel (0: feature
+  // tiles, 1: by the last digit with nt 32-column tiles, 2: by the last digit,
+  // 16 columns); each group's tiles are contiguous in qrun
+  struct QGroup { int kind, nt, off, count; };
+  std::vector<int> qkind;                  // per tile of qtiles: kind * 16 + nt
+  std::vector<QryTile> qrun;
+  std::vector<QGroup> qgroups;
+  QryTile* d_qrun = nullptr;
   float* view = nullptr;    // canonical view buffer
   bool timing = false;      // kernel timing (sketch_timing)
   std::vector<hipEvent_t> tev[3][2];   // [kind][start, stop], created on first use
@@ -524,10 +587,44 @@ bool plan_kr_units(sk_sketch* s) {
   return true;
 }
 
+// EXPSKETCH_QUERY_FOLD=0 keeps levels of 8 or 16 columns off the last-digit
+// kernel (tuning aid).
+bool use_query_fold() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_QUERY_FOLD");
+    return e == nullptr || std::atoi(e) != 0;
+  }();
+  return v;
+}
+// Level j runs on the register-query kernel with its last digit on the column
+// side: C of 8 or 16 (dividing the 32 columns of an MFMA tile), d <= 64, at least
+// one digit left on the row side and d C >= 32 columns.
+bool query_level_fold(const sk_sketch* s, int j) {
+  const int C = s->C[j];
+  return use_query_fold() && (C == 8 || C == 16) && s->d <= 64 && j >= 1 &&
+         s->d * C >= 32;
+}
+
 // Query tiles of level j: t trailing digits in the columns (the fewest giving at
 // least SK_TNQ columns), 128-column tiles, a_hi ranges of query_rows_per_tile().
+// Kernel of level j's query: by the last digit when its C columns fill MFMA
+// columns (32x32x2 for C > 16, in 64-column tiles), or with the last digit on
+// the column side for C = 8 or 16 (query_level_fold); 16x16x4 for other
+// 8 < C <= 16 at d <= 16 when asked for; else the feature-tile kernel.  Returns
+// kind * 16.
+int query_level_kind(const sk_sketch* s, int j) {
+  const int C = s->C[j];
+  if (!use_query_dg()) return 0;
+  if (C > 16 || query_level_fold(s, j)) return 16;
+  // (other 8 < C <= 16 stay on the feature-tile kernel: its folded 128-column
+  // tiles measured faster than sk_query_dg16_kernel at d = 16 and d = 8)
+  if (C > 8 && C <= 16 && s->d <= 16 && use_query_dg16()) return 32;
+  return 0;
+}
+
 void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long* pb) {
   const int d = s->d, C = s->C[j];
+  const int kind = query_level_kind(s, j);
   // t trailing digits go to the epilogue (folded with the weights q^(x)t): the
   // fewest whose d^t C columns fill a column tile.  A level whose own C columns
   // fill half a tile takes none: the half-empty tile, with its deeper rows and
@@ -542,13 +639,19 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
   // q^(x)s from that many (p <= 16 keeps j - SK_MAXDIG <= t <= SK_MAXDIG feasible)
   while (t > SK_MAXDIG) --t;
   if (t < j - SK_MAXDIG) t = j - SK_MAXDIG;
+  // by the last digit: every row on the row side, or one digit on the column side
+  const bool fold = kind != 0 && query_level_fold(s, j);
+  if (kind != 0) t = fold ? 1 : 0;
   const int sd = j - t;
   const long long N = (long long)std::llround(std::pow((double)d, t)) * C;
   const long long Kr = (long long)std::llround(std::pow((double)d, sd));
   double fj = 1.0;
   for (int i = 2; i <= j; ++i) fj *= i;
-  for (long long col0 = 0; col0 < N; col0 += SK_TNQ) {
-    const long long last = std::min(N, col0 + SK_TNQ) - 1;
+  // the last-digit kernel owns 64 columns a tile and writes a partial of those
+  // columns only; the feature-tile kernel 128 GEMM columns folded into all C
+  const long long tn = kind == 16 ? 32 * SK_DGNT : SK_TNQ;
+  for (long long col0 = 0; col0 < N; col0 += tn) {
+    const long long last = std::min(N, col0 + tn) - 1;
     for (long long a0 = 0; a0 < Kr; a0 += query_rows_per_tile()) {
       QryTile q{};
       q.xoff = s->xoff[j];
@@ -566,8 +669,11 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
       q.nalo = (int)(last / C - col0 / C + 1);
       q.wz = (float)(1.0 / (fj * (j + 1)));
       q.wn = (float)(1.0 / fj);
-      *pb += (long long)SK_TMQ * C;
+      q.fc0 = (kind == 16 && !fold) ? (int)col0 : 0;
+      q.fw = (kind == 16 && !fold) ? (int)(last - col0 + 1) : C;
+      *pb += (long long)SK_TMQ * q.fw;
       out->push_back(q);
+      s->qkind.push_back(kind);
     }
   }
 }
@@ -672,6 +778,8 @@ void plan_sym_query_block(sk_sketch* s, long long xoff, int rc0, int nrows, int 
     f.pofs = s->qpb;
     f.C = C;
     f.top = top;
+    f.fc0 = 0;
+    f.fw = C;
     s->qtiles.push_back(f);
     for (int col0 = 0; col0 < C; col0 += TN) {
       SymQryTile q{};
@@ -996,6 +1104,14 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   } else {
     for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
     for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
+    // group the query tiles by kernel (tile order kept inside a group)
+    for (int key : {0, 16, 32}) {
+      const int off = (int)s->qrun.size();
+      for (size_t i = 0; i < s->qtiles.size(); ++i)
+        if (s->qkind[i] == key) s->qrun.push_back(s->qtiles[i]);
+      const int cnt = (int)s->qrun.size() - off;
+      if (cnt > 0) s->qgroups.push_back(sk_sketch::QGroup{key / 16, key % 16, off, cnt});
+    }
     if (kr_width(d) && use_update_kr()) plan_kr_units(s);
   }
 
@@ -1030,6 +1146,19 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
       ok = hipFuncSetAttribute((const void*)sym_update_kernel_for(t0.rb, t0.cb, cen != 0),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess;
   }
+  for (size_t g = 0; ok && !sym && g < s->qgroups.size(); ++g) {
+    const sk_sketch::QGroup& G = s->qgroups[g];
+    if (G.kind == 1)
+      ok = hipFuncSetAttribute((const void*)query_dg_kernel_for(s->logd),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)query_dg_lds_bytes(d)) == hipSuccess;
+    else if (G.kind == 2)
+      ok = hipFuncSetAttribute((const void*)query_dg16_kernel_for(s->logd),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)query_dg16_lds_bytes(d)) == hipSuccess;
+  }
+  if (ok && !sym)
+    ok = upload((void**)&s->d_qrun, s->qrun.data(), sizeof(QryTile) * s->qrun.size());
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
          upload((void**)&s->d_kunits, s->kunits.data(), sizeof(KrUnit) * s->kunits.size()) &&
@@ -1043,6 +1172,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   if (!ok) {
     (void)hipGetLastError();
     (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
+    (void)hipFree(s->d_qrun);
     (void)hipFree(s->d_kunits);
     (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
     (void)hipFree(s->d_stiles); (void)hipFree(s->sparts);
@@ -1080,6 +1210,7 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->d_utiles);
   (void)hipFree(s->d_kunits);
   (void)hipFree(s->d_qtiles);
+  (void)hipFree(s->d_qrun);
   (void)hipFree(s->d_sutiles);
   (void)hipFree(s->d_sqtiles);
   (void)hipFree(s->symbuf);
@@ -1425,23 +1556,31 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     hipLaunchKernelGGL(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
                        sym_query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->state,
                        s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, s->qpb, parts);
-  } else {
-    hipLaunchKernelGGL(query_kernel_for(s->logd), dim3((unsigned)(ntiles * nqt * s->h)),
-                       dim3(SK_WG), query_lds_bytes(s->d), s->stream, Q, (long long)m,
-                       s->state, s->XS, s->d_qtiles, ntiles, (int)nqt, s->qpb, parts);
   }
   hipError_t e1 = hipGetLastError();
+  for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < s->qgroups.size(); ++g) {
+    const sk_sketch::QGroup& G = s->qgroups[g];
+    QueryKernel kern = G.kind == 0   ? query_kernel_for(s->logd)
+                       : G.kind == 1 ? query_dg_kernel_for(s->logd)
+                                     : query_dg16_kernel_for(s->logd);
+    const size_t lds = G.kind == 0   ? query_lds_bytes(s->d)
+                       : G.kind == 1 ? query_dg_lds_bytes(s->d)
+                                     : query_dg16_lds_bytes(s->d);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((long long)G.count * nqt * s->h)), dim3(SK_WG), lds,
+                       s->stream, Q, (long long)m, s->state, s->XS, s->d_qrun + G.off, G.count,
+                       (int)nqt, s->qpb, parts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) e1 = e;
+  }
   timing_mark(s, 1, true);
-  // threads per (query, column) and queries per finishing workgroup (a power of
-  // two with qg * (d + dv) * lanes <= 256)
+  // queries per finishing workgroup: a power of two with qg * (d + dv) <= SK_QFIN_ENT
   const int cols = s->d + s->dv;
-  const int lanes = cols <= 64 ? 4 : (cols <= 128 ? 2 : 1);
   int qg = 1;
-  while (qg < SK_TMQ && 2 * qg * cols * lanes <= 256) qg *= 2;
+  while (qg < SK_TMQ && 2 * qg * cols <= SK_QFIN_ENT) qg *= 2;
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / qg) * s->h)),
                      dim3(256), 0, s->stream,
                      parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
-                     s->dv, qg, lanes, (float)s->count, Q, s->center, out, Z);
+                     s->dv, qg, (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
   release_workspace(&s->qws, parts, own, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
@@ -1619,20 +1758,26 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   const bool qb4 = mfma16 && d <= 32;
   const long long per_wg = !use_mfma ? 256 : (qb4 ? 256 : SK_XQ);   // queries per workgroup
   const long long nqt = decode ? 1 : (m + per_wg - 1) / per_wg;
-  // EXPSKETCH_EXACT_MINKEYS=<k> sets the fewest keys per slice (tuning aid).
+  // EXPSKETCH_EXACT_MINKEYS=<k> sets the fewest keys per slice, and
+  // EXPSKETCH_EXACT_WGCU=<w> the long decode slices per CU (tuning aids).
   static const long long min_keys_env = [] {
     const char* v = std::getenv("EXPSKETCH_EXACT_MINKEYS");
     return v ? std::max(0LL, std::atoll(v)) : 0LL;
   }();
-  // Decode streams K/V once: about two long (>= 4096-key) slices per CU keep HBM
+  static const long long wg_per_cu = [] {
+    const char* v = std::getenv("EXPSKETCH_EXACT_WGCU");
+    const long long x = v ? std::atoll(v) : 0LL;
+    return x >= 1 ? x : 2LL;
+  }();
+  // Decode streams K/V once: about two long (>= 2048-key) slices per CU keep HBM
   // busiest, but never fewer slices than one per CU while slices stay >= 512
   // keys.  The batched kernel is compute-bound: more, shorter slices.
   const long long hq = h * nqt;
   long long ns;
   if (decode) {
-    const long long lk = min_keys_env > 0 ? min_keys_env : 4096;
+    const long long lk = min_keys_env > 0 ? min_keys_env : 2048;
     const long long nn = n;
-    const long long ns_long = std::min((2LL * di.num_cu + hq - 1) / hq, (nn + lk - 1) / lk);
+    const long long ns_long = std::min((wg_per_cu * di.num_cu + hq - 1) / hq, (nn + lk - 1) / lk);
     const long long ns_fill = std::min(((long long)di.num_cu + hq - 1) / hq, (nn + 511) / 512);
     ns = std::max(ns_long, ns_fill);
   } else {
@@ -1668,6 +1813,8 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   }
   const long long nn = n;
   const long long mm = m;
+  const bool timed = fixed == nullptr && g_xtiming && g_xrec < (int)g_xev[0].size();
+  if (timed) (void)hipEventRecord(g_xev[0][g_xrec], st);
   if (decode) {
     const int mq = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
     dim3 grid(nsplit, h), blk(256);
@@ -1736,6 +1883,7 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
 #undef SK_XM
   }
   hipError_t e1 = hipGetLastError();
+  if (timed) (void)hipEventRecord(g_xev[1][g_xrec++], st);
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
@@ -1792,6 +1940,33 @@ int exact_attend_noalloc(const float* K, const float* V, int64_t n, int d, int d
   return exact_run(K, V, n, d, dv, h, Q, m, out, Z, hip_stream, buf, kScratchFloats);
 }
 
+
+int exact_timing(int enable) {
+  std::lock_guard<std::mutex> lock(g_xws_mutex);
+  if (enable && g_xev[0].empty()) {
+    for (int w = 0; w < 2; ++w) {
+      g_xev[w].resize(kTimingPairsX);
+      for (int i = 0; i < kTimingPairsX; ++i) SK_TRY(hipEventCreate(&g_xev[w][i]));
+    }
+  }
+  g_xtiming = enable != 0;
+  g_xrec = 0;
+  return SK_OK;
+}
+
+int exact_kernel_times(float* ms, int cap, int* count) {
+  if (cap < 0 || (ms == nullptr && cap > 0)) return SK_EINVAL;
+  std::lock_guard<std::mutex> lock(g_xws_mutex);
+  const int nrec = g_xrec;
+  if (count) *count = nrec;
+  if (nrec > 0) {
+    SK_TRY(hipEventSynchronize(g_xev[1][nrec - 1]));
+    for (int i = 0; i < nrec && i < cap; ++i)
+      SK_TRY(hipEventElapsedTime(&ms[i], g_xev[0][i], g_xev[1][i]));
+  }
+  g_xrec = 0;
+  return SK_OK;
+}
 
 int exact_release_workspaces(void) {
   std::lock_guard<std::mutex> ws_lock(g_xws_mutex);

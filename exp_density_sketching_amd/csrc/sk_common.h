@@ -88,4 +88,5 @@ struct QryTile {
   int col0;         // first GEMM column of the tile
   int alo0, nalo;   // a_lo values the tile's columns touch
   float wz, wn;     // 1/(j+1)! (weights of M_{j+1}), 1/j! (weights of N_j)
+  int fc0, fw;      // the partial holds columns fc0 .. fc0 + fw - 1 of the level: [128][fw]
 };

@@ -206,28 +206,28 @@ void sk_query_kernel(const float* __restrict__ Q, long long m,
 }
 
 // Sum the partials of every tile in tile order, add the count, divide.  One
-// workgroup per (head, query tile, group of qg queries), the tile table staged in
-// LDS once.  Entry (query, col) adds column col of its query over the tiles in
-// four running sums (tile index mod 4, each in tile order), added as (s0 + s1) +
-// (s2 + s3); `lanes` (4, 2 or 1) threads share an entry, each taking residues
-// lane, lane + lanes, ..., so the tiles' loads go out in parallel.  qg * (d + dv)
-// * lanes <= 256.  A column col < d of a lower level holds a share of Zhat, col >=
-// d one of Ntilde[col - d] (top-level tiles hold only the Ntilde columns, at
-// col - d).  Zhat is then the count plus the Zhat columns of the query, added in
-// column order.
+// workgroup per (head, query tile, group of qg queries, qg * (d + dv) <=
+// SK_QFIN_ENT), the tile table staged in LDS once.  Each thread owns up to 8 of
+// the group's (query, column) entries and walks the tiles in order, adding each
+// tile's term to each of its entries (the loads of four tiles go out together).
+// A tile's record holds columns fc0 .. fc0 + fw - 1 of its level; a column col < d
+// of a lower level holds a share of Zhat, col >= d one of Ntilde[col - d]
+// (top-level tiles hold only the Ntilde columns, at col - d).  Zhat is then the count plus the query's Zhat columns in four running sums
+// by column mod 4, added as (s0 + s1) + (s2 + s3).
 #define SK_QFIN_LDS 1024
+#define SK_QFIN_ENT 2048
 __global__ __launch_bounds__(256)
 void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
                      int ntiles, int nqt, long long PB, long long m, int d, int dv, int qg,
-                     int lanes, float count, const float* __restrict__ Q,
+                     float count, const float* __restrict__ Q,
                      const float* __restrict__ center, float* __restrict__ out,
                      float* __restrict__ Z) {
   __shared__ long long tp[SK_QFIN_LDS];
-  __shared__ int tc[SK_QFIN_LDS];
+  __shared__ int tc[SK_QFIN_LDS];      // record width fw
+  __shared__ int tf[SK_QFIN_LDS];      // record's first column fc0
   __shared__ int tt[SK_QFIN_LDS];
-  __shared__ float rs[4][256];        // residue sums per entry
-  __shared__ float cs[256];
-  __shared__ float zq[256];
+  __shared__ float cs[SK_QFIN_ENT];
+  __shared__ float zq[SK_TMQ];
   const int tid = threadIdx.x;
   const int cols = d + dv;
   const int ngrp = SK_TMQ / qg;
@@ -242,34 +242,50 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     for (int i = tid; i < ntiles; i += 256) {
       const QryTile T = tiles[i];
       tp[i] = T.pofs;
-      tc[i] = T.C;
+      tc[i] = T.fw;
+      tf[i] = T.fc0;
       tt[i] = T.top;
     }
   }
   __syncthreads();
   const int nent = qg * cols;
-  const int ent = tid / lanes, ln = tid - ent * lanes;
-  const bool act = ent < nent;
-  const int ql = act ? ent / cols : 0;
-  const int col = act ? ent - ql * cols : 0;
-  const long long qoff = qi0 + ql;
-  // one term: the partial of tile ti for (query, col), zero if the tile has no such column
-  auto term = [&](int ti) -> float {
-    long long pofs; int C, top;
-    if (staged) { pofs = tp[ti]; C = tc[ti]; top = tt[ti]; }
-    else { const QryTile T = tiles[ti]; pofs = T.pofs; C = T.C; top = T.top; }
-    const int c = top ? col - d : col;
-    return (c >= 0) ? P[pofs + qoff * C + c] : 0.f;
-  };
-  if (act) {
-    for (int r = ln; r < 4; r += lanes) {
-      float a = 0.f;
-      for (int ti = r; ti < ntiles; ti += 4) a += term(ti);
-      rs[r][ent] = a;
-    }
+  const int ne = (nent - tid + 255) / 256;   // entries of this thread (<= 8)
+  int eq[8], ec[8];
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e = tid + 256 * k;
+    eq[k] = e / cols;
+    ec[k] = e - eq[k] * cols;
+    acc[k] = 0.f;
   }
-  __syncthreads();
-  for (int e = tid; e < nent; e += 256) cs[e] = (rs[0][e] + rs[1][e]) + (rs[2][e] + rs[3][e]);
+  // four tiles a step: up to 32 loads of a thread in flight, added in tile order
+  for (int t0 = 0; t0 < ntiles; t0 += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ti = t0 + u;
+      long long pofs = 0; int fw = 0, fc = 0, top = 0;
+      if (ti < ntiles) {
+        if (staged) { pofs = tp[ti]; fw = tc[ti]; fc = tf[ti]; top = tt[ti]; }
+        else { const QryTile T = tiles[ti]; pofs = T.pofs; fw = T.fw; fc = T.fc0; top = T.top; }
+      }
+      const int sh = (top ? d : 0) + fc;     // entry column -> record column
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = ec[k] - sh;
+        x[u][k] = (k < ne && c >= 0 && c < fw)
+                      ? P[pofs + (long long)(qi0 + eq[k]) * fw + c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += x[u][k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < ne) cs[tid + 256 * k] = acc[k];
   __syncthreads();
   if (tid < qg) {
     const float* row = cs + tid * cols;
@@ -280,8 +296,12 @@ void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict_
     zq[tid] = ((z0 + z1) + (z2 + z3)) + count;
   }
   __syncthreads();
-  const long long q = qbase + ql;
-  if (act && ln == 0 && col >= d && q < m) out[(head * m + q) * dv + (col - d)] = cs[ent] / zq[ql];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const long long q = qbase + eq[k];
+    if (k < ne && ec[k] >= d && q < m)
+      out[(head * m + q) * dv + (ec[k] - d)] = acc[k] / zq[eq[k]];
+  }
   // with a centre c the moments are those of k - c: the returned Zhat carries
   // e^{<q,c>}, which cancels in ohat
   if (tid < qg && qbase + tid < m) {

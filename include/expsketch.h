@@ -251,6 +251,20 @@ int exact_attend_noalloc(const float* K, const float* V, int64_t n, int d, int d
                          const float* Q, int64_t m, float* out, float* Z, void* hip_stream);
 
 /*
+ * exact_timing -- kernel timing of the exact path with HIP events (for
+ * measurement).  While enabled, each exact_attend call records a pair of
+ * library-owned events on its stream around its slice kernel (the decode or
+ * batched kernel, not the combine), up to 256 pairs; enable != 0 starts (and
+ * clears) recording, 0 stops it.
+ * exact_kernel_times -- waits for the last recorded pair, writes the elapsed
+ * milliseconds of up to `cap` pairs into ms (host array), sets *count to the
+ * number recorded, and clears them.
+ * Errors: SK_EINVAL (cap < 0, ms NULL with cap > 0), SK_EHIP.
+ */
+int exact_timing(int enable);
+int exact_kernel_times(float* ms, int cap, int* count);
+
+/*
  * exact_release_workspaces -- frees every partials buffer exact_attend keeps
  * (waiting on the host for each buffer's last use first).  Later calls allocate
  * again.  For a caller that wants the memory back, e.g. before its streams are

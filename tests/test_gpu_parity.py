@@ -105,12 +105,15 @@ def test_state_matches_oracle_moments(ident, n, h):
     assert ptr and D == w.D and cols == 1 + w.dv and cnt == n
 
 
-# the last four put 64 or more columns (d + dv, or dv at the top) on levels j >= 1,
-# where the query contracts the whole level without folding a digit
+# (16, 64, 3) .. (32, 32, 2) put 64 or more columns (d + dv, or dv at the top) on
+# levels j >= 1, where the query contracts the whole level without folding a
+# digit; (4, 4, 7) .. (16, 16, 3) have levels of 8 or 16 columns, whose last digit
+# the query moves to the column side (d C = 32 up to 512 columns)
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
-                                    (128, 128, 1), (4, 4, 7), (32, 8, 2), (32, 16, 2),
+                                    (128, 128, 1), (32, 8, 2), (32, 16, 2),
                                     (64, 16, 1), (128, 16, 1),
-                                    (16, 64, 3), (8, 64, 3), (4, 64, 4), (32, 32, 2)])
+                                    (16, 64, 3), (8, 64, 3), (4, 64, 4), (32, 32, 2),
+                                    (4, 4, 7), (64, 8, 2), (8, 8, 4), (16, 16, 3)])
 def test_other_shapes(d, dv, p):
     w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})

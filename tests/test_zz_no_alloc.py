@@ -55,3 +55,10 @@ def test_beyond_the_scratch_is_refused():
     with pytest.raises(E.SketchError) as err:
         E.exact_attend_noalloc(Kg, Vg, Qg, out, Z)
     assert err.value.code == -5
+
+
+def test_decode_calls_in_a_row():
+    """Decode calls (m <= 8) with other head counts, key counts and query counts
+    in a row on the one scratch array: each must match exact_attend."""
+    for i, (h, n, m) in enumerate([(3, 9000, 1), (7, 4000, 8), (2, 70000, 3), (3, 9000, 1)]):
+        _compare(h, n, m, 16, 32, 10 + i, f"decode call {i}")
