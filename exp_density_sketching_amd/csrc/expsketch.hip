@@ -51,12 +51,14 @@ namespace {
   } while (0)
 
 constexpr int kMaxP = 16;
-// a_hi rows per query tile (EXPSKETCH_QUERY_ROWS overrides, tuning aid)
-long long query_rows_per_tile() {
+// a_hi rows per query tile: the full layout keeps plans of 512, 256 and 128 rows
+// and a query takes the longest whose launch fills the GPU (query_plan_for);
+// EXPSKETCH_QUERY_ROWS fixes one length instead (a multiple of 64; tuning aid)
+long long query_rows_fixed() {
   static const long long v = [] {
     const char* e = std::getenv("EXPSKETCH_QUERY_ROWS");
     const long long r = e ? std::atoll(e) : 0;
-    return r >= SK_KB ? r / SK_KB * SK_KB : 512LL;
+    return r >= 64 ? r / 64 * 64 : 0LL;
   }();
   return v;
 }
@@ -259,7 +261,7 @@ QueryDgKernel query_dg16_kernel_for(int logd) {
 }
 size_t query_dg_lds_bytes(int d) {
   const size_t ldb = 32 * SK_DGNT + 32;
-  if (d <= 64) return sizeof(float) * 2 * (size_t)std::max(d, SK_DGK) * ldb;
+  if (d <= 64) return sizeof(float) * 2 * (size_t)(d >= 8 ? 64 : SK_DGK) * ldb;
   return sizeof(float) * ((size_t)d * (SK_DGQ + 33) + 2 * (size_t)SK_DGK * ldb);
 }
 size_t query_dg16_lds_bytes(int d) {
@@ -405,22 +407,29 @@ struct sk_sketch {
   std::vector<long long> xoff, rows;
   std::vector<int> C;
   std::vector<UpdTile> utiles;
-  std::vector<QryTile> qtiles;
   UpdTile* d_utiles = nullptr;
   std::vector<KrUnit> kunits;      // digit-organised update units (d >= 16)
   std::vector<int> kgroup0;        // their groups (first unit of each, then the count)
   std::vector<int> kweight;        // work per key of each group's units
   KrUnit* d_kunits = nullptr;
-  QryTile* d_qtiles = nullptr;
-  long long qpb = 0;        // floats of query partials per (head, query tile)
-  // query launches of the full layout: tiles grouped by kernel (0: feature
-  // tiles, 1: by the last digit with nt 32-column tiles, 2: by the last digit,
-  // 16 columns); each group's tiles are contiguous in qrun
+  // query plans: the full layout one per row length of its tiles (longest
+  // first), the multiset layout one (its tiles are sqtiles; the plan holds the
+  // finishing records)
   struct QGroup { int kind, nt, off, count; };
-  std::vector<int> qkind;                  // per tile of qtiles: kind * 16 + nt
-  std::vector<QryTile> qrun;
-  std::vector<QGroup> qgroups;
-  QryTile* d_qrun = nullptr;
+  struct QPlan {
+    long long rows = 0;                    // a_hi rows per tile
+    std::vector<QryTile> tiles;            // in level order
+    std::vector<int> kind;                 // per tile: kind * 16
+    // launches of the full layout: tiles grouped by kernel (0: feature tiles,
+    // 1: by the last digit, 2: by the last digit, 16 columns); each group's
+    // tiles are contiguous in run
+    std::vector<QryTile> run;
+    std::vector<QGroup> groups;
+    long long pb = 0;                      // floats of partials per (head, query tile)
+    QryTile* d_run = nullptr;
+    FinTile* d_fin = nullptr;              // finishing records, one per tile
+  };
+  std::vector<QPlan> qplans;
   float* view = nullptr;    // canonical view buffer
   bool timing = false;      // kernel timing (sketch_timing)
   std::vector<hipEvent_t> tev[3][2];   // [kind][start, stop], created on first use
@@ -597,16 +606,16 @@ bool use_query_fold() {
   return v;
 }
 // Level j runs on the register-query kernel with its last digit on the column
-// side: C of 8 or 16 (dividing the 32 columns of an MFMA tile), d <= 64, at least
-// one digit left on the row side and d C >= 32 columns.
+// side: C of 8 or 16 (dividing the 32 columns of an MFMA tile), 16 <= d <= 64 and
+// at least one digit left on the row side.  (At d = 8 the feature-tile kernel
+// measured faster: 0.50 against 0.48 of peak on the d = 8, p = 6 workload.)
 bool query_level_fold(const sk_sketch* s, int j) {
   const int C = s->C[j];
-  return use_query_fold() && (C == 8 || C == 16) && s->d <= 64 && j >= 1 &&
-         s->d * C >= 32;
+  return use_query_fold() && (C == 8 || C == 16) && s->d >= 16 && s->d <= 64 && j >= 1;
 }
 
 // Query tiles of level j: t trailing digits in the columns (the fewest giving at
-// least SK_TNQ columns), 128-column tiles, a_hi ranges of query_rows_per_tile().
+// least SK_TNQ columns), 128-column tiles, a_hi ranges of the plan's rows.
 // Kernel of level j's query: by the last digit when its C columns fill MFMA
 // columns (32x32x2 for C > 16, in 64-column tiles), or with the last digit on
 // the column side for C = 8 or 16 (query_level_fold); 16x16x4 for other
@@ -622,7 +631,7 @@ int query_level_kind(const sk_sketch* s, int j) {
   return 0;
 }
 
-void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long* pb) {
+void plan_query_level(sk_sketch* s, int j, sk_sketch::QPlan* qp) {
   const int d = s->d, C = s->C[j];
   const int kind = query_level_kind(s, j);
   // t trailing digits go to the epilogue (folded with the weights q^(x)t): the
@@ -652,12 +661,12 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
   const long long tn = kind == 16 ? 32 * SK_DGNT : SK_TNQ;
   for (long long col0 = 0; col0 < N; col0 += tn) {
     const long long last = std::min(N, col0 + tn) - 1;
-    for (long long a0 = 0; a0 < Kr; a0 += query_rows_per_tile()) {
+    for (long long a0 = 0; a0 < Kr; a0 += qp->rows) {
       QryTile q{};
       q.xoff = s->xoff[j];
       q.a0 = a0;
-      q.a1 = std::min(Kr, a0 + query_rows_per_tile());
-      q.pofs = *pb;
+      q.a1 = std::min(Kr, a0 + qp->rows);
+      q.pofs = qp->pb;
       q.level = j;
       q.C = C;
       q.top = (j == s->p);
@@ -671,9 +680,9 @@ void plan_query_level(sk_sketch* s, int j, std::vector<QryTile>* out, long long*
       q.wn = (float)(1.0 / fj);
       q.fc0 = (kind == 16 && !fold) ? (int)col0 : 0;
       q.fw = (kind == 16 && !fold) ? (int)(last - col0 + 1) : C;
-      *pb += (long long)SK_TMQ * q.fw;
-      out->push_back(q);
-      s->qkind.push_back(kind);
+      qp->pb += (long long)SK_TMQ * q.fw;
+      qp->tiles.push_back(q);
+      qp->kind.push_back(kind);
     }
   }
 }
@@ -771,20 +780,21 @@ void plan_sym_update_block(sk_sketch* s, SymHost* t, long long xoff, int rc0, in
 // Query ranges of one block: one [SY_TQ][C] partial per range of sym_query_rows()
 // rows, filled by the range's column tiles.
 void plan_sym_query_block(sk_sketch* s, long long xoff, int rc0, int nrows, int C, int top) {
+  sk_sketch::QPlan& qp = s->qplans[0];
   const int cb = C <= 16 ? 1 : (C <= 32 ? 2 : (C <= 64 ? 4 : 8));
   const int TN = 16 * cb;
   for (int r0 = 0; r0 < nrows; r0 += sym_query_rows()) {
     QryTile f{};
-    f.pofs = s->qpb;
+    f.pofs = qp.pb;
     f.C = C;
     f.top = top;
     f.fc0 = 0;
     f.fw = C;
-    s->qtiles.push_back(f);
+    qp.tiles.push_back(f);
     for (int col0 = 0; col0 < C; col0 += TN) {
       SymQryTile q{};
       q.xoff = xoff;
-      q.pofs = s->qpb;
+      q.pofs = qp.pb;
       q.rc0 = rc0;
       q.row0 = r0;
       q.nrows = std::min(sym_query_rows(), nrows - r0);
@@ -794,7 +804,7 @@ void plan_sym_query_block(sk_sketch* s, long long xoff, int rc0, int nrows, int 
       q.cb = cb;
       s->sqtiles.push_back(q);
     }
-    s->qpb += (long long)SY_TQ * C;
+    qp.pb += (long long)SY_TQ * C;
   }
 }
 
@@ -818,6 +828,7 @@ int build_sym(sk_sketch* s) {
                       s->sutiles[i - 1].rb * 8 + s->sutiles[i - 1].cb)
       s->sgroup.push_back((int)i);
   s->sgroup.push_back((int)s->sutiles.size());
+  s->qplans.resize(1);
   if (s->Rlo > 0) plan_sym_query_block(s, 0, 0, (int)s->Rlo, Cl, 0);
   plan_sym_query_block(s, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
   // one device allocation: code | prefix | last | lmul | rslot | winv | slots
@@ -1103,14 +1114,23 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     }
   } else {
     for (int j = 0; j <= p; ++j) plan_update_level(s, j, &s->utiles);
-    for (int j = 0; j <= p; ++j) plan_query_level(s, j, &s->qtiles, &s->qpb);
-    // group the query tiles by kernel (tile order kept inside a group)
-    for (int key : {0, 16, 32}) {
-      const int off = (int)s->qrun.size();
-      for (size_t i = 0; i < s->qtiles.size(); ++i)
-        if (s->qkind[i] == key) s->qrun.push_back(s->qtiles[i]);
-      const int cnt = (int)s->qrun.size() - off;
-      if (cnt > 0) s->qgroups.push_back(sk_sketch::QGroup{key / 16, key % 16, off, cnt});
+    if (query_rows_fixed() > 0) {
+      s->qplans.resize(1);
+      s->qplans[0].rows = query_rows_fixed();
+    } else {
+      s->qplans.resize(3);
+      for (int i = 0; i < 3; ++i) s->qplans[i].rows = 512 >> i;
+    }
+    for (sk_sketch::QPlan& qp : s->qplans) {
+      for (int j = 0; j <= p; ++j) plan_query_level(s, j, &qp);
+      // group the query tiles by kernel (tile order kept inside a group)
+      for (int key : {0, 16, 32}) {
+        const int off = (int)qp.run.size();
+        for (size_t i = 0; i < qp.tiles.size(); ++i)
+          if (qp.kind[i] == key) qp.run.push_back(qp.tiles[i]);
+        const int cnt = (int)qp.run.size() - off;
+        if (cnt > 0) qp.groups.push_back(sk_sketch::QGroup{key / 16, key % 16, off, cnt});
+      }
     }
     if (kr_width(d) && use_update_kr()) plan_kr_units(s);
   }
@@ -1128,7 +1148,15 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     return hipMalloc(dst, bytes) == hipSuccess &&
            hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice) == hipSuccess;
   };
-  bool ok = upload((void**)&s->d_qtiles, s->qtiles.data(), sizeof(QryTile) * s->qtiles.size()) &&
+  bool ok = true;
+  for (sk_sketch::QPlan& qp : s->qplans) {
+    // finishing records: tile record offset, width, entry column of its column 0
+    std::vector<FinTile> fin;
+    for (const QryTile& T : qp.tiles) fin.push_back(FinTile{T.pofs, T.fw, (T.top ? d : 0) + T.fc0});
+    ok = ok && upload((void**)&qp.d_fin, fin.data(), sizeof(FinTile) * fin.size()) &&
+         upload((void**)&qp.d_run, qp.run.data(), sizeof(QryTile) * qp.run.size());
+  }
+  ok = ok &&
             upload((void**)&s->d_stiles, s->stiles.data(),
                    sizeof(StepTile) * s->stiles.size()) &&
             hipMalloc(&s->sparts, sizeof(float) * (size_t)h * s->stiles.size() * (1 + dv)) ==
@@ -1146,8 +1174,8 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
       ok = hipFuncSetAttribute((const void*)sym_update_kernel_for(t0.rb, t0.cb, cen != 0),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ul) == hipSuccess;
   }
-  for (size_t g = 0; ok && !sym && g < s->qgroups.size(); ++g) {
-    const sk_sketch::QGroup& G = s->qgroups[g];
+  for (size_t g = 0; ok && !sym && g < s->qplans[0].groups.size(); ++g) {
+    const sk_sketch::QGroup& G = s->qplans[0].groups[g];
     if (G.kind == 1)
       ok = hipFuncSetAttribute((const void*)query_dg_kernel_for(s->logd),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1157,8 +1185,6 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)query_dg16_lds_bytes(d)) == hipSuccess;
   }
-  if (ok && !sym)
-    ok = upload((void**)&s->d_qrun, s->qrun.data(), sizeof(QryTile) * s->qrun.size());
   if (ok && !sym)
     ok = upload((void**)&s->d_utiles, s->utiles.data(), sizeof(UpdTile) * s->utiles.size()) &&
          upload((void**)&s->d_kunits, s->kunits.data(), sizeof(KrUnit) * s->kunits.size()) &&
@@ -1171,8 +1197,8 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
   if (ok) ok = launch_fill_zero(s->state, s->XS * h, s->stream) == SK_OK;
   if (!ok) {
     (void)hipGetLastError();
-    (void)hipFree(s->state); (void)hipFree(s->d_utiles); (void)hipFree(s->d_qtiles);
-    (void)hipFree(s->d_qrun);
+    (void)hipFree(s->state); (void)hipFree(s->d_utiles);
+    for (sk_sketch::QPlan& qp : s->qplans) { (void)hipFree(qp.d_fin); (void)hipFree(qp.d_run); }
     (void)hipFree(s->d_kunits);
     (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
     (void)hipFree(s->d_stiles); (void)hipFree(s->sparts);
@@ -1209,8 +1235,10 @@ int sketch_destroy(sk_handle s) {
   (void)hipFree(s->state);
   (void)hipFree(s->d_utiles);
   (void)hipFree(s->d_kunits);
-  (void)hipFree(s->d_qtiles);
-  (void)hipFree(s->d_qrun);
+  for (sk_sketch::QPlan& qp : s->qplans) {
+    (void)hipFree(qp.d_fin);
+    (void)hipFree(qp.d_run);
+  }
   (void)hipFree(s->d_sutiles);
   (void)hipFree(s->d_sqtiles);
   (void)hipFree(s->symbuf);
@@ -1538,12 +1566,18 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     const int rc = settle(s);
     if (rc != SK_OK) return rc;
   }
-  const int ntiles = (int)s->qtiles.size();
   const long long nqt = (m + SK_TMQ - 1) / SK_TMQ;
-  const long long nlaunch = std::max<long long>(
-      SK_TMQ, std::max<long long>(ntiles, (long long)s->sqtiles.size()));
-  if (nqt * nlaunch * s->h > 0x7fffffffLL) return SK_EINVAL;
-  const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * s->qpb;
+  // the plan with the longest row ranges whose launch still gives every CU two
+  // workgroups (shorter ranges: more partials to add, so only where needed)
+  size_t pi = 0;
+  while (pi + 1 < s->qplans.size() &&
+         (long long)s->qplans[pi].tiles.size() * nqt * s->h < 2LL * s->dev.num_cu)
+    ++pi;
+  const sk_sketch::QPlan& qp = s->qplans[pi];
+  const int ntiles = (int)qp.tiles.size();
+  const long long nlaunch = std::max<long long>(ntiles, (long long)s->sqtiles.size());
+  if (nqt * nlaunch * s->h > 0x7fffffffLL || m * s->h > 0x7fffffffLL) return SK_EINVAL;
+  const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * qp.pb;
   float* parts = nullptr;
   bool own = false;
   {
@@ -1555,11 +1589,11 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     const long long nst = (long long)s->sqtiles.size();
     hipLaunchKernelGGL(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
                        sym_query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->state,
-                       s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, s->qpb, parts);
+                       s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, qp.pb, parts);
   }
   hipError_t e1 = hipGetLastError();
-  for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < s->qgroups.size(); ++g) {
-    const sk_sketch::QGroup& G = s->qgroups[g];
+  for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < qp.groups.size(); ++g) {
+    const sk_sketch::QGroup& G = qp.groups[g];
     QueryKernel kern = G.kind == 0   ? query_kernel_for(s->logd)
                        : G.kind == 1 ? query_dg_kernel_for(s->logd)
                                      : query_dg16_kernel_for(s->logd);
@@ -1567,20 +1601,16 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
                        : G.kind == 1 ? query_dg_lds_bytes(s->d)
                                      : query_dg16_lds_bytes(s->d);
     hipLaunchKernelGGL(kern, dim3((unsigned)((long long)G.count * nqt * s->h)), dim3(SK_WG), lds,
-                       s->stream, Q, (long long)m, s->state, s->XS, s->d_qrun + G.off, G.count,
-                       (int)nqt, s->qpb, parts);
+                       s->stream, Q, (long long)m, s->state, s->XS, qp.d_run + G.off, G.count,
+                       (int)nqt, qp.pb, parts);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) e1 = e;
   }
   timing_mark(s, 1, true);
-  // queries per finishing workgroup: a power of two with qg * (d + dv) <= SK_QFIN_ENT
-  const int cols = s->d + s->dv;
-  int qg = 1;
-  while (qg < SK_TMQ && 2 * qg * cols <= SK_QFIN_ENT) qg *= 2;
-  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(nqt * (SK_TMQ / qg) * s->h)),
-                     dim3(256), 0, s->stream,
-                     parts, s->d_qtiles, ntiles, (int)nqt, s->qpb, (long long)m, s->d,
-                     s->dv, qg, (float)s->count, Q, s->center, out, Z);
+  // one finishing workgroup per (head, query)
+  hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(m * s->h)), dim3(256), 0, s->stream,
+                     parts, qp.d_fin, ntiles, (int)nqt, qp.pb, (long long)m, s->d, s->dv,
+                     (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
   release_workspace(&s->qws, parts, own, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;

@@ -205,113 +205,102 @@ void sk_query_kernel(const float* __restrict__ Q, long long m,
   }
 }
 
-// Sum the partials of every tile in tile order, add the count, divide.  One
-// workgroup per (head, query tile, group of qg queries, qg * (d + dv) <=
-// SK_QFIN_ENT), the tile table staged in LDS once.  Each thread owns up to 8 of
-// the group's (query, column) entries and walks the tiles in order, adding each
-// tile's term to each of its entries (the loads of four tiles go out together).
-// A tile's record holds columns fc0 .. fc0 + fw - 1 of its level; a column col < d
-// of a lower level holds a share of Zhat, col >= d one of Ntilde[col - d]
-// (top-level tiles hold only the Ntilde columns, at col - d).  Zhat is then the count plus the query's Zhat columns in four running sums
-// by column mod 4, added as (s0 + s1) + (s2 + s3).
-#define SK_QFIN_LDS 1024
-#define SK_QFIN_ENT 2048
+// Sum the partials of every tile, add the count, divide.  One workgroup per
+// (head, query).  A tile's record holds columns fc0 .. fc0 + fw - 1 of its level;
+// a column col < d of a lower level holds a share of Zhat, col >= d one of
+// Ntilde[col - d] (top-level tiles hold only the Ntilde columns, at col - d), so
+// entry column c of the query (c < d: Zhat shares, c >= d: Ntilde[c - d]) takes
+// record column c - sh of every tile whose [sh, sh + fw) holds c (FinTile.sh).
+// The tiles are split over S = 256 / (d + dv) groups of d + dv threads: group g
+// adds the tiles g, g + S, g + 2S, ... in that order (eight loads in flight per
+// thread), then the group sums are added in group order; Zhat is the count plus
+// the query's Zhat columns in four running sums by column mod 4, added as
+// (s0 + s1) + (s2 + s3).  The tile table is staged in LDS once.
+#define SK_QFIN_LDS 512
+struct FinTile {
+  long long pofs;   // record offset in a query tile's block of partials
+  int fw;           // record width
+  int sh;           // entry column of record column 0
+};
 __global__ __launch_bounds__(256)
-void sk_query_finish(const float* __restrict__ parts, const QryTile* __restrict__ tiles,
-                     int ntiles, int nqt, long long PB, long long m, int d, int dv, int qg,
+void sk_query_finish(const float* __restrict__ parts, const FinTile* __restrict__ fin,
+                     int ntiles, int nqt, long long PB, long long m, int d, int dv,
                      float count, const float* __restrict__ Q,
                      const float* __restrict__ center, float* __restrict__ out,
                      float* __restrict__ Z) {
   __shared__ long long tp[SK_QFIN_LDS];
-  __shared__ int tc[SK_QFIN_LDS];      // record width fw
-  __shared__ int tf[SK_QFIN_LDS];      // record's first column fc0
-  __shared__ int tt[SK_QFIN_LDS];
-  __shared__ float cs[SK_QFIN_ENT];
-  __shared__ float zq[SK_TMQ];
+  __shared__ int tw[SK_QFIN_LDS];
+  __shared__ int ts[SK_QFIN_LDS];
+  __shared__ float red[256];
+  __shared__ float zq;
   const int tid = threadIdx.x;
   const int cols = d + dv;
-  const int ngrp = SK_TMQ / qg;
-  const int grpq = blockIdx.x % ngrp;
-  const int qt = (blockIdx.x / ngrp) % nqt;
-  const long long head = blockIdx.x / ((long long)ngrp * nqt);
+  const int S = cols >= 256 ? 1 : 256 / cols;
+  const long long gq = blockIdx.x;                  // head * m + query
+  const long long head = gq / m, q = gq - head * m;
+  const long long qt = q / SK_TMQ;
+  const int ql = (int)(q - qt * SK_TMQ);
   const float* P = parts + (head * nqt + qt) * PB;
-  const int qi0 = grpq * qg;                                        // inside the tile
-  const long long qbase = (long long)qt * SK_TMQ + qi0;             // first query
   const bool staged = ntiles <= SK_QFIN_LDS;
   if (staged) {
     for (int i = tid; i < ntiles; i += 256) {
-      const QryTile T = tiles[i];
-      tp[i] = T.pofs;
-      tc[i] = T.fw;
-      tf[i] = T.fc0;
-      tt[i] = T.top;
+      const FinTile f = fin[i];
+      tp[i] = f.pofs;
+      tw[i] = f.fw;
+      ts[i] = f.sh;
     }
   }
   __syncthreads();
-  const int nent = qg * cols;
-  const int ne = (nent - tid + 255) / 256;   // entries of this thread (<= 8)
-  int eq[8], ec[8];
-  float acc[8];
+  const int g = tid / cols, c = tid - g * cols;
+  float acc = 0.f;
+  if (g < S) {
+    for (int t0 = g; t0 < ntiles; t0 += 8 * S) {
+      float x[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int e = tid + 256 * k;
-    eq[k] = e / cols;
-    ec[k] = e - eq[k] * cols;
-    acc[k] = 0.f;
-  }
-  // four tiles a step: up to 32 loads of a thread in flight, added in tile order
-  for (int t0 = 0; t0 < ntiles; t0 += 4) {
-    float x[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ti = t0 + u;
-      long long pofs = 0; int fw = 0, fc = 0, top = 0;
-      if (ti < ntiles) {
-        if (staged) { pofs = tp[ti]; fw = tc[ti]; fc = tf[ti]; top = tt[ti]; }
-        else { const QryTile T = tiles[ti]; pofs = T.pofs; fw = T.fw; fc = T.fc0; top = T.top; }
+      for (int u = 0; u < 8; ++u) {
+        const int t = t0 + u * S;
+        x[u] = 0.f;
+        if (t < ntiles) {
+          long long pofs;
+          int fw, sh;
+          if (staged) { pofs = tp[t]; fw = tw[t]; sh = ts[t]; }
+          else { const FinTile f = fin[t]; pofs = f.pofs; fw = f.fw; sh = f.sh; }
+          const int cc = c - sh;
+          if (cc >= 0 && cc < fw) x[u] = P[pofs + (long long)ql * fw + cc];
+        }
       }
-      const int sh = (top ? d : 0) + fc;     // entry column -> record column
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = ec[k] - sh;
-        x[u][k] = (k < ne && c >= 0 && c < fw)
-                      ? P[pofs + (long long)(qi0 + eq[k]) * fw + c] : 0.f;
-      }
+      for (int u = 0; u < 8; ++u) acc += x[u];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += x[u][k];
   }
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k < ne) cs[tid + 256 * k] = acc[k];
+  red[tid] = acc;
   __syncthreads();
-  if (tid < qg) {
-    const float* row = cs + tid * cols;
+  float v = 0.f;
+  if (tid < cols) {
+    v = red[tid];
+    for (int k = 1; k < S; ++k) v += red[k * cols + tid];
+  }
+  __syncthreads();
+  if (tid < cols) red[tid] = v;
+  __syncthreads();
+  if (tid == 0) {
     float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
     for (int e = 0; e < d; e += 4) {
-      z0 += row[e]; z1 += row[e + 1]; z2 += row[e + 2]; z3 += row[e + 3];
+      z0 += red[e]; z1 += red[e + 1]; z2 += red[e + 2]; z3 += red[e + 3];
     }
-    zq[tid] = ((z0 + z1) + (z2 + z3)) + count;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const long long q = qbase + eq[k];
-    if (k < ne && ec[k] >= d && q < m)
-      out[(head * m + q) * dv + (ec[k] - d)] = acc[k] / zq[eq[k]];
-  }
-  // with a centre c the moments are those of k - c: the returned Zhat carries
-  // e^{<q,c>}, which cancels in ohat
-  if (tid < qg && qbase + tid < m) {
+    float zz = ((z0 + z1) + (z2 + z3)) + count;
+    zq = zz;
+    // with a centre c the moments are those of k - c: the returned Zhat carries
+    // e^{<q,c>}, which cancels in ohat
     float f = 1.f;
     if (center != nullptr) {
-      const float* q = Q + (head * m + qbase + tid) * d;
+      const float* qv = Q + (head * m + q) * d;
       float dot = 0.f;
-      for (int e = 0; e < d; ++e) dot += q[e] * center[head * d + e];
+      for (int e = 0; e < d; ++e) dot += qv[e] * center[head * d + e];
       f = expf(dot);
     }
-    Z[head * m + qbase + tid] = zq[tid] * f;
+    Z[head * m + q] = zz * f;
   }
+  __syncthreads();
+  if (tid >= d && tid < cols) out[(head * m + q) * dv + (tid - d)] = v / zq;
 }

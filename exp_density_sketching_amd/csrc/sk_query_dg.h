@@ -207,12 +207,20 @@ void sk_query_dg_kernel(const float* __restrict__ Q, long long m,
 }
 
 // sk_query_dgr_kernel<LOGD>: the same contraction for d <= 64 with the query
-// components in registers instead of an LDS tile.  A stage holds R = max(32, d)
-// rows (it starts at a multiple of d, so a row's last digit is its row within the
+// components in registers instead of an LDS tile.  A stage holds R = 64 rows (32
+// at d = 4; it starts at a multiple of R, so a row's last digit is its row within the
 // stage mod d, a compile-time index after unrolling); lane (l32, lhi) keeps its
-// query's d / 2 components of parity lhi.  The prefixes P_F (one per d rows) and
-// the epilogue's column weights read the query from global memory.  With no query
-// tile in LDS only the two stage buffers remain there, so more workgroups fit.
+// query's d / 2 components of parity lhi.  With no query tile in LDS only the two
+// stage buffers remain there, so more workgroups fit.
+//
+// Every global read is a raw buffer load against a resource whose range ends
+// where the data ends (the tile's rows, the workgroup's queries): a load past it
+// returns zero, so a partial stage, the columns outside a narrow tile and the
+// queries past m need no branches; a lane with nothing to load points its offset
+// past every range (DG_OOB).  The next stage's rows and the query components of
+// its prefixes P_F are loaded while the current stage runs, and the state rows of
+// a stage are read from LDS one group of k-steps ahead of the MFMAs that use them
+// (scheduling barriers keep that order).
 //
 // A level of C = 8 or 16 columns fills only part of a 32-column MFMA tile; such a
 // level's tiles (T.t == 1) move its last digit b' to the column side: rows are
@@ -220,87 +228,154 @@ void sk_query_dg_kernel(const float* __restrict__ Q, long long m,
 // epilogue weights column (b', e) with q[b'] and sums over b' (lane shuffles
 // inside each 32-lane half, then over the wave's column tiles) into a [128][C]
 // partial.
+#define DG_OOB 0x80000000u
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dg_rsrc(const float* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float4 dg_ld4(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  // (the whole vector is reinterpreted at once: bit casts of single elements of
+  // the loaded vector compiled to one dword load broadcast to all four)
+  const floatx4v v =
+      __builtin_bit_cast(floatx4v, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// High digits of F whose query components are loaded a stage ahead; deeper
+// digits (levels of narrow keys beyond these) are loaded when used.
+template <int LOGD>
+struct DgDigits {
+  static constexpr int d = 1 << LOGD;
+  // rows per stage: 64 (d itself at d = 64), 32 at d = 4 (whose stages would
+  // otherwise take 16 prefixes of two varying digits)
+  static constexpr int R = LOGD >= 3 ? (d > 64 ? d : 64) : SK_DGK;
+  static constexpr int NF = R >> LOGD;                 // prefixes per stage
+  static constexpr int LV = NF > d ? 2 : 1;            // low digits of F varying in a stage
+  static constexpr int MAXH = LOGD >= 6 ? 2 : (LOGD == 5 ? 3 : 4);
+};
+
 template <int LOGD, int NT>
 __device__ __forceinline__ void dgr_tile_loop(const QryTile& T, const float* __restrict__ Xh,
-                                              const float* __restrict__ qg, float* Bs,
-                                              const float* qr, int gw, int tid, int lhi,
-                                              int l32, floatx16* acc) {
+                                              __amdgpu_buffer_rsrc_t rq, unsigned qoff,
+                                              float* Bs, const float* qr, int gw, int tid,
+                                              int lhi, int l32, floatx16* acc) {
+  using G = DgDigits<LOGD>;
   constexpr int d = 1 << LOGD;
-  constexpr int R = d > SK_DGK ? d : SK_DGK;     // rows per stage
+  constexpr int R = G::R, NF = G::NF, LV = G::LV, MAXH = G::MAXH;
   constexpr int LDB = 32 * SK_DGNT + 32;
-  constexpr int NF = R >> LOGD;                   // prefixes per stage
-  constexpr int KPF = R / 2 / NF;                 // k-steps per prefix
+  constexpr int KS = R / 2;                       // k-steps per stage
+  constexpr int KG = 4;                           // k-steps per group of LDS reads
+  constexpr int NG = KS / KG;
   constexpr int W4 = 8 * NT;                      // float4 per stage row
-  constexpr int PV = (R * W4 + SK_WG - 1) / SK_WG;
-  // row length N (C, or d C with the last digit on the column side), w GEMM
+  constexpr int PV = R * W4 / SK_WG;              // float4 per thread and stage
+  static_assert(R * W4 % SK_WG == 0 && KS % KG == 0, "stage shape");
+  // row length N (C, or d C with the last digit on the column side), gw GEMM
   // columns from col0, s digits on the row side
   const long long N = T.N;
-  const int col0 = T.col0, w = gw;
-  const int ndig = T.s > 0 ? T.s - 1 : 0;
-  float4 pre[PV];
-  auto fetch = [&](long long r0) {
-#pragma unroll
-    for (int v = 0; v < PV; ++v) {
-      const int i = tid + v * SK_WG;
-      const int row = i / W4, c4 = i - row * W4;
-      pre[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row < R && r0 + row < T.a1 && 4 * c4 < w)
-        pre[v] = *reinterpret_cast<const float4*>(Xh + (r0 + row) * N + col0 + 4 * c4);
-    }
-  };
-  auto store = [&](float* dst) {
-#pragma unroll
-    for (int v = 0; v < PV; ++v) {
-      const int i = tid + v * SK_WG;
-      const int row = i / W4, c4 = i - row * W4;
-      if (row < R) *reinterpret_cast<float4*>(dst + row * LDB + 4 * c4) = pre[v];
-    }
-  };
   if (T.s == 0) {
     // no digit on the row side: one row, feature 1
-    fetch(0);
-    store(Bs);
+    if (tid < W4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * tid < gw) v = *reinterpret_cast<const float4*>(Xh + T.col0 + 4 * tid);
+      *reinterpret_cast<float4*>(Bs + 4 * tid) = v;
+    }
     __syncthreads();
     const float a = lhi == 0 ? 1.f : 0.f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma32x32x2(a, Bs[lhi * LDB + 32 * t + l32], acc[t]);
+    for (int t = 0; t < NT; ++t)
+      acc[t] = mfma32x32x2(a, lhi == 0 ? Bs[32 * t + l32] : 0.f, acc[t]);
     return;
   }
-  if (T.a0 < T.a1) fetch(T.a0);
-  int buf = 0;
-  for (long long r0 = T.a0; r0 < T.a1; r0 += R, buf ^= 1) {
-    // prefixes of the stage's d-row blocks, from the query in global memory
-    float pf[NF];
+  const int ndig = T.s - 1;                       // digits of F
+  const long long nrows = T.a1 - T.a0;
+  const int nst = (int)((nrows + R - 1) / R);
+  // the tile's rows: loads past row a1 return zero
+  const __amdgpu_buffer_rsrc_t rx = dg_rsrc(Xh + T.a0 * N, (unsigned)(nrows * N * 4));
+  const unsigned sbytes = (unsigned)(R * N * 4);  // bytes per stage
+  unsigned voff[PV];
+#pragma unroll
+  for (int v = 0; v < PV; ++v) {
+    const int i = tid + v * SK_WG;
+    const int row = i / W4, c4 = i - row * W4;
+    voff[v] = (4 * c4 < gw) ? (unsigned)((row * N + T.col0 + 4 * c4) * 4) : DG_OOB;
+  }
+  float4 pre[PV];
+  auto fetch = [&](int st) {
+#pragma unroll
+    for (int v = 0; v < PV; ++v) pre[v] = dg_ld4(rx, voff[v] + (unsigned)st * sbytes);
+  };
+  // query component c of the lane's query (c wave-uniform)
+  auto qld = [&](int c) { return sk_ld(rq, qoff, (unsigned)c * 4u); };
+  // prefix components of stage st: the LV low digits of F0 + f (f < NF) and the
+  // MAXH digits above them; unconditional loads (digit 0 where none is needed),
+  // the unused ones replaced by 1 when the prefixes are formed
+  float plo[NF * LV], phi[MAXH];
+  auto pfetch = [&](int st) {
+    const long long F0 = (T.a0 + (long long)st * R) >> LOGD;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int i = 0; i < LV; ++i)
+        plo[f * LV + i] = qld(i < ndig ? (int)(((F0 + f) >> (LOGD * i)) & (d - 1)) : 0);
+#pragma unroll
+    for (int i = 0; i < MAXH; ++i)
+      phi[i] = qld(LV + i < ndig ? (int)((F0 >> (LOGD * (LV + i))) & (d - 1)) : 0);
+  };
+  auto pform = [&](int st, float* pf) {
+    const long long F0 = (T.a0 + (long long)st * R) >> LOGD;
+    float h = 1.f;
+#pragma unroll
+    for (int i = 0; i < MAXH; ++i) h *= (LV + i < ndig) ? phi[i] : 1.f;
+    for (int i = LV + MAXH; i < ndig; ++i) h *= qld((int)((F0 >> (LOGD * i)) & (d - 1)));
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      long long F = (r0 >> LOGD) + f;
-      float pp = 1.f;
-      for (int i = 0; i < ndig; ++i) {
-        pp *= qg[F & (d - 1)];
-        F >>= LOGD;
-      }
-      pf[f] = pp;
+      float x = h;
+#pragma unroll
+      for (int i = 0; i < LV; ++i) x *= (i < ndig) ? plo[f * LV + i] : 1.f;
+      pf[f] = x;
     }
-    const float* B = Bs + buf * (R * LDB);
-    store(Bs + buf * (R * LDB));
+  };
+  fetch(0);
+  pfetch(0);
+  for (int st = 0; st < nst; ++st) {
+    float* B = Bs + (st & 1) * (R * LDB);
+#pragma unroll
+    for (int v = 0; v < PV; ++v) {
+      const int i = tid + v * SK_WG;
+      const int row = i / W4, c4 = i - row * W4;
+      *reinterpret_cast<float4*>(B + row * LDB + 4 * c4) = pre[v];
+    }
+    float pf[NF];
+    pform(st, pf);
     __syncthreads();
-    if (r0 + R < T.a1) fetch(r0 + R);
-    float bv[3][NT];
+    if (st + 1 < nst) {
+      fetch(st + 1);
+      pfetch(st + 1);
+    }
+    // k-step ks multiplies rows 2 ks and 2 ks + 1 (lane half lhi): last digit
+    // (2 ks + lhi) mod d, i.e. register ks mod d/2, prefix ks / (d/2)
+    const float* Bl = B + lhi * LDB + l32;
+    float bv[2][KG][NT];
+    auto rd = [&](int g, float (*dst)[NT]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int k = 0; k < KG; ++k)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bv[u][t] = B[(2 * u + lhi) * LDB + 32 * t + l32];
+        for (int t = 0; t < NT; ++t) dst[k][t] = Bl[2 * (g * KG + k) * LDB + 32 * t];
+    };
+    rd(0, bv[0]);
 #pragma unroll
-    for (int ks = 0; ks < R / 2; ++ks) {
-      if (ks + 2 < R / 2) {
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) rd(g + 1, bv[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          bv[(ks + 2) % 3][t] = B[(2 * (ks + 2) + lhi) * LDB + 32 * t + l32];
+      for (int k = 0; k < KG; ++k) {
+        const int ks = g * KG + k;
+        const float a = pf[ks / (d / 2)] * qr[ks % (d / 2)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma32x32x2(a, bv[g & 1][k][t], acc[t]);
       }
-      // row 2 ks + lhi: last digit (2 ks + lhi) mod d, i.e. register (ks mod d/2)
-      const float a = pf[ks / KPF] * qr[ks % (d / 2)];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mfma32x32x2(a, bv[ks % 3][t], acc[t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -324,12 +399,15 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
   const long long head = lg / ((long long)nqt * ntiles);
   const QryTile T = tiles[tile_id];
   const long long q0 = (long long)qt * SK_DGQ;
-  const long long qa = q0 + wave * 32 + l32;  // the lane's query (A operand row)
-  const bool qok = qa < m;
-  const float* qg = Q + (head * m + (qok ? qa : 0)) * d;
+  // the workgroup's queries: loads past query m - 1 return zero
+  const long long nq = m - q0 < SK_DGQ ? m - q0 : SK_DGQ;
+  const float* Qh = Q + (head * m + q0) * d;
+  const __amdgpu_buffer_rsrc_t rq = dg_rsrc(Qh, (unsigned)(nq * d * 4));
+  const int ql0 = wave * 32 + l32;            // the lane's query (A operand row)
+  const unsigned qoff = (unsigned)(ql0 * d * 4);
   float qr[d / 2];
 #pragma unroll
-  for (int i = 0; i < d / 2; ++i) qr[i] = qok ? qg[2 * i + lhi] : 0.f;
+  for (int i = 0; i < d / 2; ++i) qr[i] = sk_ld(rq, qoff + 4u * lhi, 8u * i);
   const float* Xh = X + head * head_stride + T.xoff;
   floatx16 acc[SK_DGNT];
 #pragma unroll
@@ -338,14 +416,13 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
   // last digit on the column side
   const int gw = T.t ? T.nalo * T.C : T.fw;
   if ((gw + 31) / 32 == 1)
-    dgr_tile_loop<LOGD, 1>(T, Xh, qg, Bs, qr, gw, tid, lhi, l32, acc);
+    dgr_tile_loop<LOGD, 1>(T, Xh, rq, qoff, Bs, qr, gw, tid, lhi, l32, acc);
   else
-    dgr_tile_loop<LOGD, SK_DGNT>(T, Xh, qg, Bs, qr, gw, tid, lhi, l32, acc);
+    dgr_tile_loop<LOGD, SK_DGNT>(T, Xh, rq, qoff, Bs, qr, gw, tid, lhi, l32, acc);
 
   // epilogue: column weights (from the queries in global memory), then the
   // [128][fw] partial of columns fc0 ..
   float* P = parts + (head * nqt + qt) * PB + T.pofs;
-  const float* Qh = Q + (head * m + q0) * d;
   if (T.t) {
     // column (b', e) = col0 + 32 t + l32 (C divides 32): weight q[b'] times e's
     // weight, summed over b' into the [128][C] partial

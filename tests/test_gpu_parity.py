@@ -108,7 +108,8 @@ def test_state_matches_oracle_moments(ident, n, h):
 # (16, 64, 3) .. (32, 32, 2) put 64 or more columns (d + dv, or dv at the top) on
 # levels j >= 1, where the query contracts the whole level without folding a
 # digit; (4, 4, 7) .. (16, 16, 3) have levels of 8 or 16 columns, whose last digit
-# the query moves to the column side (d C = 32 up to 512 columns)
+# the query moves to the column side for d >= 16 (d C = 128 up to 1024 columns)
+# and contracts with folded trailing digits for d <= 8
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
                                     (128, 128, 1), (32, 8, 2), (32, 16, 2),
                                     (64, 16, 1), (128, 16, 1),
