@@ -288,25 +288,25 @@ bool use_query_dg() {
 // Per-call partials (query, exact path).  A hipMallocAsync that follows a
 // hipFreeAsync on the same stream makes the host wait here until that stream has
 // drained (measured: back-to-back calls then return only as each previous call's
-// kernels finish), so the partials live in a buffer kept across calls: the
-// event recorded after each use orders the next user behind it.  Requests above
-// kKeepBytes take a stream-ordered allocation of their own (their kernels run
-// longer than that wait).
+// kernels finish), so the partials live in a buffer kept across calls.  Every
+// use of a kept buffer is on one stream (the handle's stream, which waits for
+// the previous one on a change; or the stream an exact-path buffer belongs to),
+// so stream order alone serialises its users: no event is recorded or waited
+// for per call (each would add a barrier packet between the kernels).  Requests
+// above kKeepBytes take a stream-ordered allocation of their own (their kernels
+// run longer than that wait).
 constexpr size_t kKeepBytes = size_t(256) << 20;
 
 struct Workspace {
   float* ptr = nullptr;
   size_t cap = 0;                          // bytes
-  hipEvent_t done = nullptr;               // recorded after the last use
 };
 
-// Points *out at `bytes` of device memory for one call on stream st: the kept
-// buffer (grown, once the work that last used it has finished, when too small)
-// or, beyond kKeepBytes, its own stream-ordered allocation (*own = true).
-// `ordered`: every use of ws is on st (stream order alone serialises them);
-// otherwise st first waits for the last use.
-int take_workspace(Workspace* ws, size_t bytes, hipStream_t st, bool ordered, float** out,
-                   bool* own) {
+// Points *out at `bytes` of device memory for one call on stream st, the stream
+// of every earlier use of ws: the kept buffer (grown, once the stream has
+// finished the work that used it, when too small) or, beyond kKeepBytes, its own
+// stream-ordered allocation (*own = true).
+int take_workspace(Workspace* ws, size_t bytes, hipStream_t st, float** out, bool* own) {
   *out = nullptr;
   *own = false;
   if (bytes > kKeepBytes) {
@@ -317,12 +317,8 @@ int take_workspace(Workspace* ws, size_t bytes, hipStream_t st, bool ordered, fl
     *own = true;
     return SK_OK;
   }
-  if (ws->done == nullptr)
-    SK_TRY(hipEventCreateWithFlags(&ws->done, hipEventDisableTiming));
-  else if (!ordered)
-    SK_TRY(hipStreamWaitEvent(st, ws->done, 0));
   if (bytes > ws->cap) {
-    SK_TRY(hipEventSynchronize(ws->done));
+    SK_TRY(hipStreamSynchronize(st));
     (void)hipFree(ws->ptr);
     ws->ptr = nullptr;
     ws->cap = 0;
@@ -338,23 +334,22 @@ int take_workspace(Workspace* ws, size_t bytes, hipStream_t st, bool ordered, fl
 }
 
 // Ends the call's use of what take_workspace gave it (work already enqueued).
-void release_workspace(Workspace* ws, float* p, bool own, hipStream_t st) {
-  if (own)
-    (void)hipFreeAsync(p, st);
-  else if (p != nullptr)
-    (void)hipEventRecord(ws->done, st);
+void release_workspace(float* p, bool own, hipStream_t st) {
+  if (own) (void)hipFreeAsync(p, st);
 }
 
+// Frees the kept buffer; no work that uses it may be in flight.
 void free_workspace(Workspace* ws) {
-  if (ws->done != nullptr) (void)hipEventSynchronize(ws->done);
   (void)hipFree(ws->ptr);
-  if (ws->done != nullptr) (void)hipEventDestroy(ws->done);
   *ws = Workspace{};
 }
 
 // exact_attend's kept partials, per (device, stream): at most kMaxXws buffers;
 // a new (device, stream) pair beyond that takes the place of the one used least
-// recently, once that buffer's last use has finished
+// recently, after the device has finished all its work.  (A stream's handle
+// names one live stream object for as long as work queued on it runs: the
+// runtime keeps a destroyed stream's object until that work is done, so a new
+// stream cannot take the handle of one whose kernels still use the buffer.)
 constexpr size_t kMaxXws = 8;
 struct XwsEntry {
   Workspace ws;
@@ -372,9 +367,9 @@ bool g_xtiming = false;
 std::vector<hipEvent_t> g_xev[2];
 int g_xrec = 0;
 
-// The kept partials buffer of (dev, stream); the caller holds g_xws_mutex.
-Workspace* xws_for(int dev, void* stream) {
-  const auto key = std::make_pair(dev, stream);
+// The kept partials of (dev, stream); the caller holds g_xws_mutex.
+int xws_for(int dev, hipStream_t stream, XwsEntry** out) {
+  const auto key = std::make_pair(dev, reinterpret_cast<void*>(stream));
   auto it = g_xws.find(key);
   if (it == g_xws.end()) {
     if (g_xws.size() >= kMaxXws) {
@@ -384,14 +379,16 @@ Workspace* xws_for(int dev, void* stream) {
       int cur = 0;
       (void)hipGetDevice(&cur);
       if (old->first.first != cur) (void)hipSetDevice(old->first.first);
-      free_workspace(&old->second.ws);          // waits for its last use
+      (void)hipDeviceSynchronize();             // its stream may be gone: all work
+      free_workspace(&old->second.ws);
       if (old->first.first != cur) (void)hipSetDevice(cur);
       g_xws.erase(old);
     }
     it = g_xws.emplace(key, XwsEntry{}).first;
   }
   it->second.last_use = ++g_xws_clock;
-  return &it->second.ws;
+  *out = &it->second;
+  return SK_OK;
 }
 
 }  // namespace
@@ -1581,7 +1578,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
   float* parts = nullptr;
   bool own = false;
   {
-    const int rc = take_workspace(&s->qws, pbytes, s->stream, true, &parts, &own);
+    const int rc = take_workspace(&s->qws, pbytes, s->stream, &parts, &own);
     if (rc != SK_OK) return rc;
   }
   timing_mark(s, 1, false);
@@ -1612,7 +1609,7 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
                      parts, qp.d_fin, ntiles, (int)nqt, qp.pb, (long long)m, s->d, s->dv,
                      (float)s->count, Q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
-  release_workspace(&s->qws, parts, own, s->stream);
+  release_workspace(parts, own, s->stream);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   return SK_OK;
 }
@@ -1826,19 +1823,17 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   kps = (kps + 31) / 32 * 32;
   const int nsplit = kps > 0 ? (int)((n + kps - 1) / kps) : 1;
   const size_t pbytes = sizeof(float) * (size_t)h * m * nsplit * (2 + dv);
-  // one kept partials buffer per (device, stream), held until the process ends;
-  // the lock covers the whole call, so calls from several threads on one stream
-  // do not interleave their kernels on it.  The stream still waits for the
-  // buffer's last use: a destroyed stream's handle value can come back as a new
-  // stream while the old one's kernels run.
+  // one kept partials buffer per (device, stream), held until released; the
+  // lock covers the whole call, so calls from several threads on one stream do
+  // not interleave their kernels on it
   std::unique_lock<std::mutex> ws_lock(g_xws_mutex, std::defer_lock);
-  Workspace* ws = nullptr;
+  XwsEntry* xe = nullptr;
   float* parts = fixed;
   bool own = false;
   if (fixed == nullptr) {
     ws_lock.lock();
-    ws = xws_for(dev, reinterpret_cast<void*>(st));
-    rc = take_workspace(ws, pbytes, st, false, &parts, &own);
+    rc = xws_for(dev, st, &xe);
+    if (rc == SK_OK) rc = take_workspace(&xe->ws, pbytes, st, &parts, &own);
     if (rc != SK_OK) return rc;
   }
   const long long nn = n;
@@ -1917,7 +1912,7 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();
-  if (ws != nullptr) release_workspace(ws, parts, own, st);
+  if (xe != nullptr) release_workspace(parts, own, st);
   if (e1 != hipSuccess || e2 != hipSuccess) return SK_EHIP;
   return SK_OK;
 }
@@ -2004,7 +1999,8 @@ int exact_release_workspaces(void) {
   SK_TRY(hipGetDevice(&cur));
   for (auto& kv : g_xws) {
     if (kv.first.first != cur) (void)hipSetDevice(kv.first.first);
-    free_workspace(&kv.second.ws);              // waits for its last use
+    SK_TRY(hipDeviceSynchronize());             // the buffers' last uses
+    free_workspace(&kv.second.ws);
   }
   g_xws.clear();
   SK_TRY(hipSetDevice(cur));

@@ -40,6 +40,89 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The fold of one (head, query)'s slice records P[nsplit][2 + dv] by one
+// workgroup of 256 threads, in one pass over the records: thread (g, slot) walks
+// slices g, g + G, g + 2G, ... (G = 256 / (1 + dv) groups) keeping its own
+// running maximum m and the sum of slot 0 (l) or slot 1 + c (acc[c]) rescaled to
+// it; the records come in blocks of sixteen (each block's terms rescaled to the
+// block's new maximum at once), the next block's loads issued before the current
+// block is added (the records were written on other XCDs, so each load is a
+// long round trip).
+// Then the largest m of the workgroup is found, every thread's sum is rescaled
+// to it, and the G group sums are added in group order.  Fixed order
+// throughout, so the result does not depend on timing.  red: 256 floats of LDS,
+// lsum: one.
+__device__ __forceinline__ void exact_fold(const float* __restrict__ P, int nsplit, int dv,
+                                           float* __restrict__ o, float* __restrict__ z,
+                                           float* red, float* lsum) {
+  constexpr int FB = 16;                       // records per block
+  const int tid = threadIdx.x;
+  const int rec = 2 + dv;
+  const int slots = 1 + dv;
+  const int groups = 256 / slots > 0 ? 256 / slots : 1;
+  const int g = tid / slots, slot = tid - g * slots;
+  float m = -INFINITY, acc = 0.f;
+  // slices of this thread: g + G t for t < nt
+  const int nt = g < groups && g < nsplit ? (nsplit - g + groups - 1) / groups : 0;
+  auto load = [&](int t0, float (&mu)[FB], float (&x)[FB]) {
+#pragma unroll
+    for (int u = 0; u < FB; ++u) {
+      // past the last slice: re-read this thread's first one, ignored when added
+      const int t = t0 + u < nt ? t0 + u : 0;
+      const float* r = P + (long long)(g + t * groups) * rec;
+      mu[u] = r[0];
+      x[u] = r[1 + slot];
+    }
+  };
+  // a block: its largest maximum first, then its terms rescaled to the new
+  // running maximum (independent exponentials) and the running sum once
+  auto add = [&](int t0, const float (&mu)[FB], const float (&x)[FB]) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < FB; ++u)
+      if (t0 + u < nt) bm = fmaxf(bm, mu[u]);
+    if (bm == -INFINITY) return;
+    const float nm = fmaxf(m, bm);
+    float sb = 0.f;
+#pragma unroll
+    for (int u = 0; u < FB; ++u)
+      if (t0 + u < nt) sb += x[u] * expf(mu[u] - nm);
+    acc = acc * expf(m - nm) + sb;
+    m = nm;
+  };
+  if (nt > 0) {
+    float mu0[FB], x0[FB], mu1[FB], x1[FB];
+    load(0, mu0, x0);
+    for (int t0 = 0; t0 < nt; t0 += 2 * FB) {
+      if (t0 + FB < nt) load(t0 + FB, mu1, x1);
+      add(t0, mu0, x0);
+      if (t0 + FB < nt) {
+        if (t0 + 2 * FB < nt) load(t0 + 2 * FB, mu0, x0);
+        add(t0 + FB, mu1, x1);
+      }
+    }
+  }
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float ms = red[0];
+  __syncthreads();
+  red[tid] = (m == -INFINITY) ? 0.f : acc * expf(m - ms);
+  __syncthreads();
+  float sum = 0.f;
+  if (tid < slots) {
+    for (int gg = 0; gg < groups; ++gg) sum += red[gg * slots + tid];
+    if (tid == 0) *lsum = sum;
+  }
+  __syncthreads();
+  if (tid == 0) *z = (ms == -INFINITY) ? 0.f : expf(ms) * *lsum;
+  else if (tid < slots) o[tid - 1] = sum / *lsum;
+  __syncthreads();
+}
+
 // sk_exact_mfma (many queries per head): one workgroup = 4 waves x 32 queries,
 // one key slice; per stage of 32 keys (K and V rows staged in LDS):
 //   S^T = K Q^T         v_mfma_f32_32x32x2_f32, rows = keys, columns = queries;
@@ -570,61 +653,13 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
   }
 }
 
-// One workgroup per (head, query).  The slices' maxima are reduced first; then
-// thread (g, slot) sums slot 0 (l) or slot 1 + c (acc[c]) over slices g, g + G,
-// ... with the rescale e^(mu_s - mu*), and the G group sums are added in group
-// order.  Fixed order throughout, so the result does not depend on timing.
+// One workgroup per (head, query): exact_fold of its slice records.
 __global__ __launch_bounds__(256)
 void sk_exact_combine(const float* __restrict__ parts, int nsplit, long long m, int dv,
                       int h, float* __restrict__ out, float* __restrict__ Z) {
   __shared__ float red[256];
   __shared__ float lsum;
   const long long hq = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int rec = 2 + dv;
-  const float* P = parts + hq * (long long)nsplit * rec;
-  float mx = -INFINITY;
-  for (int sp = tid; sp < nsplit; sp += 256) mx = fmaxf(mx, P[(long long)sp * rec]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float ms = red[0];
-  __syncthreads();
-  const int slots = 1 + dv;
-  const int groups = 256 / slots > 0 ? 256 / slots : 1;
-  const int g = tid / slots, slot = tid - g * slots;
-  float acc = 0.f;
-  if (g < groups && ms != -INFINITY) {
-    int sp = g;
-    // eight slice records in flight per thread (each load is a long round trip:
-    // the records were written on other XCDs), added in slice order
-    for (; sp + 7 * groups < nsplit; sp += 8 * groups) {
-      float mu[8], x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* r = P + (long long)(sp + u * groups) * rec;
-        mu[u] = r[0];
-        x[u] = r[1 + slot];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += x[u] * expf(mu[u] - ms);
-    }
-    for (; sp < nsplit; sp += groups) {
-      const float* r = P + (long long)sp * rec;
-      acc += r[1 + slot] * expf(r[0] - ms);
-    }
-  }
-  red[tid] = acc;
-  __syncthreads();
-  float sum = 0.f;
-  if (tid < slots) {
-    for (int gg = 0; gg < groups; ++gg) sum += red[gg * slots + tid];
-    if (tid == 0) lsum = sum;
-  }
-  __syncthreads();
-  if (tid == 0) Z[hq] = (ms == -INFINITY) ? 0.f : expf(ms) * lsum;
-  else if (tid < slots) out[hq * dv + (tid - 1)] = sum / lsum;
+  exact_fold(parts + hq * (long long)nsplit * (2 + dv), nsplit, dv, out + hq * dv, Z + hq, red,
+             &lsum);
 }

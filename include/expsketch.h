@@ -220,11 +220,12 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
  *   K [h][n][d], V [h][n][dv], Q [h][m][d], out [h][m][dv], Z [h][m]: device.
  *   hip_stream: hipStream_t to run on (NULL = default stream).
  * The per-slice partials (h * m * slices * (2 + dv) floats) live in a buffer
- * the library keeps per (device, stream), grown on demand up to 256 MB; larger
- * ones are taken from the stream-ordered allocator (hipMallocAsync) for the
- * call.  At most 8 such buffers are kept: a call on a ninth (device, stream)
- * frees the one used least recently, after waiting for its last use.  Calls
- * from several host threads are serialised while they enqueue their kernels.
+ * the library keeps per (device, stream), grown on demand up to 256 MB (growing
+ * waits on the host for the stream's earlier work); larger ones are taken from
+ * the stream-ordered allocator (hipMallocAsync) for the call.  At most 8 such
+ * buffers are kept: a call on a ninth (device, stream) frees the one used least
+ * recently, after waiting on the host for all work of the device.  Calls from
+ * several host threads are serialised while they enqueue their kernels.
  * Errors: SK_EINVAL (shapes, NULL/misaligned pointers, n or m < 0), SK_ENOMEM,
  * SK_EHIP.
  */
@@ -266,7 +267,7 @@ int exact_kernel_times(float* ms, int cap, int* count);
 
 /*
  * exact_release_workspaces -- frees every partials buffer exact_attend keeps
- * (waiting on the host for each buffer's last use first).  Later calls allocate
+ * (waiting on the host for all work of each device first).  Later calls allocate
  * again.  For a caller that wants the memory back, e.g. before its streams are
  * destroyed.
  * Errors: SK_EHIP.
