@@ -136,7 +136,7 @@ size_t sym_update_lds_bytes(int d, int dv) {
 }
 size_t sym_query_lds_bytes(int d) {
   // Qs + At + Bt (widest column tile, 128 columns: row stride 144) + row codes
-  return sizeof(float) * ((size_t)d * (SY_TQ + 1) + (size_t)SY_QKB * (SY_TQ + 16) +
+  return sizeof(float) * ((size_t)d * (SY_TQ + 4) + (size_t)SY_QKB * (SY_TQ + 16) +
                           (size_t)SY_QKB * 144) +
          sizeof(unsigned long long) * SY_QKB;
 }

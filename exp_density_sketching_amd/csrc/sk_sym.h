@@ -331,7 +331,7 @@ void sk_sym_query_tile(const float* __restrict__ Q, long long m, int d,
                        const SymQryTile& T, const SymTables& tb, int qt, long long head,
                        long long PB, float* __restrict__ parts) {
   constexpr int TN = 16 * CB;
-  constexpr int LDQ = SY_TQ + 1;
+  constexpr int LDQ = SY_TQ + 4;                      // rows 16-byte aligned (float4 reads)
   constexpr int LDA = SY_TQ + 16;                     // rows 16 banks apart
   constexpr int LDB = TN <= 16 ? 16 : (TN + 63) / 64 * 64 + 16;
   constexpr int NB4 = SY_QKB * TN / 4;                // float4 of a weighted stage
@@ -394,7 +394,8 @@ void sk_sym_query_tile(const float* __restrict__ Q, long long m, int d,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = floatx4v{0.f, 0.f, 0.f, 0.f};
 
-  const int qq = tid % SY_TQ, kp = tid / SY_TQ;       // feature thread: query, row phase
+  const int fr = tid >> 3, fq = 16 * (tid & 7);       // feature thread: row, first query
+  static_assert(SY_QKB * SY_TQ / 16 == SK_WG, "one feature thread per row and 16 queries");
   const int r_end = T.row0 + T.nrows;
   __syncthreads();
   if (T.nrows > 0) fetch(T.row0);
@@ -412,18 +413,27 @@ void sk_sym_query_tile(const float* __restrict__ Q, long long m, int d,
       Rc[tid] = br < r_end ? tb.code[T.rc0 + br] : ~0ull;   // size 255: outside
     }
     __syncthreads();
-    // features q^beta of query qq for rows kp, kp + 2, ...
-#pragma unroll 4
-    for (int u = 0; u < SY_QKB / 2; ++u) {
-      const int row = kp + 2 * u;
-      const unsigned long long c = Rc[row];
+    // features q^beta: thread (row fr, queries fq .. fq + 15), the row's indices
+    // decoded once and each one's 16 query components read as four float4
+    {
+      const unsigned long long c = Rc[fr];
       const int cnt = (int)(c >> 56);
-      float f = 0.f;
+      float4 f[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        f[v] = cnt == 255 ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(1.f, 1.f, 1.f, 1.f);
       if (cnt != 255) {
-        f = 1.f;
-        for (int q = 0; q < cnt; ++q) f *= Qs[(int)((c >> (8 * q)) & 0xffu) * LDQ + qq];
+        for (int k = 0; k < cnt; ++k) {
+          const float* qs = Qs + (int)((c >> (8 * k)) & 0xffu) * LDQ + fq;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float4 x = *reinterpret_cast<const float4*>(qs + 4 * v);
+            f[v].x *= x.x; f[v].y *= x.y; f[v].z *= x.z; f[v].w *= x.w;
+          }
+        }
       }
-      At[row * LDA + qq] = f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) *reinterpret_cast<float4*>(At + fr * LDA + fq + 4 * v) = f[v];
     }
     __syncthreads();
     if (rb0 + SY_QKB < r_end) fetch(rb0 + SY_QKB);
