@@ -20,6 +20,7 @@
 #include "sk_query_dg.h"
 #include "sk_step.h"
 #include "sk_sym.h"
+#include "sk_sym_dg.h"
 #include "sk_update.h"
 #include "sk_update_kr.h"
 
@@ -443,6 +444,11 @@ struct sk_sketch {
   std::vector<SymQryTile> sqtiles;
   SymUpdTile* d_sutiles = nullptr;
   SymQryTile* d_sqtiles = nullptr;
+  // multiset blocks queried by the last index (sk_sym_dg.h): tiles and runs
+  std::vector<SymDgTile> sdtiles;
+  std::vector<SymDgRun> sdruns;
+  SymDgTile* d_sdtiles = nullptr;
+  SymDgRun* d_sdruns = nullptr;
   // decode steps (sketch_step): row-range tiles of the whole state, partials
   std::vector<StepTile> stiles;
   StepTile* d_stiles = nullptr;
@@ -805,6 +811,141 @@ void plan_sym_query_block(sk_sketch* s, long long xoff, int rc0, int nrows, int 
   }
 }
 
+// EXPSKETCH_SYM_DG=0 keeps every multiset block on the row-range query kernel
+// (tuning aid).
+bool use_sym_dg() {
+  static const bool v = [] {
+    const char* e = std::getenv("EXPSKETCH_SYM_DG");
+    return e == nullptr || std::atoi(e) != 0;
+  }();
+  return v;
+}
+
+// The multiset block of width C whose largest multiset size is jhi runs on the
+// last-index query kernel: C >= 64 columns (two full MFMA tiles per wave), d <= 64
+// (the query components in registers) and sizes up to 2, whose runs of one prefix
+// are long (about d / 2 rows: a stage is mostly rows that exist).  Measured: the
+// d = 64, p = 2 workload 0.157 -> 0.234 of the fp32 peak; the d = 32, p = 3
+// workload 0.149 -> 0.100 with both its blocks on it (the top block's 32 columns
+// and runs of about d / 3 rows give too few matrix instructions per stage), 0.105
+// with its lower block alone.
+bool sym_dg_block(const sk_sketch* s, int C, int jhi) {
+  return use_sym_dg() && C >= 64 && s->d <= 64 && jhi <= 2 && jhi <= sd_max_j(s->d);
+}
+
+using SymDgKernel = void (*)(const float*, long long, const float*, long long, const SymDgTile*,
+                             int, const SymDgRun*, int, long long, float*);
+SymDgKernel sym_dg_kernel_for(int logd) {
+  switch (logd) {
+    case 2: return sk_sym_dg_kernel<2>;
+    case 3: return sk_sym_dg_kernel<3>;
+    case 4: return sk_sym_dg_kernel<4>;
+    case 5: return sk_sym_dg_kernel<5>;
+    default: return sk_sym_dg_kernel<6>;
+  }
+}
+size_t sym_dg_lds_bytes() { return sizeof(float) * 2 * SD_R * (32 * SK_DGNT + 32); }
+
+// Last-index query tiles of the multiset sizes jlo .. jhi of one block (block row
+// 0 = canonical row rc0, float offset xoff): per size, its runs (one per
+// multiset of the size below, in order) and tiles of up to 64 columns and about
+// six full stages' work, each with a [128][fw] partial and a finishing record.
+void plan_sym_dg_block(sk_sketch* s, const SymHost& t, long long xoff, long long rc0, int C,
+                       int top, int jlo, int jhi) {
+  sk_sketch::QPlan& qp = s->qplans[0];
+  const int d = s->d;
+  const int NF = SD_R / d;
+  // canonical start of each size
+  std::vector<long long> start(s->p + 2, (long long)t.code.size());
+  for (long long r = (long long)t.code.size() - 1; r >= 0; --r)
+    start[(int)(t.code[r] >> 56)] = r;
+  for (int j = jlo; j <= jhi; ++j) {
+    const long long cnt = start[j + 1] - start[j];
+    const long long lxoff = xoff + (start[j] - rc0) * C;
+    const int run0 = (int)s->sdruns.size();
+    if (j == 0) {
+      s->sdruns.push_back(SymDgRun{0, 0, 0, 1.f, 0ull});
+    } else {
+      long long lr = 0;      // level row of the run's first multiset
+      for (long long b = start[j - 1]; b < start[j]; ++b) {
+        const int lb = j == 1 ? 0 : t.last[b];
+        SymDgRun R{};
+        R.row0 = (int)(lr - lb);
+        R.lb = lb;
+        R.mlb = j == 1 ? 0 : t.lmul[b];
+        R.winv = t.winv[b];
+        R.code = t.code[b] & 0x00ffffffffffffffull;
+        s->sdruns.push_back(R);
+        lr += d - lb;
+      }
+    }
+    const int nrun = (int)s->sdruns.size() - run0;
+    // tiles of about equal work: a stage costs the rows of its k-step groups
+    // that hold rows of their runs (the kernel skips the others) plus 32 rows'
+    // worth of fixed cost; a tile takes stages up to six full stages' cost (runs
+    // of one prefix shrink from d rows to 1 along a level, so equal run counts
+    // leave the first tiles several times the work of the last).  Measured on
+    // the d = 64, p = 2 workload (fraction of the fp32 peak): equal counts of 8
+    // runs 0.230, of 4 runs 0.187; by cost, 6 stages and 32 rows 0.247, 8 and 64
+    // 0.218, 8 and 16 0.187, 16 and 64 0.139 (the best fill one round of three
+    // workgroups per CU).  EXPSKETCH_SYM_DG_STAGES and EXPSKETCH_SYM_DG_OVH set
+    // the two numbers (tuning aids).
+    auto live_rows = [&](int r) {
+      // rows of the 8-row groups of run r's slot that reach its first index
+      const int lb = j == 0 ? 0 : s->sdruns[run0 + r].lb;
+      return d >= 8 ? d - lb / 8 * 8 : (lb < d ? 8 : 0);
+    };
+    std::vector<int> cut{0};
+    {
+      static const long long stages = [] {
+        const char* e = std::getenv("EXPSKETCH_SYM_DG_STAGES");
+        return e && std::atoll(e) > 0 ? std::atoll(e) : 6LL;
+      }();
+      static const long long ovh = [] {
+        const char* e = std::getenv("EXPSKETCH_SYM_DG_OVH");
+        return e && std::atoll(e) >= 0 ? std::atoll(e) : 32LL;
+      }();
+      const long long target = stages * (SD_R + ovh);
+      long long cost = 0;
+      for (int r = 0; r < nrun; r += NF) {
+        long long sc = ovh;
+        for (int f = 0; f < NF && r + f < nrun; ++f) sc += live_rows(r + f);
+        if (cost > 0 && cost + sc > target) {
+          cut.push_back(r);
+          cost = 0;
+        }
+        cost += sc;
+      }
+      cut.push_back(nrun);
+    }
+    for (int col0 = 0; col0 < C; col0 += 64) {
+      for (size_t ci = 0; ci + 1 < cut.size(); ++ci) {
+        const int r0 = cut[ci];
+        SymDgTile T{};
+        T.xoff = lxoff;
+        T.pofs = qp.pb;
+        T.nrows = (int)cnt;
+        T.C = C;
+        T.top = top;
+        T.j = j;
+        T.col0 = col0;
+        T.fw = std::min(64, C - col0);
+        T.run0 = run0 + r0;
+        T.nrun = cut[ci + 1] - r0;
+        s->sdtiles.push_back(T);
+        QryTile f{};
+        f.pofs = qp.pb;
+        f.C = C;
+        f.top = top;
+        f.fc0 = col0;
+        f.fw = T.fw;
+        qp.tiles.push_back(f);
+        qp.pb += (long long)SK_DGQ * T.fw;
+      }
+    }
+  }
+}
+
 // Builds the multiset layout's plans and device tables of a new handle.
 int build_sym(sk_sketch* s) {
   SymHost t;
@@ -826,8 +967,16 @@ int build_sym(sk_sketch* s) {
       s->sgroup.push_back((int)i);
   s->sgroup.push_back((int)s->sutiles.size());
   s->qplans.resize(1);
-  if (s->Rlo > 0) plan_sym_query_block(s, 0, 0, (int)s->Rlo, Cl, 0);
-  plan_sym_query_block(s, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
+  // both blocks by the last index, or both by row ranges (one launch either way;
+  // the two kernels side by side measured slower than the row-range kernel alone)
+  const bool dg = (s->Rlo == 0 || sym_dg_block(s, Cl, s->p - 1)) && sym_dg_block(s, s->dv, s->p);
+  if (dg) {
+    if (s->Rlo > 0) plan_sym_dg_block(s, t, 0, 0, Cl, 0, 0, s->p - 1);
+    plan_sym_dg_block(s, t, s->Rlo * Cl, s->Rlo, s->dv, 1, s->p, s->p);
+  } else {
+    if (s->Rlo > 0) plan_sym_query_block(s, 0, 0, (int)s->Rlo, Cl, 0);
+    plan_sym_query_block(s, s->Rlo * Cl, (int)s->Rlo, (int)s->Rtop, s->dv, 1);
+  }
   // one device allocation: code | prefix | last | lmul | rslot | winv | slots
   const size_t n = (size_t)s->Dsym, ns = t.slots.size();
   const size_t bytes = 8 * n + 4 * (5 * n + ns) + 64;
@@ -1163,6 +1312,12 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
                 sizeof(SymUpdTile) * s->sutiles.size()) &&
          upload((void**)&s->d_sqtiles, s->sqtiles.data(),
                 sizeof(SymQryTile) * s->sqtiles.size()) &&
+         upload((void**)&s->d_sdtiles, s->sdtiles.data(),
+                sizeof(SymDgTile) * s->sdtiles.size()) &&
+         upload((void**)&s->d_sdruns, s->sdruns.data(), sizeof(SymDgRun) * s->sdruns.size()) &&
+         hipFuncSetAttribute((const void*)sym_dg_kernel_for(s->logd),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)sym_dg_lds_bytes()) == hipSuccess &&
          hipFuncSetAttribute((const void*)sk_sym_query_kernel,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql) == hipSuccess;
   for (size_t g = 0; ok && sym && g + 1 < s->sgroup.size(); ++g) {
@@ -1198,6 +1353,7 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
     for (sk_sketch::QPlan& qp : s->qplans) { (void)hipFree(qp.d_fin); (void)hipFree(qp.d_run); }
     (void)hipFree(s->d_kunits);
     (void)hipFree(s->d_sutiles); (void)hipFree(s->d_sqtiles); (void)hipFree(s->symbuf);
+    (void)hipFree(s->d_sdtiles); (void)hipFree(s->d_sdruns);
     (void)hipFree(s->d_stiles); (void)hipFree(s->sparts);
     delete s;
     return SK_EHIP;
@@ -1238,6 +1394,8 @@ int sketch_destroy(sk_handle s) {
   }
   (void)hipFree(s->d_sutiles);
   (void)hipFree(s->d_sqtiles);
+  (void)hipFree(s->d_sdtiles);
+  (void)hipFree(s->d_sdruns);
   (void)hipFree(s->symbuf);
   (void)hipFree(s->d_stiles);
   (void)hipFree(s->sparts);
@@ -1572,7 +1730,8 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     ++pi;
   const sk_sketch::QPlan& qp = s->qplans[pi];
   const int ntiles = (int)qp.tiles.size();
-  const long long nlaunch = std::max<long long>(ntiles, (long long)s->sqtiles.size());
+  const long long nlaunch = std::max<long long>(
+      ntiles, std::max<long long>((long long)s->sqtiles.size(), (long long)s->sdtiles.size()));
   if (nqt * nlaunch * s->h > 0x7fffffffLL || m * s->h > 0x7fffffffLL) return SK_EINVAL;
   const size_t pbytes = sizeof(float) * (size_t)s->h * nqt * qp.pb;
   float* parts = nullptr;
@@ -1582,13 +1741,22 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     if (rc != SK_OK) return rc;
   }
   timing_mark(s, 1, false);
-  if (s->layout == SK_LAYOUT_SYM) {
+  hipError_t e1 = hipSuccess;
+  if (s->layout == SK_LAYOUT_SYM && !s->sqtiles.empty()) {
     const long long nst = (long long)s->sqtiles.size();
     hipLaunchKernelGGL(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
                        sym_query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->state,
                        s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, qp.pb, parts);
+    e1 = hipGetLastError();
   }
-  hipError_t e1 = hipGetLastError();
+  if (s->layout == SK_LAYOUT_SYM && !s->sdtiles.empty()) {
+    const long long nsd = (long long)s->sdtiles.size();
+    hipLaunchKernelGGL(sym_dg_kernel_for(s->logd), dim3((unsigned)(nsd * nqt * s->h)),
+                       dim3(SK_WG), sym_dg_lds_bytes(), s->stream, Q, (long long)m, s->state,
+                       s->XS, s->d_sdtiles, (int)nsd, s->d_sdruns, (int)nqt, qp.pb, parts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) e1 = e;
+  }
   for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < qp.groups.size(); ++g) {
     const sk_sketch::QGroup& G = qp.groups[g];
     QueryKernel kern = G.kind == 0   ? query_kernel_for(s->logd)
