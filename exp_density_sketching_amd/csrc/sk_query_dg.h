@@ -420,8 +420,23 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
   else
     dgr_tile_loop<LOGD, SK_DGNT>(T, Xh, rq, qoff, Bs, qr, gw, tid, lhi, l32, acc);
 
-  // epilogue: column weights (from the queries in global memory), then the
-  // [128][fw] partial of columns fc0 ..
+  // epilogue: column weights, then the [128][fw] partial of columns fc0 ..  The
+  // weights read other queries' components than the lane's own: the workgroup's
+  // query tile goes to LDS first (the stage buffers are free once every wave is
+  // past its last stage), zeros past query m - 1.
+  constexpr int LDQ = d + 1;
+  float* Qs = lds;                            // [SK_DGQ][LDQ]
+  if (T.t || (!T.top && T.fc0 < d)) {         // uniform
+    __syncthreads();
+    for (int i = tid; i < SK_DGQ * d / 4; i += SK_WG) {
+      const int ql = (4 * i) >> LOGD, c = (4 * i) & (d - 1);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ql < nq) v = *reinterpret_cast<const float4*>(Qh + (long long)ql * d + c);
+      float* dst = Qs + ql * LDQ + c;
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    }
+    __syncthreads();
+  }
   float* P = parts + (head * nqt + qt) * PB + T.pofs;
   if (T.t) {
     // column (b', e) = col0 + 32 t + l32 (C divides 32): weight q[b'] times e's
@@ -438,13 +453,8 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
         const bool zcol = (!T.top) && (e < d);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ql = wave * 32 + acc_row(r, lane);
-          float wq = 0.f;
-          if (q0 + ql < m) {
-            const float* qrow = Qh + (long long)ql * d;
-            wq = qrow[bp] * (zcol ? qrow[e] * T.wz : T.wn);
-          }
-          y[r] += acc[t][r] * wq;
+          const float* qrow = Qs + (wave * 32 + acc_row(r, lane)) * LDQ;
+          y[r] += acc[t][r] * (qrow[bp] * (zcol ? qrow[e] * T.wz : T.wn));
         }
       }
     }
@@ -472,8 +482,7 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ql = wave * 32 + acc_row(r, lane);
-        float w = T.wn;
-        if (zcol) w = (q0 + ql < m) ? Qh[(long long)ql * d + col] * T.wz : 0.f;
+        const float w = zcol ? Qs[ql * LDQ + col] * T.wz : T.wn;
         P[(long long)ql * T.fw + cr] = acc[t][r] * w;
       }
     }
