@@ -448,6 +448,9 @@ def coreset_leg(w, E, torch, Kg, Vg, Qg, out_s, z_s, out_e, z_e, steps, block=51
             E.coreset_update(cs[i], k, v)
         for i in range(1, S):
             E.coreset_merge(cs[0], cs[i])
+        # blocks of small calls wait to share launches; info() takes them in, so
+        # every reduce of the stream is inside the timed ingest
+        cs[0].info()
 
     ingest()
     torch.cuda.synchronize()

@@ -38,6 +38,10 @@ bool cs_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u)
 constexpr size_t kGramBytes = size_t(256) << 20;
 // raw blocks of one update call handled per round (bounds the live buffers)
 constexpr long long kRoundBlocks = 64;
+// full blocks of small calls wait, copied, until this many (or this many bytes)
+// have gathered or a reader needs the coreset: the reduces of several calls then
+// share launches (a call of 4096 keys alone gives four reduces, one per depth)
+constexpr size_t kPendBytes = size_t(64) << 20;
 
 }  // namespace
 
@@ -55,6 +59,7 @@ struct sk_coreset {
   std::vector<int> freebuf;
   int fill = -1;              // buffer of the partial block
   std::vector<int> level;     // buffer per level, -1 = empty
+  std::vector<int> pending;   // full blocks not yet entered at level 0, in order
   double* inv = nullptr;      // 1/j, j < CS_NINV
   double* gram = nullptr;     // Gram workspace
   size_t gram_bytes = 0;
@@ -213,46 +218,78 @@ int store_slots(sk_coreset* c, std::vector<Blk>& slots) {
   return SK_OK;
 }
 
-// Appends n rows per head of src (rows r0 ..) to the partial buffer; every full
-// buffer enters at level 0.  Whole blocks of the input past a full buffer enter
-// in place (read from the caller's memory by the reduces), in rounds of
-// kRoundBlocks.
+// The pending blocks enter level 0 in order (one schedule, reduces batched by
+// depth).
+int flush(sk_coreset* c) {
+  if (c->pending.empty()) return SK_OK;
+  std::vector<Blk> slots = slots_of(c);
+  std::vector<PlannedOp> ops;
+  for (int b : c->pending) {
+    const int rc = plan_carry(c, &slots, Blk{b, lib_ref(c, b), 0}, 0, &ops);
+    if (rc != SK_OK) return rc;
+  }
+  c->pending.clear();
+  int rc = run_ops(c, ops);
+  if (rc == SK_OK) rc = store_slots(c, slots);
+  return rc;
+}
+
+int pend(sk_coreset* c, int b) {
+  c->pending.push_back(b);
+  const size_t bytes = sizeof(float) * (size_t)c->h * c->B * (c->d + c->dv);
+  if ((long long)c->pending.size() >= kRoundBlocks || c->pending.size() * bytes >= kPendBytes)
+    return flush(c);
+  return SK_OK;
+}
+
+// Appends n rows per head of src to the partial buffer; every full buffer joins
+// the pending blocks.  With no blocks pending, rounds of kRoundBlocks whole
+// blocks of the input enter level 0 in place (read from the caller's memory by
+// the reduces); fewer whole blocks are copied and join the pending ones.  Blocks
+// enter the binary counter in stream order either way, so every reduce gets the
+// same inputs and serial number as when each block enters at once.
 int append_rows(sk_coreset* c, const CsRef& src, long long n) {
   long long i = 0;
   while (i < n) {
-    std::vector<Blk> slots = slots_of(c);
-    std::vector<PlannedOp> ops;
-    long long blocks = 0;
-    while (i < n && blocks < kRoundBlocks) {
-      if (c->nfill == 0 && n - i >= c->B) {          // a whole block of the input
-        Blk blk{-1, CsRef{src.K + i * c->d, src.V + i * c->dv, src.hsK, src.hsV}, 0};
-        const int rc = plan_carry(c, &slots, blk, 0, &ops);
+    if (c->nfill == 0 && n - i >= c->B) {
+      const long long nb = (n - i) / c->B;
+      if (c->pending.empty() && nb >= kRoundBlocks) {
+        std::vector<Blk> slots = slots_of(c);
+        std::vector<PlannedOp> ops;
+        for (long long k = 0; k < kRoundBlocks; ++k, i += c->B) {
+          Blk blk{-1, CsRef{src.K + i * c->d, src.V + i * c->dv, src.hsK, src.hsV}, 0};
+          const int rc = plan_carry(c, &slots, blk, 0, &ops);
+          if (rc != SK_OK) return rc;
+        }
+        int rc = run_ops(c, ops);
+        if (rc == SK_OK) rc = store_slots(c, slots);
         if (rc != SK_OK) return rc;
-        i += c->B;
-        ++blocks;
         continue;
       }
-      if (c->fill < 0) {
-        const int rc = take_buffer(c, &c->fill);
-        if (rc != SK_OK) return rc;
-      }
-      const int take = (int)std::min<long long>(c->B - c->nfill, n - i);
-      int rc = copy_rows(c, src, i, take, c->fill, c->nfill);
+      int b = -1;
+      int rc = take_buffer(c, &b);
+      if (rc == SK_OK) rc = copy_rows(c, src, i, c->B, b, 0);
+      if (rc == SK_OK) rc = pend(c, b);
       if (rc != SK_OK) return rc;
-      c->nfill += take;
-      i += take;
-      if (c->nfill == c->B) {
-        Blk blk{c->fill, lib_ref(c, c->fill), 0};
-        c->fill = -1;
-        c->nfill = 0;
-        rc = plan_carry(c, &slots, blk, 0, &ops);
-        if (rc != SK_OK) return rc;
-        ++blocks;
-      }
+      i += c->B;
+      continue;
     }
-    int rc = run_ops(c, ops);
-    if (rc == SK_OK) rc = store_slots(c, slots);
+    if (c->fill < 0) {
+      const int rc = take_buffer(c, &c->fill);
+      if (rc != SK_OK) return rc;
+    }
+    const int take = (int)std::min<long long>(c->B - c->nfill, n - i);
+    int rc = copy_rows(c, src, i, take, c->fill, c->nfill);
     if (rc != SK_OK) return rc;
+    c->nfill += take;
+    i += take;
+    if (c->nfill == c->B) {
+      const int b = c->fill;
+      c->fill = -1;
+      c->nfill = 0;
+      rc = pend(c, b);
+      if (rc != SK_OK) return rc;
+    }
   }
   return SK_OK;
 }
@@ -366,6 +403,8 @@ int coreset_reset(sk_coreset_handle c) {
   if (c == nullptr) return SK_EINVAL;
   for (int b : c->level)
     if (b >= 0) c->freebuf.push_back(b);
+  for (int b : c->pending) c->freebuf.push_back(b);
+  c->pending.clear();
   c->level.clear();
   c->nfill = 0;
   c->count = 0;
@@ -395,10 +434,14 @@ int coreset_merge(sk_coreset_handle dst, sk_coreset_handle src) {
     CS_TRY(hipStreamWaitEvent(dst->stream, src->switch_ev, 0));
   }
   // src's buffered points enter dst's buffer in order, then src's blocks carry in
-  // at their own levels, lowest first; src's buffers are read, never kept
-  int rc = SK_OK;
+  // at their own levels, lowest first; src's buffers are read, never kept.  Both
+  // first take in their pending blocks.
+  int rc = flush(src);
+  if (rc == SK_OK) rc = flush(dst);
+  if (rc != SK_OK) return rc;
   if (src->fill >= 0 && src->nfill > 0)
     rc = append_rows(dst, lib_ref(src, src->fill), src->nfill);
+  if (rc == SK_OK) rc = flush(dst);
   if (rc != SK_OK) return rc;
   std::vector<Blk> slots = slots_of(dst);
   std::vector<PlannedOp> ops;
@@ -418,6 +461,8 @@ int coreset_merge(sk_coreset_handle dst, sk_coreset_handle src) {
 
 int coreset_info(sk_coreset_handle c, int64_t* points, int64_t* count, int64_t* reduces) {
   if (c == nullptr) return SK_EINVAL;
+  const int rc = flush(c);
+  if (rc != SK_OK) return rc;
   long long np = 0;
   (void)segments(c, &np);
   if (points) *points = np;
@@ -428,6 +473,8 @@ int coreset_info(sk_coreset_handle c, int64_t* points, int64_t* count, int64_t* 
 
 int coreset_export(sk_coreset_handle c, float* K, float* V, float* w) {
   if (c == nullptr || K == nullptr || V == nullptr || w == nullptr) return SK_EINVAL;
+  const int rc = flush(c);
+  if (rc != SK_OK) return rc;
   long long np = 0;
   const CsSegs sg = segments(c, &np);
   if (np == 0) return SK_OK;
@@ -443,6 +490,8 @@ int coreset_query(sk_coreset_handle c, const float* Q, int64_t m, float* out, fl
   if (c == nullptr || m < 0) return SK_EINVAL;
   if (m == 0) return SK_OK;
   if (Q == nullptr || out == nullptr || Z == nullptr || !cs_aligned16(Q)) return SK_EINVAL;
+  const int rc = flush(c);
+  if (rc != SK_OK) return rc;
   long long np = 0;
   const CsSegs sg = segments(c, &np);
   if (np == 0) return SK_OK;                  // no tail: the head answer stands

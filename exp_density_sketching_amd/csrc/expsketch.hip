@@ -54,11 +54,12 @@ namespace {
 constexpr int kMaxP = 16;
 // a_hi rows per query tile: the full layout keeps plans of 512, 256 and 128 rows
 // and a query takes the longest whose launch fills the GPU (query_plan_for);
-// EXPSKETCH_QUERY_ROWS fixes one length instead (a multiple of 64; tuning aid)
+// EXPSKETCH_QUERY_ROWS fixes one length instead (a multiple of 64 up to 4096, so a
+// tile's rows stay within a 32-bit buffer range; tuning aid)
 long long query_rows_fixed() {
   static const long long v = [] {
     const char* e = std::getenv("EXPSKETCH_QUERY_ROWS");
-    const long long r = e ? std::atoll(e) : 0;
+    const long long r = e ? std::min(std::atoll(e), 4096LL) : 0;
     return r >= 64 ? r / 64 * 64 : 0LL;
   }();
   return v;

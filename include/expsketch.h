@@ -374,7 +374,12 @@ int coreset_reset(sk_coreset_handle c);
 /*
  * coreset_update -- n more pairs per head: K [h][n][d], V [h][n][dv] (device,
  * caller-owned; they may be reused once the stream has passed the call).  Runs
- * every reduce the new points cause (Merge-and-Reduce).
+ * the reduces the new points cause (Merge-and-Reduce): rounds of 64 whole
+ * blocks of the input at once; blocks of smaller calls are copied and wait until
+ * 64 blocks (or 64 MB) have gathered or a reader (coreset_query, coreset_export,
+ * coreset_info, coreset_merge on either side) needs the coreset, so that several
+ * calls' reduces share launches.  The blocks enter the binary counter in stream
+ * order either way: the kept points do not depend on when they are reduced.
  * Errors: SK_EINVAL (NULL/misaligned pointer with n > 0, n < 0), SK_ENOMEM, SK_EHIP.
  */
 int coreset_update(sk_coreset_handle c, const float* K, const float* V, int64_t n);
@@ -403,7 +408,8 @@ int coreset_merge(sk_coreset_handle dst, sk_coreset_handle src);
 int coreset_query(sk_coreset_handle c, const float* Q, int64_t m, float* out, float* Z);
 
 /* coreset_info -- points per head, points ingested per head, reduces done (any
- * pointer may be NULL).  Errors: SK_EINVAL. */
+ * pointer may be NULL); first runs the reduces of waiting blocks.
+ * Errors: SK_EINVAL, SK_ENOMEM, SK_EHIP. */
 int coreset_info(sk_coreset_handle c, int64_t* points, int64_t* count, int64_t* reduces);
 
 /*
