@@ -85,36 +85,71 @@ __device__ __forceinline__ double cs_uniform(unsigned long long seed,
   return (double)(cs_splitmix64(seed, counter) >> 11) * 0x1.0p-53;
 }
 
-// R_p(x) = sum_{j > p} x^j / j! in float64: the series (terms by the ratio x / j
-// until they stop changing the sum, past the largest term), unless its largest
-// term exceeds e^x + sum_{j <= p} |x|^j / j!, where e^x - T_p(x) rounds less.
-__device__ inline double cs_tail_exp64(double x, int p, const double* __restrict__ cs_inv) {
-  const double ax = fabs(x);
-  double term = 1.0;
-  for (int j = 1; j <= p + 1; ++j) term *= x * cs_inv[j];
-  double acc = term, big = fabs(term);
-  if (ax <= 40.0) {
-    for (int j = p + 2; j < p + 400 && j < CS_NINV; ++j) {
-      term *= x * cs_inv[j];
-      const double nw = acc + term;
-      big = fmax(big, fabs(term));
-      if (nw == acc && (double)j > 2.0 * ax) break;
-      acc = nw;
+// R_p(x) = sum_{j > p} x^j / j! in float64 for N values x at once: the series
+// (terms by the ratio x / j until they stop changing the sum, past the largest
+// term), unless its largest term exceeds e^x + sum_{j <= p} |x|^j / j!, where
+// e^x - T_p(x) rounds less.  The N series advance together, one 1/j per step for
+// all, so their dependent chains overlap; a value whose series has stopped is
+// left as it is, so each result is the one its own series alone would give.
+// Sums and products are rounded one at a time (no fused multiply-add), as in a
+// plain float64 evaluation.
+template <int N>
+__device__ inline void cs_tail_exp64_n(const double (&x)[N], int p,
+                                       const double* __restrict__ cs_inv, double (&out)[N]) {
+#pragma clang fp contract(off)
+  double term[N], acc[N], big[N];
+  bool live[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) term[e] = 1.0;
+  for (int j = 1; j <= p + 1; ++j) {
+    const double ij = cs_inv[j];
+#pragma unroll
+    for (int e = 0; e < N; ++e) term[e] *= x[e] * ij;
+  }
+  bool any = false;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    acc[e] = term[e];
+    big[e] = fabs(term[e]);
+    live[e] = fabs(x[e]) <= 40.0;
+    any = any || live[e];
+  }
+  for (int j = p + 2; any && j < p + 400 && j < CS_NINV; ++j) {
+    const double ij = cs_inv[j];
+    any = false;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      if (live[e]) {
+        term[e] *= x[e] * ij;
+        const double nw = acc[e] + term[e];
+        big[e] = fmax(big[e], fabs(term[e]));
+        if (nw == acc[e] && (double)j > 2.0 * fabs(x[e])) live[e] = false;
+        else acc[e] = nw;
+        any = any || live[e];
+      }
     }
   }
-  double hm = 1.0, t = 1.0;
-  for (int i = 1; i <= p; ++i) {
-    t *= ax * cs_inv[i];
-    hm += t;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const double ax = fabs(x[e]);
+    double hm = 1.0, t = 1.0;
+    for (int i = 1; i <= p; ++i) {
+      t *= ax * cs_inv[i];
+      hm += t;
+    }
+    double r = acc[e];
+    // (big <= hm already decides for the series without e^x: e^x > 0)
+    if (!(ax <= 40.0 && big[e] <= hm)) {
+      const double ex = exp(x[e]);
+      if (!(ax <= 40.0 && big[e] <= ex + hm)) {
+        // e^x - T_p(x), T_p by Horner from the top
+        double tp = 1.0;
+        for (int i = p; i >= 1; --i) tp = 1.0 + x[e] * cs_inv[i] * tp;
+        r = ex - tp;
+      }
+    }
+    out[e] = r;
   }
-  // (big <= hm already decides for the series without e^x: e^x > 0)
-  if (ax <= 40.0 && big <= hm) return acc;
-  const double ex = exp(x);
-  if (ax <= 40.0 && big <= ex + hm) return acc;
-  // e^x - T_p(x), T_p by Horner from the top
-  double tp = 1.0;
-  for (int i = p; i >= 1; --i) tp = 1.0 + x * cs_inv[i] * tp;
-  return ex - tp;
 }
 
 // Pair Gram matrix of a batch of reduces.  Grid: (reduce, head, upper tile) with
@@ -192,11 +227,16 @@ void cs_gram_kernel(CsOps ops, int B, int d, int dv, int p, int h,
       }
     }
   }
-  double g[4][4];
+  double g[4][4], xs[16], rs[16];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) g[a][b] = cs_tail_exp64(kd[a][b], p, inv) * (1.0 + vd[a][b]);
+    for (int b = 0; b < 4; ++b) xs[4 * a + b] = kd[a][b];
+  cs_tail_exp64_n<16>(xs, p, inv, rs);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) g[a][b] = rs[4 * a + b] * (1.0 + vd[a][b]);
   double* Dh = Dws + ((long long)oi * h + head) * (long long)B * B;
 #pragma unroll
   for (int P = 0; P < 2; ++P)
