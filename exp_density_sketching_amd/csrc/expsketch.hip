@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <numeric>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -824,12 +825,12 @@ bool use_sym_dg() {
 
 // The multiset block of width C whose largest multiset size is jhi runs on the
 // last-index query kernel: C >= 64 columns (two full MFMA tiles per wave), d <= 64
-// (the query components in registers) and sizes up to 2, whose runs of one prefix
-// are long (about d / 2 rows: a stage is mostly rows that exist).  Measured: the
-// d = 64, p = 2 workload 0.157 -> 0.234 of the fp32 peak; the d = 32, p = 3
-// workload 0.149 -> 0.100 with both its blocks on it (the top block's 32 columns
-// and runs of about d / 3 rows give too few matrix instructions per stage), 0.105
-// with its lower block alone.
+// (the query components in registers) and sizes up to 2 (a prefix of at most one
+// index; runs pair up into full slots).  Measured: the d = 64, p = 2 workload
+// 0.157 (row ranges) -> 0.302 of the fp32 peak; with sizes up to 3 and one run
+// per slot, the d = 32, p = 3 workload went 0.149 -> 0.100 with both its blocks
+// on it (the top block's 32 columns and runs of about d / 3 rows give too few
+// matrix instructions per stage), 0.105 with its lower block alone.
 bool sym_dg_block(const sk_sketch* s, int C, int jhi) {
   return use_sym_dg() && C >= 64 && s->d <= 64 && jhi <= 2 && jhi <= sd_max_j(s->d);
 }
@@ -849,13 +850,15 @@ size_t sym_dg_lds_bytes() { return sizeof(float) * 2 * SD_R * (32 * SK_DGNT + 32
 
 // Last-index query tiles of the multiset sizes jlo .. jhi of one block (block row
 // 0 = canonical row rc0, float offset xoff): per size, its runs (one per
-// multiset of the size below, in order) and tiles of up to 64 columns and about
-// six full stages' work, each with a [128][fw] partial and a finishing record.
+// multiset of the size below) paired into slots, and tiles of up to 64 columns
+// and about six full stages' work, each with a [128][fw] partial and a
+// finishing record.
 void plan_sym_dg_block(sk_sketch* s, const SymHost& t, long long xoff, long long rc0, int C,
                        int top, int jlo, int jhi) {
   sk_sketch::QPlan& qp = s->qplans[0];
   const int d = s->d;
   const int NF = SD_R / d;
+  const SymDgRun none{0, d, 0, 0.f, 0ull};
   // canonical start of each size
   std::vector<long long> start(s->p + 2, (long long)t.code.size());
   for (long long r = (long long)t.code.size() - 1; r >= 0; --r)
@@ -863,10 +866,12 @@ void plan_sym_dg_block(sk_sketch* s, const SymHost& t, long long xoff, long long
   for (int j = jlo; j <= jhi; ++j) {
     const long long cnt = start[j + 1] - start[j];
     const long long lxoff = xoff + (start[j] - rc0) * C;
-    const int run0 = (int)s->sdruns.size();
+    const int run0 = (int)s->sdruns.size() / 2;
     if (j == 0) {
       s->sdruns.push_back(SymDgRun{0, 0, 0, 1.f, 0ull});
+      s->sdruns.push_back(none);
     } else {
+      std::vector<SymDgRun> lv;
       long long lr = 0;      // level row of the run's first multiset
       for (long long b = start[j - 1]; b < start[j]; ++b) {
         const int lb = j == 1 ? 0 : t.last[b];
@@ -876,31 +881,55 @@ void plan_sym_dg_block(sk_sketch* s, const SymHost& t, long long xoff, long long
         R.mlb = j == 1 ? 0 : t.lmul[b];
         R.winv = t.winv[b];
         R.code = t.code[b] & 0x00ffffffffffffffull;
-        s->sdruns.push_back(R);
+        lv.push_back(R);
         lr += d - lb;
       }
+      // slots: the longest run left with the shortest when the shorter one's
+      // positions (pairwise reversed: up to its length - 1, or its length when
+      // odd) stay below the longer one's first index rounded down to even, else alone
+      auto fits = [&](const SymDgRun& a, const SymDgRun& b) {
+        const int L = d - b.lb;
+        return L - 1 + (L & 1) < (a.lb & ~1);
+      };
+      std::vector<int> ord(lv.size());
+      std::iota(ord.begin(), ord.end(), 0);
+      std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return lv[x].lb < lv[y].lb; });
+      for (int lo = 0, hi = (int)ord.size() - 1; lo <= hi;) {
+        s->sdruns.push_back(lv[ord[lo]]);
+        if (lo < hi && fits(lv[ord[lo]], lv[ord[hi]])) {
+          s->sdruns.push_back(lv[ord[hi]]);
+          --hi;
+        } else {
+          s->sdruns.push_back(none);
+        }
+        ++lo;
+      }
     }
-    const int nrun = (int)s->sdruns.size() - run0;
+    const int nrun = (int)s->sdruns.size() / 2 - run0;
     // tiles of about equal work: a stage costs the rows of its k-step groups
-    // that hold rows of their runs (the kernel skips the others) plus 32 rows'
-    // worth of fixed cost; a tile takes stages up to six full stages' cost (runs
-    // of one prefix shrink from d rows to 1 along a level, so equal run counts
-    // leave the first tiles several times the work of the last).  Measured on
-    // the d = 64, p = 2 workload (fraction of the fp32 peak): equal counts of 8
-    // runs 0.230, of 4 runs 0.187; by cost, 6 stages and 32 rows 0.247, 8 and 64
-    // 0.218, 8 and 16 0.187, 16 and 64 0.139 (the best fill one round of three
-    // workgroups per CU).  EXPSKETCH_SYM_DG_STAGES and EXPSKETCH_SYM_DG_OVH set
-    // the two numbers (tuning aids).
+    // that hold rows of their slots (the kernel skips the others) plus 32 rows'
+    // worth of fixed cost; a tile takes stages up to five full stages' cost.
+    // Measured on the d = 64, p = 2 workload (fraction of the fp32 peak), with
+    // paired runs: 5 stages and 32 rows 0.302, 5 and 64 0.300, 6 and 0/32/64
+    // 0.28, 4 and 32 0.27, 7 and 32 0.26, 3 and 32 0.22, 2 and 32 0.22; with one
+    // run per slot the best was 6 and 32 at 0.247 (of 8 and 64 0.218, 16 and 64
+    // 0.139, equal counts of 8 runs 0.230).  EXPSKETCH_SYM_DG_STAGES and
+    // EXPSKETCH_SYM_DG_OVH set the two numbers (tuning aids).
     auto live_rows = [&](int r) {
-      // rows of the 8-row groups of run r's slot that reach its first index
-      const int lb = j == 0 ? 0 : s->sdruns[run0 + r].lb;
-      return d >= 8 ? d - lb / 8 * 8 : (lb < d ? 8 : 0);
+      // rows of the 8-row groups of slot r that hold a row of either run
+      const int la = s->sdruns[2 * (run0 + r)].lb, lb2 = s->sdruns[2 * (run0 + r) + 1].lb;
+      if (j == 0) return 8;
+      if (d < 8) return (la < d || lb2 < d) ? 4 : 0;
+      int rows = 0;
+      for (int p0 = 0; p0 < d; p0 += 8)
+        if (p0 + 7 >= la || p0 <= d - 1 - lb2) rows += 8;
+      return rows;
     };
     std::vector<int> cut{0};
     {
       static const long long stages = [] {
         const char* e = std::getenv("EXPSKETCH_SYM_DG_STAGES");
-        return e && std::atoll(e) > 0 ? std::atoll(e) : 6LL;
+        return e && std::atoll(e) > 0 ? std::atoll(e) : 5LL;
       }();
       static const long long ovh = [] {
         const char* e = std::getenv("EXPSKETCH_SYM_DG_OVH");

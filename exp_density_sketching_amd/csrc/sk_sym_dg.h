@@ -1,6 +1,6 @@
 // Query of the multiset storage by the last index, for blocks of at least 32
-// columns and d <= 64: the counterpart of sk_query_dgr_kernel for the rows of one
-// multiset size j.
+// columns, d <= 64 and multisets of at most two indices: the counterpart of
+// sk_query_dgr_kernel for the rows of one multiset size j.
 // Source: "Rumo a Limites Estritos para Atenção em Streaming", "Metodologia",
 // pillar "O Método Polinomial" (answering from the low-degree moments; the
 // pages leave their storage open).
@@ -8,25 +8,32 @@
 // The rows of size j come in runs that share a prefix (the multiset minus its
 // largest index): for prefix beta' the run holds beta' + {e} for e = lb .. d - 1
 // (lb = the largest index of beta', 0 for the empty prefix), consecutive in the
-// block.  A stage of 64 rows holds NF = 64 / d runs, each laid out at rows
-// f d + e for e = 0 .. d - 1 (rows e < lb of a run read zeros), so row f d + e
-// has the query feature
+// block.  A stage of 64 rows holds NF = 64 / d slots of d rows.  A slot holds
+// one run a at positions e = lb_a .. d - 1 and, below them, a second run b
+// reversed in pairs of positions: index e of run b sits at position
+// (d - 1 - e) xor 1, which keeps e's parity, so for every row the lane's query
+// component is a register at a compile-time index.  Run b fits when its
+// positions (up to d - lb_b - 1, or d - lb_b when that length is odd) stay below
+// lb_a rounded down to even, so that the two rows of a k-step (positions 2 i and
+// 2 i + 1) always belong to the same run.  The planner pairs long runs with short
+// ones, so a level of runs shrinking from d rows to 1 fills its stages.  Row beta' + {e} has the query feature
 //     q^(beta' + e) / (beta' + e)! = [q^beta' / beta'!] * q[e] * h
 // with h = 1 / (multiplicity of e in beta' + 1) (only e = lb can repeat an index
-// of beta').  The bracket is one number per run and query (its components loaded
+// of beta').  The bracket is one number per run and query (its component loaded
 // a stage ahead); q[e] is the lane's query component in a register at a
-// compile-time index (the stage starts at a multiple of d); h scales the state
-// row when it is staged.  Below the top level, column e' < d of row beta holds
-// the moment of beta + {e'}, weighted 1 / (multiplicity of e' in beta + 1)
-// relative to the row (0 for e' below the row's largest index, whose entries
-// repeat others), also applied when staging; the epilogue multiplies those
-// columns by q[e'].  k-step groups whose rows all lie below their run's lb are
-// skipped (wave-uniform), so the padding of the runs costs little MFMA work.
+// compile-time index of the position (q[p] for run a, q[(d - 1 - p) xor 1] for
+// run b, both in the lane's half of the components); h scales the state row
+// when it is staged.  Below the top level, column e' < d of row beta holds the
+// moment of beta + {e'}, weighted 1 / (multiplicity of e' in beta + 1) relative
+// to the row (0 for e' below the row's largest index, whose entries repeat
+// others), also applied when staging; the epilogue multiplies those columns by
+// q[e'].  k-step groups with no row of
+// either run are skipped (wave-uniform).
 //
 // Everything else follows sk_query_dgr_kernel: v_mfma_f32_32x32x2_f32, 128
 // queries (32 per wave) x up to 64 columns per workgroup, state rows through
 // double-buffered LDS by bounded buffer loads (rows past the level's last row,
-// of empty runs, and columns outside the tile read zeros), one barrier per
+// of empty slots, and columns outside the tile read zeros), one barrier per
 // stage, the stage's rows read from LDS a group of k-steps ahead.
 #pragma once
 
@@ -35,15 +42,18 @@
 #include "sk_sym.h"
 
 #define SD_R 64            // rows per stage
-#define SD_MAXC 16         // prefix components per stage (runs x (j - 1)) held in registers
 
-// Largest multiset size j whose levels the kernel takes at key width d (the
-// prefix components of a stage's runs must fit SD_MAXC registers).
-__host__ __device__ constexpr int sd_max_j(int d) {
-  return (SD_MAXC / (SD_R / d) < SY_MAXP ? SD_MAXC / (SD_R / d) : SY_MAXP) + 1;
+// Largest multiset size j whose levels the kernel takes (a run's prefix holds at
+// most one index).
+__host__ __device__ constexpr int sd_max_j(int) { return 2; }
+
+// 1 / k for the multiplicities k = 1, 2, 3 that rows of at most two indices give
+// (each the correctly rounded quotient; h / 3 for h = 1 / 2 is then exact too).
+__device__ __forceinline__ float sd_recip(int k) {
+  return k == 1 ? 1.f : (k == 2 ? 0.5f : 1.f / 3.f);
 }
 
-// One run: beta' + {e} for e = lb .. d - 1.
+// One run: beta' + {e} for e = lb .. d - 1 (lb = d: no rows).
 struct SymDgRun {
   int row0;                // level row of e = 0 (that of e = lb, less lb)
   int lb;                  // first index of the run
@@ -52,7 +62,8 @@ struct SymDgRun {
   unsigned long long code; // beta' indices in bytes 0 .. j - 2
 };
 
-// One (level, column tile, range of runs) of the multiset query.
+// One (level, column tile, range of slots) of the multiset query; slot s is the
+// run pair runs[2 s] (a, forward) and runs[2 s + 1] (b, reversed).
 struct SymDgTile {
   long long xoff;          // float offset of the level's first row in one head's state
   long long pofs;          // offset of the tile's [128][fw] partial in a query-tile block
@@ -61,7 +72,7 @@ struct SymDgTile {
   int top;
   int j;                   // multiset size of the level's rows
   int col0, fw;            // the tile's columns
-  int run0, nrun;          // runs of the tile in the run table
+  int run0, nrun;          // slots of the tile in the slot table
   int pad_[2];
 };
 
@@ -72,17 +83,14 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
                                              const float* qr, int d_, int tid, int lhi, int l32,
                                              floatx16* acc) {
   constexpr int d = 1 << LOGD;
-  constexpr int NF = SD_R / d;                  // runs per stage
-  // prefix components per run in registers (the planner keeps j - 1 within it)
-  constexpr int MAXJ = SD_MAXC / NF < SY_MAXP ? SD_MAXC / NF : SY_MAXP;
+  constexpr int NF = SD_R / d;                  // slots per stage
   constexpr int LDB = 32 * SK_DGNT + 32;
   constexpr int KS = SD_R / 2;
   constexpr int KG = 4;
   constexpr int NG = KS / KG;
   constexpr int W4 = 8 * NT;
   constexpr int PV = SD_R * W4 / SK_WG;
-  static_assert(MAXJ >= 1, "stage shape");
-  const int C = T.C, col0 = T.col0, gw = T.fw, j = T.j, jm1 = T.j - 1;
+  const int C = T.C, col0 = T.col0, gw = T.fw, j = T.j;
   const bool lower = !T.top;
   if (j == 0) {
     // the empty multiset: one row, feature 1, every column weighted 1
@@ -100,7 +108,7 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
   }
   const int nst = (T.nrun + NF - 1) / NF;
   const __amdgpu_buffer_rsrc_t rx = dg_rsrc(Xl, (unsigned)((long long)T.nrows * C * 4));
-  // the thread's stage positions: row f d + e, float4 c4 of the tile's columns
+  // the thread's stage positions: slot row f d + p, float4 c4 of the tile's columns
   int prow[PV], pc4[PV];
 #pragma unroll
   for (int v = 0; v < PV; ++v) {
@@ -109,30 +117,34 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
     pc4[v] = i - prow[v] * W4;
   }
   float4 pre[PV];
-  float hv[PV];            // row factor h of the staged rows
-  int ev[PV];              // their last index e
-  int mv[PV];              // and its multiplicity in the row
+  int em[PV];              // the staged rows' last index e | its multiplicity in the row << 8
+  // a thread's positions v cover rows v S .. v S + S - 1 of the stage (S = SK_WG /
+  // W4 threads per row block); when S <= d they lie in one slot, known per v
+  constexpr int S = SK_WG / W4;
   auto fetch = [&](int st) {
 #pragma unroll
     for (int v = 0; v < PV; ++v) {
-      const int f = prow[v] >> LOGD, e = prow[v] & (d - 1);
+      const int f = S <= d ? (v * S) >> LOGD : prow[v] >> LOGD;
+      const int p = prow[v] & (d - 1);
       const int r = st * NF + f;
       unsigned off = DG_OOB;
-      float h = 1.f;
-      int mult = 1;
+      int e = p, mult = 1;
       if (r < T.nrun) {
-        const SymDgRun R = runs[T.run0 + r];
-        if (e >= R.lb && 4 * pc4[v] < gw)
-          off = (unsigned)(((long long)(R.row0 + e) * C + col0 + 4 * pc4[v]) * 4);
+        const SymDgRun A = runs[2 * (T.run0 + r)];
+        const SymDgRun B = runs[2 * (T.run0 + r) + 1];
+        const int eb = (d - 1 - p) ^ 1;
+        const bool ina = p >= A.lb;
+        const bool in = ina || eb >= B.lb;
+        e = ina ? p : eb;
+        const int row = (ina ? A.row0 : B.row0) + e;
+        if (in && 4 * pc4[v] < gw)
+          off = (unsigned)(((long long)row * C + col0 + 4 * pc4[v]) * 4);
         // e = lb may repeat the largest index of beta': the row's multiplicity of
         // e is then mlb + 1, and its weight relative to beta' 1 / (mlb + 1)
-        mult = (e == R.lb ? R.mlb : 0) + 1;
-        h = 1.f / (float)mult;
+        mult = (in && e == (ina ? A.lb : B.lb) ? (ina ? A.mlb : B.mlb) : 0) + 1;
       }
       pre[v] = dg_ld4(rx, off);
-      hv[v] = h;
-      ev[v] = e;
-      mv[v] = mult;
+      em[v] = e | (mult << 8);
     }
   };
   // column weights of a staged float4 (rows below the top): e' < e -> 0, e' = e ->
@@ -141,50 +153,46 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
 #pragma unroll
     for (int v = 0; v < PV; ++v) {
       float4 x = pre[v];
-      const float h = hv[v];
+      const int e = em[v] & 0xff, mult = em[v] >> 8;
+      const float h = sd_recip(mult);
       const int c = col0 + 4 * pc4[v];
       float w[4] = {h, h, h, h};
       if (lower) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int ec = c + u;
-          if (ec < d_) w[u] = ec > ev[v] ? h : (ec == ev[v] ? h / (float)(mv[v] + 1) : 0.f);
+          if (ec < d_) w[u] = ec > e ? h : (ec == e ? h * sd_recip(mult + 1) : 0.f);
         }
       }
       x.x *= w[0]; x.y *= w[1]; x.z *= w[2]; x.w *= w[3];
       *reinterpret_cast<float4*>(B + prow[v] * LDB + 4 * pc4[v]) = x;
     }
   };
-  // prefix components of stage st's runs (unconditional loads, component 0 where
-  // none is needed); the prefixes q^beta' / beta'! formed at the stage
-  float pc[SD_MAXC];
+  // prefix component of each run of stage st's slots (j = 2; none for j = 1); the
+  // brackets q^beta' / beta'! formed at the stage
+  float pc[2 * NF];
   auto pfetch = [&](int st) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int r = st * NF + f;
-      const unsigned long long code = r < T.nrun ? runs[T.run0 + r].code : 0ull;
-#pragma unroll
-      for (int k = 0; k < MAXJ; ++k) {
-        const int idx = k < jm1 ? (int)((code >> (8 * k)) & 0xffu) : 0;
-        pc[f * MAXJ + k] = sk_ld(rq, qoff, (unsigned)idx * 4u);
-      }
+    for (int i = 0; i < 2 * NF; ++i) {
+      const int r = st * NF + i / 2;
+      pc[i] = 1.f;
+      if (j == 2 && r < T.nrun)
+        pc[i] = sk_ld(rq, qoff, (unsigned)(runs[2 * (T.run0 + r) + (i & 1)].code & 0xffu) * 4u);
     }
   };
   auto pform = [&](int st, float* pf, int* lbs) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int r = st * NF + f;
+    for (int i = 0; i < 2 * NF; ++i) {
+      const int r = st * NF + i / 2;
       float x = 0.f;
       int lb = d;
       if (r < T.nrun) {
-        const SymDgRun R = runs[T.run0 + r];
-        x = R.winv;
+        const SymDgRun R = runs[2 * (T.run0 + r) + (i & 1)];
+        x = R.winv * pc[i];
         lb = R.lb;
-#pragma unroll
-        for (int k = 0; k < MAXJ; ++k) x *= k < jm1 ? pc[f * MAXJ + k] : 1.f;
       }
-      pf[f] = x;
-      lbs[f] = lb;
+      pf[i] = x;
+      lbs[i] = lb;
     }
   };
   fetch(0);
@@ -192,8 +200,8 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
   for (int st = 0; st < nst; ++st) {
     float* B = Bs + (st & 1) * (SD_R * LDB);
     store(B);
-    float pf[NF];
-    int lbs[NF];
+    float pf[2 * NF];
+    int lbs[2 * NF];
     pform(st, pf, lbs);
     __syncthreads();
     if (st + 1 < nst) {
@@ -208,15 +216,16 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
 #pragma unroll
         for (int t = 0; t < NT; ++t) dst[k][t] = Bl[2 * (g * KG + k) * LDB + 32 * t];
     };
-    // group g holds rows 8 g .. 8 g + 7 of run (8 g) / d, indices (8 g) mod d ..
-    // (8 g) mod d + 7 (8 <= d: one run; d = 4: two runs, the group is skipped
-    // only when both are)
+    // group g holds slot rows 8 g .. 8 g + 7: positions (8 g) mod d .. + 7 of slot
+    // (8 g) / d (8 <= d), or all of slots 2 g and 2 g + 1 (d = 4)
     auto live = [&](int g) {
       constexpr int GR = 2 * KG;
       if constexpr (d >= GR) {
-        return (GR * g) % d + GR - 1 >= lbs[(GR * g) / d];
+        const int f = (GR * g) / d, p0 = (GR * g) % d;
+        return p0 + GR - 1 >= lbs[2 * f] || p0 <= d - 1 - lbs[2 * f + 1];
       } else {
-        return lbs[(GR * g) / d] < d || lbs[(GR * g) / d + 1] < d;
+        const int f = (GR * g) / d;
+        return lbs[2 * f] < d || lbs[2 * f + 1] < d || lbs[2 * f + 2] < d || lbs[2 * f + 3] < d;
       }
     };
     rd(0, bv[0]);
@@ -225,10 +234,16 @@ __device__ __forceinline__ void sd_tile_loop(const SymDgTile& T, const SymDgRun*
       if (g + 1 < NG) rd(g + 1, bv[(g + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       if (live(g)) {
+        // the lane's row is position 2 i + lhi of slot f: run a's from lb_a rounded
+        // down to even on (rows below lb_a there are zeros), run b's of index
+        // (d - 1 - 2 i - lhi) xor 1 = 2 (d/2 - 1 - i) + lhi below; the boundary is
+        // even, so both rows of a k-step take the same run
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
           const int ks = g * KG + k;
-          const float a = pf[(2 * ks) / d] * qr[ks % (d / 2)];
+          const int f = (2 * ks) / d, i = ks % (d / 2);
+          const bool ra = 2 * i >= (lbs[2 * f] & ~1);   // wave-uniform
+          const float a = ra ? pf[2 * f] * qr[i] : pf[2 * f + 1] * qr[d / 2 - 1 - i];
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[t] = mfma32x32x2(a, bv[g & 1][k][t], acc[t]);
         }

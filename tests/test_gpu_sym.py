@@ -56,13 +56,14 @@ def test_sym_state_matches_oracle(ident, n, h):
 
 
 # blocks of 64 or more columns with multisets of at most 2 indices (d <= 64) are
-# queried by the last index: (4, 64, 2), (8, 64, 2), (16, 64, 2) and (64, 128, 2)
-# put 16, 8, 4 and 1 prefix runs in a stage ((16, 64, 3), (64, 32, 3): one block
-# would qualify, so both take the row-range kernel)
+# queried by the last index: (4, 64, 2), (8, 64, 2), (16, 64, 2), (32, 64, 2) and
+# (64, 128, 2) put 16, 8, 4, 2 and 1 slots of paired prefix runs in a stage
+# ((16, 64, 3), (64, 32, 3): one block would qualify, so both take the row-range
+# kernel)
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
                                     (128, 128, 1), (4, 4, 7), (32, 8, 2), (64, 128, 2),
                                     (128, 4, 2), (4, 64, 2), (8, 64, 2), (16, 64, 2),
-                                    (16, 64, 3), (64, 32, 3)])
+                                    (32, 64, 2), (16, 64, 3), (64, 32, 3)])
 def test_sym_other_shapes(d, dv, p):
     w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
