@@ -85,85 +85,85 @@ __device__ __forceinline__ double cs_uniform(unsigned long long seed,
   return (double)(cs_splitmix64(seed, counter) >> 11) * 0x1.0p-53;
 }
 
-// R_p(x) = sum_{j > p} x^j / j! in float64 for N values x at once: the series
-// (terms by the ratio x / j until they stop changing the sum, past the largest
-// term), unless its largest term exceeds e^x + sum_{j <= p} |x|^j / j!, where
-// e^x - T_p(x) rounds less.  The N series advance together, one 1/j per step for
-// all, so their dependent chains overlap; a value whose series has stopped is
-// left as it is, so each result is the one its own series alone would give.
-// Sums and products are rounded one at a time (no fused multiply-add), as in a
-// plain float64 evaluation.
+// R_p(x) = sum_{j > p} x^j / j! in float64 for N values x at once.  For
+// |x| <= p + 1 the series x^(p+1) / (p+1)! * sum_k x^k (p+1)! / (p+1+k)! by Horner
+// from the top, its terms counted for the largest such |x| of the N values (until
+// the ratio of the next term to the first falls below 2^-56), so every value
+// advances through the same fused multiply-adds; there the terms shrink from the
+// first on, so the sum's rounding stays within a few units of the last place of
+// the largest term.  For |x| > p + 1, e^x - T_p(x), T_p by Horner: for x > p + 1,
+// e^x exceeds twice T_p(x); below -(p + 1), T_p(x) and e^x do not cancel (T_p is
+// positive for even p, negative there for odd p).  (The float64 oracle chooses
+// between the plain series and e^x - T_p(x) by the size of the series' largest
+// term; both are accurate to a few units of the last place, which a Gram entry
+// of the walk needs.)
 template <int N>
 __device__ inline void cs_tail_exp64_n(const double (&x)[N], int p,
                                        const double* __restrict__ cs_inv, double (&out)[N]) {
 #pragma clang fp contract(off)
-  double term[N], acc[N], big[N];
-  bool live[N];
+  const double lim = (double)(p + 1);
+  double X = 0.0;
 #pragma unroll
-  for (int e = 0; e < N; ++e) term[e] = 1.0;
+  for (int e = 0; e < N; ++e)
+    if (fabs(x[e]) <= lim) X = fmax(X, fabs(x[e]));
+  int nt = 0;
+  for (double t = 1.0; t > 0x1p-56 && p + 2 + nt < CS_NINV;) {
+    ++nt;
+    t *= X * cs_inv[p + 1 + nt];
+  }
+  double hh[N], xp[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) hh[e] = xp[e] = 1.0;
+  for (int k = nt; k >= 1; --k) {
+    const double ik = cs_inv[p + 1 + k];
+#pragma unroll
+    for (int e = 0; e < N; ++e) hh[e] = fma(x[e] * ik, hh[e], 1.0);
+  }
   for (int j = 1; j <= p + 1; ++j) {
     const double ij = cs_inv[j];
 #pragma unroll
-    for (int e = 0; e < N; ++e) term[e] *= x[e] * ij;
-  }
-  bool any = false;
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    acc[e] = term[e];
-    big[e] = fabs(term[e]);
-    live[e] = fabs(x[e]) <= 40.0;
-    any = any || live[e];
-  }
-  for (int j = p + 2; any && j < p + 400 && j < CS_NINV; ++j) {
-    const double ij = cs_inv[j];
-    any = false;
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-      if (live[e]) {
-        term[e] *= x[e] * ij;
-        const double nw = acc[e] + term[e];
-        big[e] = fmax(big[e], fabs(term[e]));
-        if (nw == acc[e] && (double)j > 2.0 * fabs(x[e])) live[e] = false;
-        else acc[e] = nw;
-        any = any || live[e];
-      }
-    }
+    for (int e = 0; e < N; ++e) xp[e] *= x[e] * ij;
   }
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    const double ax = fabs(x[e]);
-    double hm = 1.0, t = 1.0;
-    for (int i = 1; i <= p; ++i) {
-      t *= ax * cs_inv[i];
-      hm += t;
-    }
-    double r = acc[e];
-    // (big <= hm already decides for the series without e^x: e^x > 0)
-    if (!(ax <= 40.0 && big[e] <= hm)) {
-      const double ex = exp(x[e]);
-      if (!(ax <= 40.0 && big[e] <= ex + hm)) {
-        // e^x - T_p(x), T_p by Horner from the top
-        double tp = 1.0;
-        for (int i = p; i >= 1; --i) tp = 1.0 + x[e] * cs_inv[i] * tp;
-        r = ex - tp;
-      }
+    double r = xp[e] * hh[e];
+    if (fabs(x[e]) > lim) {
+      // e^x - T_p(x), T_p by Horner from the top
+      double tp = 1.0;
+      for (int i = p; i >= 1; --i) tp = 1.0 + x[e] * cs_inv[i] * tp;
+      r = exp(x[e]) - tp;
     }
     out[e] = r;
   }
 }
 
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
 // Pair Gram matrix of a batch of reduces.  Grid: (reduce, head, upper tile) with
-// the tile index fastest; 256 threads, thread (ti, tj) = (tid / 16, tid % 16)
-// owns points 4 ti .. 4 ti + 3 of the tile's rows (pairs 2 ti, 2 ti + 1) and
-// 4 tj .. 4 tj + 3 of its columns, accumulates their 16 key and value dot
-// products in float64 over feature chunks of 32 staged in LDS, and writes the 4
-// pair entries.  D: [reduce][head][B][B] float64.
+// the tile index fastest; 256 threads in 4 waves.  The tile's 64 row points and
+// 64 column points (32 pairs each) are staged in LDS (fp32, as given), up to 128
+// features of [k | v] at a time with one barrier; wave w takes rows
+// 32 (w >> 1) .. + 31 and columns 32 (w & 1) .. + 31 as 2 x 2 blocks of
+// v_mfma_f64_16x16x4_f64 on the features widened to float64 (A: lane l gives row
+// slot l % 16 at feature l / 16 of the k-step, B the same for the column; the
+// 16 x 16 result: lane l holds row slots l / 16 + 4 i, i = 0..3, of column
+// l % 16), the key products and the value products in separate accumulators.
+// Row slot m holds point 4 (m % 4) + m / 4 of the block, so that lane l holds
+// points 4 (l / 16) + i: the two pairs 2 (l / 16) and 2 (l / 16) + 1.  Each entry
+// then becomes g = R_p(<k, k'>) (1 + <v, v'>), and the pair entry
+//     D[t][s] = ((g[2t][2s] - g[2t][2s+1]) - g[2t+1][2s]) + g[2t+1][2s+1]
+// is formed by lane pairs (the two columns of a pair are neighbouring lanes; the
+// even lane writes pair row 2 (l / 16), the odd lane the next).
+// D: [reduce][head][B][B] float64.
+#define CS_GF 128          // features staged at once
+#define CS_GLD 80          // LDS row stride (floats): the 4 features of a k-step hit 4 bank groups
 __global__ __launch_bounds__(256)
 void cs_gram_kernel(CsOps ops, int B, int d, int dv, int p, int h,
                     const double* __restrict__ inv, double* __restrict__ Dws) {
-  __shared__ double Rs[32][64];
-  __shared__ double Cs[32][64];
+  __shared__ float Rs[CS_GF][CS_GLD];
+  __shared__ float Cs[CS_GF][CS_GLD];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int nt = B / CS_TP;
   const int ntiles = nt * (nt + 1) / 2;
   const long long lg = blockIdx.x;
@@ -178,75 +178,85 @@ void cs_gram_kernel(CsOps ops, int B, int d, int dv, int p, int h,
   }
   const int tc = tr + rem;
   const CsOp& O = ops.op[oi];
-  // merged point index i -> row of block a (i < B) or b
-  auto rowptr = [&](int i, bool val) -> const float* {
+  const int r0 = tr * 2 * CS_TP, c0 = tc * 2 * CS_TP;   // first merged point of rows / cols
+  // the staging thread's point pt (tid / 4) of the rows and of the columns: its key
+  // and value rows (merged point i < B: block a, else b)
+  const int pt = tid >> 2, q = tid & 3;
+  auto rows_of = [&](int i, const float*& k, const float*& v) {
     const CsRef& R = (i < B) ? O.a : O.b;
     const int r = (i < B) ? i : i - B;
-    return val ? R.V + head * R.hsV + (long long)r * dv : R.K + head * R.hsK + (long long)r * d;
+    k = R.K + head * R.hsK + (long long)r * d;
+    v = R.V + head * R.hsV + (long long)r * dv;
   };
-  const int ti = tid >> 4, tj = tid & 15;
-  const int r0 = tr * 2 * CS_TP, c0 = tc * 2 * CS_TP;   // first merged point of rows / cols
-  double kd[4][4], vd[4][4];
+  const float *rk, *rv, *ck, *cv;
+  rows_of(r0 + pt, rk, rv);
+  rows_of(c0 + pt, ck, cv);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l16 = lane & 15, lk = lane >> 4;
+  const int rslot = 4 * (l16 & 3) + (l16 >> 2);         // point of the lane's row slot
+  doublex4 kacc[2][2], vacc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kd[a][b] = vd[a][b] = 0.0;
-  for (int part = 0; part < 2; ++part) {
-    const int width = part == 0 ? d : dv;
-    for (int f0 = 0; f0 < width; f0 += 32) {
-      const int fw = min(32, width - f0);
-      // stage 64 row points and 64 column points, features f0 .. f0 + fw - 1
-      __syncthreads();
-      {
-        const int pt = tid >> 2, q = tid & 3;       // 8 features per thread
-        for (int k = 0; k < 8; k += 4) {
-          const int f = q * 8 + k;
-          if (f < fw) {
-            const float4 x = *reinterpret_cast<const float4*>(rowptr(r0 + pt, part == 1) + f0 + f);
-            const float4 y = *reinterpret_cast<const float4*>(rowptr(c0 + pt, part == 1) + f0 + f);
-            Rs[f][pt] = x.x; Rs[f + 1][pt] = x.y; Rs[f + 2][pt] = x.z; Rs[f + 3][pt] = x.w;
-            Cs[f][pt] = y.x; Cs[f + 1][pt] = y.y; Cs[f + 2][pt] = y.z; Cs[f + 3][pt] = y.w;
-          }
-        }
-      }
-      __syncthreads();
-      for (int f = 0; f < fw; ++f) {
-        double rv[4], cv[4];
+    for (int b = 0; b < 2; ++b) kacc[a][b] = vacc[a][b] = doublex4{0.0, 0.0, 0.0, 0.0};
+  // k-steps [k0, k1) of the staged features into acc
+  auto steps = [&](int k0, int k1, doublex4 (&acc)[2][2]) {
+    for (int ks = k0; ks < k1; ks += 4) {
+      const int f = ks + lk;
+      const double a0 = Rs[f][32 * wr + rslot], a1 = Rs[f][32 * wr + 16 + rslot];
+      const double b0 = Cs[f][32 * wc + l16], b1 = Cs[f][32 * wc + 16 + l16];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  };
+  const int F = d + dv;
+  for (int f0 = 0; f0 < F; f0 += CS_GF) {
+    const int fw = min(CS_GF, F - f0);
+    // stage 64 row and 64 column points, features f0 .. f0 + fw - 1 of [k | v]:
+    // thread (pt, q) loads float4s q, q + 4, ... of its point (a float4 never
+    // straddles k and v, as d is a multiple of 4)
+    __syncthreads();
+    for (int f = 4 * q; f < fw; f += 16) {
+      const int g = f0 + f;
+      const float4 x = *reinterpret_cast<const float4*>(g < d ? rk + g : rv + (g - d));
+      const float4 y = *reinterpret_cast<const float4*>(g < d ? ck + g : cv + (g - d));
+      Rs[f][pt] = x.x; Rs[f + 1][pt] = x.y; Rs[f + 2][pt] = x.z; Rs[f + 3][pt] = x.w;
+      Cs[f][pt] = y.x; Cs[f + 1][pt] = y.y; Cs[f + 2][pt] = y.z; Cs[f + 3][pt] = y.w;
+    }
+    __syncthreads();
+    const int kend = min(fw, max(0, d - f0));      // staged key features: [0, kend)
+    steps(0, kend, kacc);
+    steps(kend, fw, vacc);
+  }
+  double* Dh = Dws + ((long long)oi * h + head) * (long long)B * B;
+  const bool odd = lane & 1;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          rv[a] = Rs[f][4 * ti + a];
-          cv[a] = Cs[f][4 * tj + a];
-        }
+  for (int rb = 0; rb < 2; ++rb) {
+    // the row block's 8 entries per lane (2 column blocks x 4 rows), one series run
+    double xs[8], rs[8];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            if (part == 0) kd[a][b] = fma(rv[a], cv[b], kd[a][b]);
-            else vd[a][b] = fma(rv[a], cv[b], vd[a][b]);
-          }
-      }
+      for (int i = 0; i < 4; ++i) xs[4 * cb + i] = kacc[rb][cb][i];
+    cs_tail_exp64_n<8>(xs, p, inv, rs);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      double g[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = rs[4 * cb + i] * (1.0 + vacc[rb][cb][i]);
+      // the even lane (column 2s) forms pair row 2 (l / 16) from rows 0, 1 and needs
+      // the odd lane's rows 0, 1; the odd lane (column 2s + 1) forms the next pair
+      // row from rows 2, 3 and needs the even lane's
+      const double ra = __shfl_xor(odd ? g[0] : g[2], 1);
+      const double rbv = __shfl_xor(odd ? g[1] : g[3], 1);
+      const double Dv = odd ? ((ra - g[2]) - rbv) + g[3] : ((g[0] - ra) - g[1]) + rbv;
+      const int t = tr * CS_TP + ((32 * wr + 16 * rb + 4 * lk) >> 1) + (odd ? 1 : 0);
+      const int sc = tc * CS_TP + ((32 * wc + 16 * cb + l16) >> 1);
+      Dh[(long long)t * B + sc] = Dv;
     }
   }
-  double g[4][4], xs[16], rs[16];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) xs[4 * a + b] = kd[a][b];
-  cs_tail_exp64_n<16>(xs, p, inv, rs);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) g[a][b] = rs[4 * a + b] * (1.0 + vd[a][b]);
-  double* Dh = Dws + ((long long)oi * h + head) * (long long)B * B;
-#pragma unroll
-  for (int P = 0; P < 2; ++P)
-#pragma unroll
-    for (int Qq = 0; Qq < 2; ++Qq) {
-      const int t = tr * CS_TP + 2 * ti + P;
-      const int s = tc * CS_TP + 2 * tj + Qq;
-      Dh[(long long)t * B + s] = g[2 * P][2 * Qq] - g[2 * P][2 * Qq + 1] -
-                                 g[2 * P + 1][2 * Qq] + g[2 * P + 1][2 * Qq + 1];
-    }
 }
 
 // The walk of one reduce and one head (one workgroup of 256 threads), then the
@@ -257,7 +267,8 @@ void cs_gram_kernel(CsOps ops, int B, int d, int dv, int p, int h,
 // <psi, f_s> of every later pair.  Every <psi, f_s> thus gets its terms in pair
 // order, as in the sequential walk.  Decision of pair t: P = (1 - alpha/c)/2
 // clamped to [0, 1] (1/2 when c = 0), U from counter (serial * H + head) * B + t,
-// e = +1 (keep point 2t + 1) when U < P, else -1 (keep point 2t).
+// e = +1 (keep point 2t + 1) when U < P, else -1 (keep point 2t); for c > 0 the
+// kernel tests the same condition as alpha < c (1 - 2U).
 __global__ __launch_bounds__(256)
 void cs_walk_kernel(CsOps ops, int B, int d, int dv, int h, const double* __restrict__ Dws,
                     double c0, unsigned long long seed) {
@@ -293,22 +304,34 @@ void cs_walk_kernel(CsOps ops, int B, int d, int dv, int h, const double* __rest
           ((unsigned long long)O.serial * (unsigned long long)h + (unsigned long long)head) *
               (unsigned long long)B + (unsigned long long)(t0 + lane);
       const double U = cs_uniform(seed, ctr);
+      // U < P = clamp((1 - a / c) / 2, 0, 1) is a < c (1 - 2 U) for c > 0 (1 - 2 U is
+      // exact: U is a multiple of 2^-53), so each decision is one compare and the
+      // wave's mask, the chain from one pair's sum to the next one decision long
+      const double thr = c * (1.0 - 2.0 * U);
+      const bool half = U < 0.5;
       double a = alpha[t0 + lane];
       int mine = 0;
       for (int i = 0; i < 64; ++i) {
-        const double P = c > 0.0 ? fmin(1.0, fmax(0.0, 0.5 * (1.0 - a / c))) : 0.5;
-        const int dec = (U < P) ? 1 : -1;
-        const int e = __shfl(dec, i, 64);
-        if (lane == i) mine = e;
-        if (lane > i) a = fma((double)e, blk[i][lane], a);
+        const unsigned long long m = __ballot(c > 0.0 ? a < thr : half);
+        const double e = ((m >> i) & 1ull) ? 1.0 : -1.0;
+        if (lane == i) mine = e > 0.0 ? 1 : -1;
+        a = fma(e, blk[i][lane], a);           // blk[i][j] = 0 for j <= i
       }
       alpha[t0 + lane] = a;
       eps[t0 + lane] = (signed char)mine;
     }
     __syncthreads();
+    // (the block's column entries loaded 16 at a time, then added in pair order)
     for (int s = t0 + 64 + tid; s < B; s += 256) {
       double x = alpha[s];
-      for (int i = 0; i < 64; ++i) x = fma((double)eps[t0 + i], Dh[(long long)(t0 + i) * B + s], x);
+      const double* col = Dh + (long long)t0 * B + s;
+      for (int i0 = 0; i0 < 64; i0 += 16) {
+        double dcol[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) dcol[u] = col[(long long)(i0 + u) * B];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x = fma((double)eps[t0 + i0 + u], dcol[u], x);
+      }
       alpha[s] = x;
     }
     __syncthreads();
