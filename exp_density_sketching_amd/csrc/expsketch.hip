@@ -611,19 +611,22 @@ bool use_query_fold() {
   return v;
 }
 // Level j runs on the register-query kernel with its last digit on the column
-// side: C of 8 or 16 (dividing the 32 columns of an MFMA tile), 16 <= d <= 64 and
-// at least one digit left on the row side.  (At d = 8 the feature-tile kernel
-// measured faster: 0.50 against 0.48 of peak on the d = 8, p = 6 workload.)
+// side: C of 8, 16 or 32 (dividing the 32 columns of an MFMA tile, so that a
+// 64-column tile is full), 16 <= d <= 64 and at least one digit left on the row
+// side (two for C = 32, which unfolded already fills one MFMA tile).  (At d = 8
+// the feature-tile kernel measured faster: 0.50 against 0.48 of peak on the
+// d = 8, p = 6 workload.)
 bool query_level_fold(const sk_sketch* s, int j) {
   const int C = s->C[j];
-  return use_query_fold() && (C == 8 || C == 16) && s->d >= 16 && s->d <= 64 && j >= 1;
+  return use_query_fold() && (C == 8 || C == 16 || (C == 32 && j >= 2)) && s->d >= 16 &&
+         s->d <= 64 && j >= 1;
 }
 
 // Query tiles of level j: t trailing digits in the columns (the fewest giving at
 // least SK_TNQ columns), 128-column tiles, a_hi ranges of the plan's rows.
 // Kernel of level j's query: by the last digit when its C columns fill MFMA
 // columns (32x32x2 for C > 16, in 64-column tiles), or with the last digit on
-// the column side for C = 8 or 16 (query_level_fold); 16x16x4 for other
+// the column side for C = 8, 16 or 32 (query_level_fold); 16x16x4 for other
 // 8 < C <= 16 at d <= 16 when asked for; else the feature-tile kernel.  Returns
 // kind * 16.
 int query_level_kind(const sk_sketch* s, int j) {

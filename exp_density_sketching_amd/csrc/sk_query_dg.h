@@ -222,12 +222,12 @@ void sk_query_dg_kernel(const float* __restrict__ Q, long long m,
 // a stage are read from LDS one group of k-steps ahead of the MFMAs that use them
 // (scheduling barriers keep that order).
 //
-// A level of C = 8 or 16 columns fills only part of a 32-column MFMA tile; such a
-// level's tiles (T.t == 1) move its last digit b' to the column side: rows are
-// the j - 1 leading digits F (row length N = d C), columns (b', e), and the
-// epilogue weights column (b', e) with q[b'] and sums over b' (lane shuffles
-// inside each 32-lane half, then over the wave's column tiles) into a [128][C]
-// partial.
+// A level of C = 8 or 16 columns fills only part of a 32-column MFMA tile, one of
+// 32 columns half of a 64-column tile; such a level's tiles (T.t == 1) move its
+// last digit b' to the column side: rows are the j - 1 leading digits F (row
+// length N = d C), columns (b', e), and the epilogue weights column (b', e) with
+// q[b'] and sums over b' (lane shuffles inside each 32-lane half for C < 32, then
+// over the wave's column tiles) into a [128][C] partial.
 #define DG_OOB 0x80000000u
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dg_rsrc(const float* base, unsigned bytes) {
@@ -458,11 +458,14 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
         }
       }
     }
-    // lanes l32 and l32 ^ 16 (and ^ 8 when C = 8) of a half share e
+    // lanes l32 and l32 ^ 16 (and ^ 8 when C = 8) of a half share e (C = 32:
+    // each lane its own e, the wave's column tiles summed above)
+    if (C <= 16) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      y[r] += __shfl_xor(y[r], 16);
-      if (C == 8) y[r] += __shfl_xor(y[r], 8);
+      for (int r = 0; r < 16; ++r) {
+        y[r] += __shfl_xor(y[r], 16);
+        if (C == 8) y[r] += __shfl_xor(y[r], 8);
+      }
     }
     if (l32 < C) {
 #pragma unroll
