@@ -612,8 +612,8 @@ bool use_query_fold() {
 }
 // Level j runs on the register-query kernel with its last digit on the column
 // side: C of 8, 16 or 32 (dividing the 32 columns of an MFMA tile, so that a
-// 64-column tile is full), 16 <= d <= 64 and at least one digit left on the row
-// side (two for C = 32, which unfolded already fills one MFMA tile).  (At d = 8
+// 64-column tile is full) and 16 <= d <= 64; for C = 32, which unfolded already
+// fills one MFMA tile, only from j = 2 on (at least d rows left).  (At d = 8
 // the feature-tile kernel measured faster: 0.50 against 0.48 of peak on the
 // d = 8, p = 6 workload.)
 bool query_level_fold(const sk_sketch* s, int j) {

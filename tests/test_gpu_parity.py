@@ -105,16 +105,19 @@ def test_state_matches_oracle_moments(ident, n, h):
     assert ptr and D == w.D and cols == 1 + w.dv and cnt == n
 
 
-# (16, 64, 3) .. (32, 32, 2) put 64 or more columns (d + dv, or dv at the top) on
+# (16, 64, 3) .. (4, 64, 4) put 64 or more columns (d + dv, or dv at the top) on
 # levels j >= 1, where the query contracts the whole level without folding a
-# digit; (4, 4, 7) .. (16, 16, 3) have levels of 8 or 16 columns, whose last digit
-# the query moves to the column side for d >= 16 (d C = 128 up to 1024 columns)
-# and contracts with folded trailing digits for d <= 8
+# digit; (32, 32, 2) .. (16, 16, 3) have levels of 8, 16 or 32 columns, whose last
+# digit the query moves to the column side for d >= 16 (d C = 128 up to 2048
+# columns; 32-column levels from j = 2 on: (32, 32, 2) and (64, 32, 2) at the top,
+# (16, 16, 3) below it, (32, 32, 3) both) and contracts with folded
+# trailing digits for d <= 8
 @pytest.mark.parametrize("d,dv,p", [(8, 4, 0), (8, 4, 1), (16, 4, 3), (4, 32, 2),
                                     (128, 128, 1), (32, 8, 2), (32, 16, 2),
                                     (64, 16, 1), (128, 16, 1),
                                     (16, 64, 3), (8, 64, 3), (4, 64, 4), (32, 32, 2),
-                                    (4, 4, 7), (64, 8, 2), (8, 8, 4), (16, 16, 3)])
+                                    (4, 4, 7), (64, 8, 2), (8, 8, 4), (16, 16, 3),
+                                    (64, 32, 2), (32, 32, 3)])
 def test_other_shapes(d, dv, p):
     w = WORKLOADS[1].scaled(n=1537, m=129)
     w = type(w)(**{**w.__dict__, "d": d, "dv": dv, "p": p, "key_r": 0.8})
