@@ -1,6 +1,7 @@
 // Host side of libexpsketch: argument checks, launch planning, state ownership.
 // The C ABI is declared (with the passages each call follows) in expsketch.h.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <numeric>
@@ -51,6 +52,19 @@ namespace {
   do {                                             \
     if ((expr) != hipSuccess) return SK_EHIP;      \
   } while (0)
+
+// A kernel launch that, when given timing events, has the launch itself record
+// them (hipExtLaunchKernel: the start event takes the kernel's start time, the
+// stop event its end), so that a timed pair brackets exactly the kernels of a
+// region and not the queue around them.  Without events: a plain launch.
+template <typename F, typename... Args>
+void launch_ev(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, hipEvent_t ev0,
+               hipEvent_t ev1, Args... args) {
+  if (ev0 == nullptr && ev1 == nullptr)
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  else
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, st, ev0, ev1, 0u, args...);
+}
 
 constexpr int kMaxP = 16;
 // a_hi rows per query tile: the full layout keeps plans of 512, 256 and 128 rows
@@ -481,11 +495,18 @@ namespace {
 
 constexpr int kTimingPairs = 256;
 
-// Records the start (stop = false) or stop event of the current pair of `kind`.
-void timing_mark(sk_sketch* s, int kind, bool stop) {
+// The current timed pair of `kind` (both null when not timing or when the pairs
+// are used up): its start event goes to the first kernel launch of the timed
+// region and its stop event to the last (launch_ev); timing_done moves on to the
+// next pair.
+void timing_pair(sk_sketch* s, int kind, hipEvent_t* ev0, hipEvent_t* ev1) {
+  *ev0 = *ev1 = nullptr;
   if (!s->timing || s->trec[kind] >= (int)s->tev[kind][0].size()) return;
-  (void)hipEventRecord(s->tev[kind][stop ? 1 : 0][s->trec[kind]], s->stream);
-  if (stop) ++s->trec[kind];
+  *ev0 = s->tev[kind][0][s->trec[kind]];
+  *ev1 = s->tev[kind][1][s->trec[kind]];
+}
+void timing_done(sk_sketch* s, int kind) {
+  if (s->timing && s->trec[kind] < (int)s->tev[kind][0].size()) ++s->trec[kind];
 }
 
 // Level split and tile shape of the update GEMM for one level: fewest tiles.
@@ -1576,37 +1597,37 @@ int run_update(sk_sketch* s, const float* K, const float* V, int64_t n, long lon
   const int acc = nsplit > 1 ? 0 : 1;
   const long long rwgs = red.parts != nullptr ? rmax : 0;
   hipError_t err = hipSuccess;
-  timing_mark(s, 0, false);
+  hipEvent_t ev0, ev1;
+  timing_pair(s, 0, &ev0, &ev1);
   if (sym) {
-    for (size_t g = 0; g + 1 < s->sgroup.size(); ++g) {
+    const size_t ng = s->sgroup.size() - 1;
+    for (size_t g = 0; g < ng; ++g) {
       const int t0 = s->sgroup[g], nt = s->sgroup[g + 1] - t0;
       const SymUpdTile& sh = s->sutiles[t0];
       PendingReduce rg = red;                  // the reduce rides on the first launch
       if (g > 0) rg.parts = nullptr;
       const long long extra = g == 0 ? rwgs : 0;
-      hipLaunchKernelGGL(sym_update_kernel_for(sh.rb, sh.cb, s->center != nullptr),
-                         dim3((unsigned)((long long)nt * nsplit * s->h + extra)), dim3(SK_WG),
-                         lds, s->stream, K, V, (long long)n, hkeys, s->d, s->dv, s->d_sutiles + t0,
-                         nt, s->tb, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center, rg);
+      launch_ev(sym_update_kernel_for(sh.rb, sh.cb, s->center != nullptr),
+                dim3((unsigned)((long long)nt * nsplit * s->h + extra)), dim3(SK_WG), lds,
+                s->stream, g == 0 ? ev0 : nullptr, g + 1 == ng ? ev1 : nullptr, K, V,
+                (long long)n, hkeys, s->d, s->dv, s->d_sutiles + t0, nt, s->tb, kps, nsplit,
+                s->h, dst, s->XS, sstride, acc, s->center, rg);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) err = e;
     }
   } else if (kr) {
-    hipLaunchKernelGGL(update_kr_kernel_for(s->center != nullptr, s->d),
-                       dim3((unsigned)(kr_wgs + rwgs)), dim3(64 * KR_WAVES), 0, s->stream, K, V,
-                       (long long)n, hkeys, s->dv, s->d_kunits, ksp, s->h, dst, s->XS, sstride,
-                       acc, s->center, red);
+    launch_ev(update_kr_kernel_for(s->center != nullptr, s->d), dim3((unsigned)(kr_wgs + rwgs)),
+              dim3(64 * KR_WAVES), 0, s->stream, ev0, ev1, K, V, (long long)n, hkeys, s->dv,
+              s->d_kunits, ksp, s->h, dst, s->XS, sstride, acc, s->center, red);
     err = hipGetLastError();
   } else {
-    hipLaunchKernelGGL(update_kernel_for(s->center != nullptr, s->d, s->dv),
-                       dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)),
-                       dim3(SK_WG),
-                       lds, s->stream, K, V, (long long)n, hkeys, s->d, s->dv, s->logd,
-                       s->d_utiles, ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc,
-                       s->center, red);
+    launch_ev(update_kernel_for(s->center != nullptr, s->d, s->dv),
+              dim3((unsigned)((long long)ntiles * nsplit * s->h + rwgs)), dim3(SK_WG), lds,
+              s->stream, ev0, ev1, K, V, (long long)n, hkeys, s->d, s->dv, s->logd, s->d_utiles,
+              ntiles, kps, nsplit, s->h, dst, s->XS, sstride, acc, s->center, red);
     err = hipGetLastError();
   }
-  timing_mark(s, 0, true);
+  timing_done(s, 0);
   if (deferred) {
     s->pend = dst;
     s->pend_ns = nsplit;
@@ -1773,38 +1794,59 @@ int sketch_query(sk_handle s, const float* Q, int64_t m, float* out, float* Z) {
     const int rc = take_workspace(&s->qws, pbytes, s->stream, &parts, &own);
     if (rc != SK_OK) return rc;
   }
-  timing_mark(s, 1, false);
   hipError_t e1 = hipSuccess;
-  if (s->layout == SK_LAYOUT_SYM && !s->sqtiles.empty()) {
-    const long long nst = (long long)s->sqtiles.size();
-    hipLaunchKernelGGL(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
-                       sym_query_lds_bytes(s->d), s->stream, Q, (long long)m, s->d, s->state,
-                       s->XS, s->d_sqtiles, (int)nst, (int)nqt, s->tb, qp.pb, parts);
-    e1 = hipGetLastError();
+  {
+    // the timed region's kernels: the start event on the first, the stop event on
+    // the last
+    hipEvent_t ev0, ev1;
+    timing_pair(s, 1, &ev0, &ev1);
+    const bool sq = s->layout == SK_LAYOUT_SYM && !s->sqtiles.empty();
+    const bool sd = s->layout == SK_LAYOUT_SYM && !s->sdtiles.empty();
+    const int nl = s->layout == SK_LAYOUT_SYM ? (sq ? 1 : 0) + (sd ? 1 : 0)
+                                              : (int)qp.groups.size();
+    int li = 0;
+    auto evs = [&](hipEvent_t* a, hipEvent_t* b) {
+      *a = li == 0 ? ev0 : nullptr;
+      *b = li + 1 == nl ? ev1 : nullptr;
+      ++li;
+    };
+    hipEvent_t a, b;
+    if (sq) {
+      const long long nst = (long long)s->sqtiles.size();
+      evs(&a, &b);
+      launch_ev(sk_sym_query_kernel, dim3((unsigned)(nst * nqt * s->h)), dim3(SK_WG),
+                sym_query_lds_bytes(s->d), s->stream, a, b, Q, (long long)m, s->d,
+                (const float*)s->state, s->XS, (const SymQryTile*)s->d_sqtiles, (int)nst,
+                (int)nqt, s->tb, qp.pb, parts);
+      e1 = hipGetLastError();
+    }
+    if (sd) {
+      const long long nsd = (long long)s->sdtiles.size();
+      evs(&a, &b);
+      launch_ev(sym_dg_kernel_for(s->logd), dim3((unsigned)(nsd * nqt * s->h)), dim3(SK_WG),
+                sym_dg_lds_bytes(), s->stream, a, b, Q, (long long)m, (const float*)s->state,
+                s->XS, (const SymDgTile*)s->d_sdtiles, (int)nsd, (const SymDgRun*)s->d_sdruns,
+                (int)nqt, qp.pb, parts);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) e1 = e;
+    }
+    for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < qp.groups.size(); ++g) {
+      const sk_sketch::QGroup& G = qp.groups[g];
+      QueryKernel kern = G.kind == 0   ? query_kernel_for(s->logd)
+                         : G.kind == 1 ? query_dg_kernel_for(s->logd)
+                                       : query_dg16_kernel_for(s->logd);
+      const size_t lds = G.kind == 0   ? query_lds_bytes(s->d)
+                         : G.kind == 1 ? query_dg_lds_bytes(s->d)
+                                       : query_dg16_lds_bytes(s->d);
+      evs(&a, &b);
+      launch_ev(kern, dim3((unsigned)((long long)G.count * nqt * s->h)), dim3(SK_WG), lds,
+                s->stream, a, b, Q, (long long)m, (const float*)s->state, s->XS,
+                (const QryTile*)(qp.d_run + G.off), G.count, (int)nqt, qp.pb, parts);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) e1 = e;
+    }
+    timing_done(s, 1);
   }
-  if (s->layout == SK_LAYOUT_SYM && !s->sdtiles.empty()) {
-    const long long nsd = (long long)s->sdtiles.size();
-    hipLaunchKernelGGL(sym_dg_kernel_for(s->logd), dim3((unsigned)(nsd * nqt * s->h)),
-                       dim3(SK_WG), sym_dg_lds_bytes(), s->stream, Q, (long long)m, s->state,
-                       s->XS, s->d_sdtiles, (int)nsd, s->d_sdruns, (int)nqt, qp.pb, parts);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) e1 = e;
-  }
-  for (size_t g = 0; s->layout != SK_LAYOUT_SYM && g < qp.groups.size(); ++g) {
-    const sk_sketch::QGroup& G = qp.groups[g];
-    QueryKernel kern = G.kind == 0   ? query_kernel_for(s->logd)
-                       : G.kind == 1 ? query_dg_kernel_for(s->logd)
-                                     : query_dg16_kernel_for(s->logd);
-    const size_t lds = G.kind == 0   ? query_lds_bytes(s->d)
-                       : G.kind == 1 ? query_dg_lds_bytes(s->d)
-                                     : query_dg16_lds_bytes(s->d);
-    hipLaunchKernelGGL(kern, dim3((unsigned)((long long)G.count * nqt * s->h)), dim3(SK_WG), lds,
-                       s->stream, Q, (long long)m, s->state, s->XS, qp.d_run + G.off, G.count,
-                       (int)nqt, qp.pb, parts);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) e1 = e;
-  }
-  timing_mark(s, 1, true);
   // one finishing workgroup per (head, query)
   hipLaunchKernelGGL(sk_query_finish, dim3((unsigned)(m * s->h)), dim3(256), 0, s->stream,
                      parts, qp.d_fin, ntiles, (int)nqt, qp.pb, (long long)m, s->d, s->dv,
@@ -1850,12 +1892,13 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
     const int rc = settle(s);
     if (rc != SK_OK) return rc;
   }
-  timing_mark(s, 2, false);
-  hipLaunchKernelGGL(sk_step_kernel, dim3((unsigned)((long long)nt * s->h)), dim3(256), 0,
-                     s->stream, s->state, s->XS, s->d_stiles, nt, s->d, s->dv, s->logd, k, v,
-                     q, s->tb, s->sparts, s->center);
+  hipEvent_t ev0, ev1;
+  timing_pair(s, 2, &ev0, &ev1);
+  launch_ev(sk_step_kernel, dim3((unsigned)((long long)nt * s->h)), dim3(256), 0, s->stream, ev0,
+            ev1, s->state, s->XS, (const StepTile*)s->d_stiles, nt, s->d, s->dv, s->logd, k, v,
+            q, s->tb, s->sparts, (const float*)s->center);
   hipError_t e1 = hipGetLastError();
-  timing_mark(s, 2, true);
+  timing_done(s, 2);
   hipLaunchKernelGGL(sk_step_finish, dim3((unsigned)s->h), dim3(256), 0, s->stream, s->sparts,
                      nt, s->d, s->dv, (float)(s->count + 1), q, s->center, out, Z);
   hipError_t e2 = hipGetLastError();
@@ -2040,13 +2083,14 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   const long long nn = n;
   const long long mm = m;
   const bool timed = fixed == nullptr && g_xtiming && g_xrec < (int)g_xev[0].size();
-  if (timed) (void)hipEventRecord(g_xev[0][g_xrec], st);
+  hipEvent_t xev0 = timed ? g_xev[0][g_xrec] : nullptr;
+  hipEvent_t xev1 = timed ? g_xev[1][g_xrec] : nullptr;
   if (decode) {
     const int mq = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
     dim3 grid(nsplit, h), blk(256);
-#define SK_DEC(BB, MQ)                                                              \
-  hipLaunchKernelGGL((sk_exact_decode<BB, MQ>), grid, blk, 0, st, K, V, nn, d, dv, Q, \
-                     mm, kps, nsplit, parts)
+#define SK_DEC(BB, MQ)                                                                \
+  launch_ev(sk_exact_decode<BB, MQ>, grid, blk, 0, st, xev0, xev1, K, V, nn, d, dv, Q, mm, kps, \
+            nsplit, parts)
 #define SK_DEC_B(BB)              \
   switch (mq) {                   \
     case 1: SK_DEC(BB, 1); break; \
@@ -2067,27 +2111,27 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
   } else if (!use_mfma) {
     dim3 grid((unsigned)(nsplit * nqt), h), blk(256);
     if (bmax <= 4)
-      hipLaunchKernelGGL((sk_exact_tiled<4, 32>), grid, blk, 0, st, K, V, nn, d, dv, Q, mm,
-                         kps, nsplit, parts);
+      launch_ev(sk_exact_tiled<4, 32>, grid, blk, 0, st, xev0, xev1, K, V, nn, d, dv, Q, mm, kps,
+                nsplit, parts);
     else
-      hipLaunchKernelGGL((sk_exact_tiled<8, 32>), grid, blk, 0, st, K, V, nn, d, dv, Q, mm,
-                         kps, nsplit, parts);
+      launch_ev(sk_exact_tiled<8, 32>, grid, blk, 0, st, xev0, xev1, K, V, nn, d, dv, Q, mm, kps,
+                nsplit, parts);
   } else {
     // fp32 MFMA: queries x keys, then values x keys; value columns in blocks of 32
     dim3 grid((unsigned)(nsplit * nqt), h), blk(256);
     const int ncb = dv <= 32 ? 1 : (dv <= 64 ? 2 : 4);
-#define SK_XM(DD, NC)                                                                \
-  hipLaunchKernelGGL((sk_exact_mfma<DD, NC>), grid, blk, 0, st, K, V, nn, dv, Q, mm, kps, \
-                     nsplit, parts)
+#define SK_XM(DD, NC)                                                                     \
+  launch_ev(sk_exact_mfma<DD, NC>, grid, blk, 0, st, xev0, xev1, K, V, nn, dv, Q, mm, kps, nsplit, \
+            parts)
 #define SK_XM_D(DD)                   \
   switch (ncb) {                      \
     case 1: SK_XM(DD, 1); break;      \
     case 2: SK_XM(DD, 2); break;      \
     default: SK_XM(DD, 4); break;     \
   }
-#define SK_XM16(DD, QB)                                                                    \
-  hipLaunchKernelGGL((sk_exact_mfma16<DD, 16, QB>), grid, blk, 0, st, K, V, nn, Q, mm, kps, \
-                     nsplit, parts)
+#define SK_XM16(DD, QB)                                                                  \
+  launch_ev(sk_exact_mfma16<DD, 16, QB>, grid, blk, 0, st, xev0, xev1, K, V, nn, Q, mm, kps, \
+            nsplit, parts)
     if (mfma16) {
       switch (d) {
         case 16: SK_XM16(16, 4); break;
@@ -2109,7 +2153,7 @@ int exact_run(const float* K, const float* V, int64_t n, int d, int dv, int h,
 #undef SK_XM
   }
   hipError_t e1 = hipGetLastError();
-  if (timed) (void)hipEventRecord(g_xev[1][g_xrec++], st);
+  if (timed) ++g_xrec;
   hipLaunchKernelGGL(sk_exact_combine, dim3((unsigned)(h * m)), dim3(256), 0, st, parts,
                      nsplit, mm, dv, h, out, Z);
   hipError_t e2 = hipGetLastError();

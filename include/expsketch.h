@@ -253,10 +253,10 @@ int exact_attend_noalloc(const float* K, const float* V, int64_t n, int d, int d
 
 /*
  * exact_timing -- kernel timing of the exact path with HIP events (for
- * measurement).  While enabled, each exact_attend call records a pair of
- * library-owned events on its stream around its slice kernel (the decode or
- * batched kernel, not the combine), up to 256 pairs; enable != 0 starts (and
- * clears) recording, 0 stops it.
+ * measurement).  While enabled, each exact_attend call has its slice kernel (the
+ * decode or batched kernel, not the combine) record a pair of library-owned
+ * events at its own start and end (the launch takes them: hipExtLaunchKernel), up
+ * to 256 pairs; enable != 0 starts (and clears) recording, 0 stops it.
  * exact_kernel_times -- waits for the last recorded pair, writes the elapsed
  * milliseconds of up to `cap` pairs into ms (host array), sets *count to the
  * number recorded, and clears them.
@@ -308,10 +308,12 @@ int sketch_info(sk_handle s, int* d, int* dv, int* p, int* h, int64_t* D,
 /*
  * sketch_timing -- kernel timing with HIP events on the handle's stream (for
  * measurement).  While enabled, each sketch_update records a pair of
- * library-owned events around its moment-update kernel(s) (kind 0), each
- * sketch_query around its contraction kernel (kind 1) and each sketch_step around
- * its fused update-and-answer kernel (kind 2), up to 256 pairs per kind;
- * later calls are not recorded until the pairs are collected.  enable != 0
+ * library-owned events over its moment-update kernel(s) (kind 0), each
+ * sketch_query over its contraction kernel(s) (kind 1) and each sketch_step over
+ * its fused update-and-answer kernel (kind 2), up to 256 pairs per kind; the
+ * launches take them (hipExtLaunchKernel: the first kernel's start, the last
+ * kernel's end), so a pair spans the kernels and not the queue before them.
+ * Later calls are not recorded until the pairs are collected.  enable != 0
  * starts (and clears) recording, 0 stops it.
  * sketch_kernel_times -- waits for the last recorded event of `kind`, writes the
  * elapsed milliseconds of up to `cap` recorded pairs into ms (host array), sets
