@@ -51,6 +51,7 @@ struct sk_coreset {
   unsigned long long seed = 0;
   hipStream_t stream = nullptr;
   int device = 0;
+  int num_cu = 256;           // compute units of the device (tail-query slicing)
   int64_t count = 0;          // points ingested per head
   int nfill = 0;              // points in the partial buffer
   long long serial = 0;       // reduces done
@@ -294,8 +295,9 @@ int append_rows(sk_coreset* c, const CsRef& src, long long n) {
   return SK_OK;
 }
 
-// Segments of the points: the partial buffer, then the levels (increasing).
-CsSegs segments(const sk_coreset* c, long long* npts) {
+// Segments of the points: the partial buffer, then the levels (increasing), cut
+// into slices of `slice` points for the tail query.
+CsSegs segments(const sk_coreset* c, long long* npts, int slice_pts = CS_SLICE) {
   CsSegs sg{};
   long long tot = 0;
   int slice = 0;
@@ -309,7 +311,7 @@ CsSegs segments(const sk_coreset* c, long long* npts) {
     s.count = count;
     s.slice0 = slice;
     s.w = w;
-    slice += (count + CS_SLICE - 1) / CS_SLICE;
+    slice += (count + slice_pts - 1) / slice_pts;
     tot += count;
   };
   if (c->fill >= 0) add(c->fill, c->nfill, 1.f);
@@ -320,7 +322,7 @@ CsSegs segments(const sk_coreset* c, long long* npts) {
   return sg;
 }
 
-using TailKernel = void (*)(const float*, long long, int, CsSegs, float*);
+using TailKernel = void (*)(const float*, long long, int, CsSegs, int, float*);
 template <int D>
 TailKernel tail_for_dv(int dv) {
   switch (dv) {
@@ -361,6 +363,8 @@ int coreset_create(int d, int dv, int p, int h, int block, double c0, uint64_t s
   std::vector<double> inv(CS_NINV, 1.0);
   for (int j = 1; j < CS_NINV; ++j) inv[j] = 1.0 / (double)j;
   if (hipGetDevice(&c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&c->num_cu, hipDeviceAttributeMultiprocessorCount, c->device) !=
+          hipSuccess ||
       hipMalloc(&c->inv, sizeof(double) * CS_NINV) != hipSuccess ||
       hipMemcpy(c->inv, inv.data(), sizeof(double) * CS_NINV, hipMemcpyHostToDevice) !=
           hipSuccess) {
@@ -493,9 +497,17 @@ int coreset_query(sk_coreset_handle c, const float* Q, int64_t m, float* out, fl
   const int rc = flush(c);
   if (rc != SK_OK) return rc;
   long long np = 0;
-  const CsSegs sg = segments(c, &np);
-  if (np == 0) return SK_OK;                  // no tail: the head answer stands
   const long long nqt = (m + CS_QT - 1) / CS_QT;
+  // slices of 512 points, shorter (down to 64) until the launch has about four
+  // workgroups per CU: a decode-sized query (a few hundred queries per head) has
+  // few query tiles, and one workgroup per (query tile, slice, head)
+  int slice_pts = CS_SLICE;
+  CsSegs sg = segments(c, &np, slice_pts);
+  while (slice_pts > 64 && nqt * sg.nslices * c->h < 4LL * c->num_cu) {
+    slice_pts /= 2;
+    sg = segments(c, &np, slice_pts);
+  }
+  if (np == 0) return SK_OK;                  // no tail: the head answer stands
   if (nqt > 0x7fffffffLL || sg.nslices > 65535 || c->h > 65535) return SK_EINVAL;
   const size_t need = sizeof(float) * (size_t)c->h * m * sg.nslices * (1 + c->dv);
   if (c->parts_bytes < need) {
@@ -510,7 +522,8 @@ int coreset_query(sk_coreset_handle c, const float* Q, int64_t m, float* out, fl
     c->parts_bytes = need;
   }
   hipLaunchKernelGGL(tail_kernel_for(c->d, c->dv), dim3((unsigned)nqt, sg.nslices, c->h),
-                     dim3(CS_QT), 0, c->stream, Q, (long long)m, c->p, sg, c->parts);
+                     dim3(CS_QT * CS_TPQ), 0, c->stream, Q, (long long)m, c->p, sg, slice_pts,
+                     c->parts);
   CS_TRY(hipGetLastError());
   hipLaunchKernelGGL(cs_tail_combine, dim3((unsigned)(c->h * m)), dim3(256), 0, c->stream,
                      c->parts, sg.nslices, (long long)m, c->dv, out, Z);

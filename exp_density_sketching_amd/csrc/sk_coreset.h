@@ -29,7 +29,8 @@
 #define CS_MAXOPS 32       // reduces per launch
 #define CS_MAXSEG 64       // point segments of a tail query (buffer + levels)
 #define CS_TP 32           // pairs per Gram tile side (64 points)
-#define CS_QT 128          // queries per tail-query workgroup
+#define CS_QT 32           // queries per tail-query workgroup
+#define CS_TPQ 4           // threads per query in the tail query
 #define CS_PT 32           // points per tail-query stage
 
 // A block of points of every head: rows of head hd start at K + hd * hsK.
@@ -53,7 +54,8 @@ struct CsOps {
 };
 
 // Tail-query segments: the partial buffer (weight 1) and the level blocks
-// (weight 2^l), each cut into slices of CS_SLICE points.
+// (weight 2^l), each cut into slices of up to CS_SLICE points (the tail query
+// picks the length per call).
 struct CsSeg {
   const float* K;
   const float* V;
@@ -67,7 +69,7 @@ struct CsSegs {
   int n;
   int nslices;
 };
-#define CS_SLICE 512
+#define CS_SLICE 512     // longest tail-query slice (points)
 
 #define CS_NINV 512       // entries of the 1/j table (float64; entry 0 unused)
 
@@ -399,25 +401,31 @@ __device__ inline float cs_tail_exp32(float x, int p, const float* __restrict__ 
 }
 
 // Tail sums of a query tile against one slice of points: partial [1 + dv] per
-// (head, query, slice): sum_s w R_p(<q, k_s>) [1, v_s].  One thread per query
-// (its query in registers), points staged CS_PT at a time in LDS.
+// (head, query, slice): sum_s w R_p(<q, k_s>) [1, v_s].  CS_TPQ threads per query
+// (its query in registers in each), thread r taking points r, r + CS_TPQ, .. of
+// every stage of CS_PT points staged in LDS (rows padded by 4 floats, so the
+// float4 reads of the CS_TPQ points hit separate banks); the dot product in four
+// independent partial sums; the query's CS_TPQ partials added in a fixed tree
+// (xor shuffles) at the end.
 template <int D, int DV>
-__global__ __launch_bounds__(CS_QT)
+__global__ __launch_bounds__(CS_QT * CS_TPQ)
 void cs_tail_kernel(const float* __restrict__ Q, long long m, int p, CsSegs segs,
-                    float* __restrict__ parts) {
-  __shared__ float Ks[CS_PT][D];
-  __shared__ float Vs[CS_PT][DV];
+                    int slice_pts, float* __restrict__ parts) {
+  constexpr int NTH = CS_QT * CS_TPQ;
+  __shared__ float Ks[CS_PT][D + 4];
+  __shared__ float Vs[CS_PT][DV + 4];
   __shared__ float inv[96];
   const int tid = threadIdx.x;
+  const int ql = tid / CS_TPQ, rr = tid % CS_TPQ;
   const int qt = blockIdx.x, slice = blockIdx.y, head = blockIdx.z;
-  for (int j = tid; j < 96; j += CS_QT) inv[j] = j == 0 ? 1.f : 1.f / (float)j;
+  for (int j = tid; j < 96; j += NTH) inv[j] = j == 0 ? 1.f : 1.f / (float)j;
   // the slice's segment
   int sg = 0;
   while (sg + 1 < segs.n && segs.s[sg + 1].slice0 <= slice) ++sg;
   const CsSeg S = segs.s[sg];
-  const int p0 = (slice - S.slice0) * CS_SLICE;
-  const int np = min(CS_SLICE, S.count - p0);
-  const long long q = (long long)qt * CS_QT + tid;
+  const int p0 = (slice - S.slice0) * slice_pts;
+  const int np = min(slice_pts, S.count - p0);
+  const long long q = (long long)qt * CS_QT + ql;
   const bool qv = q < m;
   float qr[D];
   const float* Qh = Q + ((long long)head * m + (qv ? q : 0)) * D;
@@ -434,30 +442,49 @@ void cs_tail_kernel(const float* __restrict__ Q, long long m, int p, CsSegs segs
   for (int s0 = 0; s0 < np; s0 += CS_PT) {
     const int ns = min(CS_PT, np - s0);
     __syncthreads();
-    for (int e = tid; e < CS_PT * (D / 4); e += CS_QT) {
+    for (int e = tid; e < CS_PT * (D / 4); e += NTH) {
       const int r = e / (D / 4), c4 = e - r * (D / 4);
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (r < ns) x = reinterpret_cast<const float4*>(Kb + (long long)(s0 + r) * D)[c4];
       *reinterpret_cast<float4*>(&Ks[r][4 * c4]) = x;
     }
-    for (int e = tid; e < CS_PT * (DV / 4); e += CS_QT) {
+    for (int e = tid; e < CS_PT * (DV / 4); e += NTH) {
       const int r = e / (DV / 4), c4 = e - r * (DV / 4);
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (r < ns) x = reinterpret_cast<const float4*>(Vb + (long long)(s0 + r) * DV)[c4];
       *reinterpret_cast<float4*>(&Vs[r][4 * c4]) = x;
     }
     __syncthreads();
-    for (int j = 0; j < ns; ++j) {
-      float s = 0.f;
+    for (int j = rr; j < ns; j += CS_TPQ) {
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
-      for (int a = 0; a < D; ++a) s = fmaf(qr[a], Ks[j][a], s);
-      const float r = S.w * cs_tail_exp32(s, p, inv);
+      for (int a = 0; a < D; a += 4) {
+        const float4 k = *reinterpret_cast<const float4*>(&Ks[j][a]);
+        d0 = fmaf(qr[a], k.x, d0);
+        d1 = fmaf(qr[a + 1], k.y, d1);
+        d2 = fmaf(qr[a + 2], k.z, d2);
+        d3 = fmaf(qr[a + 3], k.w, d3);
+      }
+      const float r = S.w * cs_tail_exp32((d0 + d1) + (d2 + d3), p, inv);
       z += r;
 #pragma unroll
-      for (int c = 0; c < DV; ++c) acc[c] = fmaf(r, Vs[j][c], acc[c]);
+      for (int c = 0; c < DV; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&Vs[j][c]);
+        acc[c] = fmaf(r, v.x, acc[c]);
+        acc[c + 1] = fmaf(r, v.y, acc[c + 1]);
+        acc[c + 2] = fmaf(r, v.z, acc[c + 2]);
+        acc[c + 3] = fmaf(r, v.w, acc[c + 3]);
+      }
     }
   }
-  if (qv) {
+  // the query's partials: lanes 4 ql .. 4 ql + 3, the same fixed tree in each
+#pragma unroll
+  for (int o = 1; o < CS_TPQ; o <<= 1) {
+    z += __shfl_xor(z, o);
+#pragma unroll
+    for (int c = 0; c < DV; ++c) acc[c] += __shfl_xor(acc[c], o);
+  }
+  if (qv && rr == 0) {
     float* P = parts + (((long long)head * m + q) * segs.nslices + slice) * (1 + DV);
     P[0] = z;
 #pragma unroll
