@@ -236,6 +236,15 @@ def test_full_size_decode_exact():
     _check_exact(w, K, V, Q, label="decode 32x128K")
 
 
+def test_full_size_single_head_decode_exact():
+    """Decode over one long head (d = dv = 32, 1M keys): hundreds of slices folded
+    per query, m = 1 and 3."""
+    for m in (1, 3):
+        w = WORKLOADS[3].scaled(m=m)
+        K, V, Q = generate(w)
+        _check_exact(w, K, V, Q, label=f"decode 1x1M m={m}")
+
+
 def test_sketch_error_within_bound():
     """GPU sketch against GPU exact, against the truncation bound (high-temperature
     workloads, where the bound is informative)."""
