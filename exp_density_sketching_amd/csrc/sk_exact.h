@@ -139,8 +139,16 @@ __device__ __forceinline__ void exact_fold(const float* __restrict__ P, int nspl
 // The partial record per (head, query, slice) is the one of sk_exact_decode.
 #define SK_XQ 128          // queries per workgroup (4 waves x 32)
 #define SK_XK 32           // keys per stage
+// Waves per SIMD the register allocation of sk_exact_mfma<D, NCB> keeps room for:
+// three where the accumulators and the query leave space for the next stage's
+// rows (measured with those rows in flight: 0.59 -> 0.64 of the fp32 peak at
+// d = dv = 64, 0.58 -> 0.59 at d = dv = 32), the compiler's choice otherwise.
 template <int D, int NCB>
-__global__ __launch_bounds__(256)
+struct XmWaves {
+  static constexpr int v = (D / 2 + 16 * NCB <= 64) ? 3 : 1;
+};
+template <int D, int NCB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XmWaves<D, NCB>::v)))
 void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
                    long long n, int dv, const float* __restrict__ Q, long long m,
                    long long keys_per_split, int nsplit, float* __restrict__ parts) {
@@ -173,23 +181,54 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx16{0.f};
 
+  // a stage's K and V rows: KT and VT float4 per thread, fetched into registers
+  // one stage ahead (their loads run under the current stage's MFMAs), zeros
+  // past the slice's last key and past dv
+  constexpr int KT = (SK_XK * D / 4 + 255) / 256;
+  constexpr int VT = (SK_XK * DVP / 4 + 255) / 256;
+  float4 kx[KT], vx[VT];
+  auto fetch = [&](long long k0) {
+    const long long left = k_end - k0;
+    const int nk = left < SK_XK ? (int)left : SK_XK;
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      const int i = tid + 256 * u;
+      const int key = i / (D / 4), e = 4 * (i - key * (D / 4));
+      kx[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < SK_XK * D / 4 && key < nk)
+        kx[u] = *reinterpret_cast<const float4*>(Kh + (k0 + key) * D + e);
+    }
+#pragma unroll
+    for (int u = 0; u < VT; ++u) {
+      const int i = tid + 256 * u;
+      const int key = i / (DVP / 4), c = 4 * (i - key * (DVP / 4));
+      vx[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < SK_XK * DVP / 4 && key < nk && c < dv)
+        vx[u] = *reinterpret_cast<const float4*>(Vh + (k0 + key) * dv + c);
+    }
+  };
+  if (k_begin < k_end) fetch(k_begin);
+
   for (long long kb = k_begin; kb < k_end; kb += SK_XK) {
     const long long left = k_end - kb;
     const int nk = left < SK_XK ? (int)left : SK_XK;
-    for (int i = tid; i < SK_XK * D / 4; i += 256) {
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      const int i = tid + 256 * u;
       const int key = i / (D / 4), e = 4 * (i - key * (D / 4));
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (key < nk) x = *reinterpret_cast<const float4*>(Kh + (kb + key) * D + e);
-      float* dst = Ks + key * LDKE + e;
-      dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+      if (i < SK_XK * D / 4) {
+        float* dst = Ks + key * LDKE + e;
+        dst[0] = kx[u].x; dst[1] = kx[u].y; dst[2] = kx[u].z; dst[3] = kx[u].w;
+      }
     }
-    for (int i = tid; i < SK_XK * DVP / 4; i += 256) {
+#pragma unroll
+    for (int u = 0; u < VT; ++u) {
+      const int i = tid + 256 * u;
       const int key = i / (DVP / 4), c = 4 * (i - key * (DVP / 4));
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (key < nk && c < dv) x = *reinterpret_cast<const float4*>(Vh + (kb + key) * dv + c);
-      *reinterpret_cast<float4*>(Vs + key * LDV + c) = x;
+      if (i < SK_XK * DVP / 4) *reinterpret_cast<float4*>(Vs + key * LDV + c) = vx[u];
     }
     __syncthreads();
+    if (kb + SK_XK < k_end) fetch(kb + SK_XK);
     floatx16 s = {0.f};
 #pragma unroll
     for (int st = 0; st < D / 2; ++st)
