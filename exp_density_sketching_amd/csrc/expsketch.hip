@@ -660,6 +660,13 @@ int query_level_kind(const sk_sketch* s, int j) {
   return 0;
 }
 
+// MFMA work of a last-digit query tile, in row-steps of 32 columns: its rows
+// times its 32-column GEMM tiles (one or two)
+long long query_tile_work(const QryTile& T) {
+  const long long gw = T.t ? (long long)T.nalo * T.C : T.fw;
+  return (T.s == 0 ? 1 : T.a1 - T.a0) * ((gw + 31) / 32);
+}
+
 void plan_query_level(sk_sketch* s, int j, sk_sketch::QPlan* qp) {
   const int d = s->d, C = s->C[j];
   const int kind = query_level_kind(s, j);
@@ -1329,6 +1336,13 @@ int sketch_create_ex(int d, int dv, int p, int h, int layout, void* hip_stream,
         for (size_t i = 0; i < qp.tiles.size(); ++i)
           if (qp.kind[i] == key) qp.run.push_back(qp.tiles[i]);
         const int cnt = (int)qp.run.size() - off;
+        // the last-digit kernels dispatch their tiles in this order: longest first,
+        // so the short ones fill the slots the long ones leave at the end
+        if (key == 16)
+          std::stable_sort(qp.run.begin() + off, qp.run.end(),
+                           [](const QryTile& x, const QryTile& y) {
+                             return query_tile_work(x) > query_tile_work(y);
+                           });
         if (cnt > 0) qp.groups.push_back(sk_sketch::QGroup{key / 16, key % 16, off, cnt});
       }
     }

@@ -146,9 +146,13 @@ void sk_query_dg_kernel(const float* __restrict__ Q, long long m,
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lhi = lane >> 5;
   const long long lg = blockIdx.x;
-  const int tile_id = (int)(lg % ntiles);
-  const int qt = (int)((lg / ntiles) % nqt);
-  const long long head = lg / ((long long)nqt * ntiles);
+  // tile slowest (the grid is tiles x heads x query tiles): the launch
+  // dispatches the tiles in plan order, the longest first, each for every head
+  // and query tile
+  const long long per_tile = (long long)gridDim.x / ntiles;
+  const int tile_id = (int)(lg / per_tile);
+  const int qt = (int)(lg % nqt);
+  const long long head = (lg % per_tile) / nqt;
   const QryTile T = tiles[tile_id];
   const long long q0 = (long long)qt * SK_DGQ;
   {
@@ -394,9 +398,13 @@ void sk_query_dgr_kernel(const float* __restrict__ Q, long long m,
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lhi = lane >> 5;
   const long long lg = blockIdx.x;
-  const int tile_id = (int)(lg % ntiles);
-  const int qt = (int)((lg / ntiles) % nqt);
-  const long long head = lg / ((long long)nqt * ntiles);
+  // tile slowest (the grid is tiles x heads x query tiles): the launch
+  // dispatches the tiles in plan order, the longest first, each for every head
+  // and query tile
+  const long long per_tile = (long long)gridDim.x / ntiles;
+  const int tile_id = (int)(lg / per_tile);
+  const int qt = (int)(lg % nqt);
+  const long long head = (lg % per_tile) / nqt;
   const QryTile T = tiles[tile_id];
   const long long q0 = (long long)qt * SK_DGQ;
   // the workgroup's queries: loads past query m - 1 return zero
