@@ -128,16 +128,25 @@ __device__ __forceinline__ void exact_fold(const float* __restrict__ P, int nspl
 // one key slice; per stage of 32 keys (K and V rows staged in LDS):
 //   S^T = K Q^T         v_mfma_f32_32x32x2_f32, rows = keys, columns = queries;
 //                       the lane's query components stay in registers
-//   online softmax      the stage's row maximum of a query is the larger of its
-//                       two lanes' 16 entries (one cross-lane exchange); p =
-//                       e^{s - mu}, previous sums rescaled by e^{mu_old - mu}
+//   online softmax      in base 2 (queries prescaled by log2 e, p = 2^{s - ref});
+//                       the stage's row maximum of a query is the larger of its
+//                       two lanes' 16 entries (one cross-lane exchange); the
+//                       reference ref is raised, and the sums rescaled by
+//                       2^{ref_old - ref}, only when a stage maximum exceeds it by
+//                       more than SK_XTAU (p <= 2^SK_XTAU otherwise), a branch
+//                       the whole wave takes or skips
 //   O^T += V^T P^T      the same MFMA with P taken straight from the first
 //                       product's accumulator registers: an MFMA sums over its K
 //                       index in any order, so at k-step t each lane half uses
 //                       the key its register t holds, and reads that key's value
 //                       row from LDS as the other operand.
-// The partial record per (head, query, slice) is the one of sk_exact_decode.
+// K rows sit in LDS with a stride of D + 2 floats: the two lane halves of a
+// k-step read neighbouring features of 32 rows, which then fall in distinct
+// banks for every D (D + 1 made the halves collide at D >= 64).
+// The partial record per (head, query, slice) is the one of sk_exact_decode
+// (mu = ref in natural-log units).
 #define SK_XQ 128          // queries per workgroup (4 waves x 32)
+#define SK_XTAU 8.f        // reference slack of the base-2 online softmax
 #define SK_XK 32           // keys per stage
 // Waves per SIMD the register allocation of sk_exact_mfma<D, NCB> keeps room for:
 // three where the accumulators and the query leave space for the next stage's
@@ -152,7 +161,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(XmWaves<D, 
 void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
                    long long n, int dv, const float* __restrict__ Q, long long m,
                    long long keys_per_split, int nsplit, float* __restrict__ parts) {
-  constexpr int LDKE = D + 1;               // K stage row stride (keys x D)
+  constexpr int LDKE = D + 2;               // K stage row stride (keys x D)
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float LN2 = 0.6931471805599453f;
   constexpr int DVP = 32 * NCB;             // value columns, padded to 32
   constexpr int LDV = DVP + 8;              // the two lane halves' rows 32 banks apart
   __shared__ float Ks[SK_XK * LDKE];
@@ -171,10 +182,10 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
   const float* Kh = K + head * n * D;
   const float* Vh = V + head * n * dv;
 
-  float qreg[D / 2];                        // Q[q][2 st + g]
+  float qreg[D / 2];                        // Q[q][2 st + g] * log2 e
 #pragma unroll
   for (int st = 0; st < D / 2; ++st)
-    qreg[st] = qok ? Q[(head * m + q) * D + 2 * st + g] : 0.f;
+    qreg[st] = qok ? Q[(head * m + q) * D + 2 * st + g] * LOG2E : 0.f;
 
   float mu = -INFINITY, l = 0.f;
   floatx16 acc[NCB];
@@ -217,8 +228,9 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
       const int i = tid + 256 * u;
       const int key = i / (D / 4), e = 4 * (i - key * (D / 4));
       if (i < SK_XK * D / 4) {
-        float* dst = Ks + key * LDKE + e;
-        dst[0] = kx[u].x; dst[1] = kx[u].y; dst[2] = kx[u].z; dst[3] = kx[u].w;
+        float2* dst = reinterpret_cast<float2*>(Ks + key * LDKE + e);
+        dst[0] = make_float2(kx[u].x, kx[u].y);
+        dst[1] = make_float2(kx[u].z, kx[u].w);
       }
     }
 #pragma unroll
@@ -241,32 +253,37 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
       mloc = fmaxf(mloc, s[r]);
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(mu, mloc);     // finite: every stage has a key
-    const float alpha = expf(mu - mnew);    // 0 on the first stage
+    if (__any(mloc > mu + SK_XTAU)) {       // also the first stage (mu = -inf)
+      const float mnew = fmaxf(mu, mloc);   // finite: every stage has a key
+      const float alpha = __builtin_amdgcn_exp2f(mu - mnew);   // 0 the first time
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+      mu = mnew;
+    }
     float p[16];
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = expf(s[r] - mnew);             // 0 for keys past the slice
+      p[r] = __builtin_amdgcn_exp2f(s[r] - mu);   // 0 for keys past the slice
       lsum += p[r];
     }
-    l = l * alpha + lsum;
+    l += lsum;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
 #pragma unroll
       for (int t = 0; t < 16; ++t)
         acc[cb] = mfma32x32x2(Vs[acc_row(t, lane) * LDV + 32 * cb + l32], p[t], acc[cb]);
     }
-    mu = mnew;
     __syncthreads();
   }
   l += __shfl_xor(l, 32, 64);               // the query's two lane halves
   if (qok) {
     float* P = parts + ((head * m + q) * nsplit + split) * (2 + dv);
     if (g == 0) {
-      P[0] = mu;
+      P[0] = mu * LN2;
       P[1] = l;
     }
     // acc[cb][r] = sum_i p_i v_i[c], c = 32 cb + acc_row(r, lane)
@@ -301,7 +318,6 @@ void sk_exact_mfma(const float* __restrict__ K, const float* __restrict__ V,
 //       instruction r taking keys 4 k + r (k = lane / 16) with B = P straight
 //       from S's register r and A = those keys' value rows.
 // The partial record is the one of sk_exact_decode (mu = ref in natural-log units).
-#define SK_XTAU 8.f
 template <int D, int DV, int QB>
 __global__ __launch_bounds__(256)
 void sk_exact_mfma16(const float* __restrict__ K, const float* __restrict__ V,
@@ -620,10 +636,13 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
   const float* Kh = K + head * n * d;
   const float* Vh = V + head * n * dv;
 
+  // base-2 softmax: query prescaled by log2 e, mu in log2 units until the record
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float LN2 = 0.6931471805599453f;
   float qr[B], acc[B];
 #pragma unroll
   for (int c = 0; c < B; ++c) {
-    qr[c] = (qok && c < d) ? Q[(head * m + q) * d + c] : 0.f;
+    qr[c] = (qok && c < d) ? Q[(head * m + q) * d + c] * LOG2E : 0.f;
     acc[c] = 0.f;
   }
   float mu = -INFINITY, l = 0.f;
@@ -655,7 +674,7 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
       mx = fmaxf(mx, s[kk]);
     }
     const float mnew = fmaxf(mu, mx);
-    const float alpha = expf(mu - mnew);
+    const float alpha = __builtin_amdgcn_exp2f(mu - mnew);
     float lb = 0.f;
     // Per-stage sums first (two-level summation); at B = 128 the stage sum of
     // the values would not fit in registers, so the values go straight in.
@@ -668,7 +687,7 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const float w = expf(s[kk] - mnew);
+      const float w = __builtin_amdgcn_exp2f(s[kk] - mnew);
       lb += w;
 #pragma unroll
       for (int c = 0; c < B; ++c) {
@@ -685,7 +704,7 @@ void sk_exact_tiled(const float* __restrict__ K, const float* __restrict__ V,
   }
   if (qok) {
     float* P = parts + ((head * m + q) * nsplit + split) * (2 + dv);
-    P[0] = mu;
+    P[0] = mu * LN2;
     P[1] = l;
 #pragma unroll
     for (int c = 0; c < B; ++c)
