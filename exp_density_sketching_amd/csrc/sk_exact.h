@@ -527,13 +527,20 @@ void sk_exact_decode(const float* __restrict__ K, const float* __restrict__ V,
   const float* Kh = K + head * n * d;
   const float* Vh = V + head * n * dv;
 
+  // base-2 softmax: queries prescaled by log2 e, maxima in log2 units until the
+  // record
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float LN2 = 0.6931471805599453f;
   float4 q4[MQ];
   float mu[MQ], l[MQ];
   float4 acc[MQ];
 #pragma unroll
   for (int i = 0; i < MQ; ++i) {
     q4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < m && kin) q4[i] = *reinterpret_cast<const float4*>(Q + (head * m + i) * d + c4);
+    if (i < m && kin) {
+      q4[i] = *reinterpret_cast<const float4*>(Q + (head * m + i) * d + c4);
+      q4[i].x *= LOG2E; q4[i].y *= LOG2E; q4[i].z *= LOG2E; q4[i].w *= LOG2E;
+    }
     mu[i] = -INFINITY;
     l[i] = 0.f;
     acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -567,12 +574,12 @@ void sk_exact_decode(const float* __restrict__ K, const float* __restrict__ V,
       }
       if (mx == -INFINITY) continue;
       const float mnew = fmaxf(mu[i], mx);
-      const float alpha = expf(mu[i] - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(mu[i] - mnew);
       float lb = 0.f;
       float4 ab = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int u = 0; u < SK_EX_U; ++u) {
-        const float w = expf(s[u] - mnew);   // exp(-inf) = 0 for missing keys
+        const float w = __builtin_amdgcn_exp2f(s[u] - mnew);   // 2^-inf = 0 for missing keys
         lb += w;
         ab.x += w * v4[u].x; ab.y += w * v4[u].y;
         ab.z += w * v4[u].z; ab.w += w * v4[u].w;
@@ -602,11 +609,11 @@ void sk_exact_decode(const float* __restrict__ K, const float* __restrict__ V,
       float sum = 0.f;
       if (ms != -INFINITY) {
         for (int g = 0; g < NG; ++g) {
-          const float sc = expf(sm_mu[i][g] - ms);
+          const float sc = __builtin_amdgcn_exp2f(sm_mu[i][g] - ms);
           sum += (tid == 0 ? sm_l[i][g] : sm_acc[i][g * B + tid - 1]) * sc;
         }
       }
-      if (tid == 0) { P[0] = ms; P[1] = sum; }
+      if (tid == 0) { P[0] = ms * LN2; P[1] = sum; }
       else P[1 + tid] = sum;
     }
   }
