@@ -216,7 +216,9 @@ int sketch_step(sk_handle s, const float* k, const float* v, const float* q, flo
  * finite scores; Z is returned as a plain fp32 sum e^mu * l (mu the largest
  * score), so it overflows to +inf once ln Z exceeds about 88.7 (ln of the
  * largest fp32), e.g. a largest score of 80 with more than e^8.7 ~ 6000 keys at
- * that score.
+ * that score.  The kernels take exponentials in base 2 (each query scaled by
+ * log2 e in fp32), so a score's rounding error grows with its size: a few units
+ * of 2^-24 times the largest |score|, relative, in Z.
  *   K [h][n][d], V [h][n][dv], Q [h][m][d], out [h][m][dv], Z [h][m]: device.
  *   hip_stream: hipStream_t to run on (NULL = default stream).
  * The per-slice partials (h * m * slices * (2 + dv) floats) live in a buffer
