@@ -61,7 +61,7 @@ struct sk_coreset {
   int fill = -1;              // buffer of the partial block
   std::vector<int> level;     // buffer per level, -1 = empty
   std::vector<int> pending;   // full blocks not yet entered at level 0, in order
-  double* inv = nullptr;      // 1/j, j < CS_NINV
+  double* inv = nullptr;      // 1/j, j < CS_NINV; then (p+1)!/(p+1+k)!
   double* gram = nullptr;     // Gram workspace
   size_t gram_bytes = 0;
   float* parts = nullptr;     // tail-query partials
@@ -360,13 +360,19 @@ int coreset_create(int d, int dv, int p, int h, int block, double c0, uint64_t s
   if (c == nullptr) return SK_ENOMEM;
   c->d = d; c->dv = dv; c->p = p; c->h = h; c->B = block; c->c0 = c0; c->seed = seed;
   c->stream = reinterpret_cast<hipStream_t>(hip_stream);
-  std::vector<double> inv(CS_NINV, 1.0);
+  // 1/j for j < CS_NINV, then the tail series' coefficients (p+1)!/(p+1+k)!
+  // (zero once p + 1 + k reaches CS_NINV)
+  std::vector<double> inv(2 * CS_NINV, 0.0);
+  inv[0] = 1.0;
   for (int j = 1; j < CS_NINV; ++j) inv[j] = 1.0 / (double)j;
+  inv[CS_NINV] = 1.0;
+  for (int k = 1; k < CS_NINV && p + 1 + k < CS_NINV; ++k)
+    inv[CS_NINV + k] = inv[CS_NINV + k - 1] * inv[p + 1 + k];
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->num_cu, hipDeviceAttributeMultiprocessorCount, c->device) !=
           hipSuccess ||
-      hipMalloc(&c->inv, sizeof(double) * CS_NINV) != hipSuccess ||
-      hipMemcpy(c->inv, inv.data(), sizeof(double) * CS_NINV, hipMemcpyHostToDevice) !=
+      hipMalloc(&c->inv, sizeof(double) * 2 * CS_NINV) != hipSuccess ||
+      hipMemcpy(c->inv, inv.data(), sizeof(double) * 2 * CS_NINV, hipMemcpyHostToDevice) !=
           hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(c->inv);

@@ -88,20 +88,22 @@ __device__ __forceinline__ double cs_uniform(unsigned long long seed,
 }
 
 // R_p(x) = sum_{j > p} x^j / j! in float64 for N values x at once.  For
-// |x| <= p + 1 the series x^(p+1) / (p+1)! * sum_k x^k (p+1)! / (p+1+k)! by Horner
-// from the top, its terms counted for the largest such |x| of the N values (until
-// the ratio of the next term to the first falls below 2^-56), so every value
-// advances through the same fused multiply-adds; there the terms shrink from the
-// first on, so the sum's rounding stays within a few units of the last place of
-// the largest term.  For |x| > p + 1, e^x - T_p(x), T_p by Horner: for x > p + 1,
-// e^x exceeds twice T_p(x); below -(p + 1), T_p(x) and e^x do not cancel (T_p is
-// positive for even p, negative there for odd p).  (The float64 oracle chooses
-// between the plain series and e^x - T_p(x) by the size of the series' largest
-// term; both are accurate to a few units of the last place, which a Gram entry
-// of the walk needs.)
+// |x| <= p + 1 the series x^(p+1) / (p+1)! * sum_k coef[k] x^k with coef[k] =
+// (p+1)! / (p+1+k)! (the handle's table, coef[0] = 1), one fused multiply-add
+// per term by Horner from the top, its terms counted for the largest such |x| of
+// the N values (until the ratio of the next term to the first falls below
+// 2^-56), so every value advances through the same instructions; there the
+// terms shrink from the first on, so the sum's rounding stays within a few units
+// of the last place of the largest term.  For |x| > p + 1, e^x - T_p(x), T_p by
+// Horner: for x > p + 1, e^x exceeds twice T_p(x); below -(p + 1), T_p(x) and e^x
+// do not cancel (T_p is positive for even p, negative there for odd p).  (The
+// float64 oracle chooses between the plain series and e^x - T_p(x) by the size of
+// the series' largest term; both are accurate to a few units of the last place,
+// which a Gram entry of the walk needs.)
 template <int N>
-__device__ inline void cs_tail_exp64_n(const double (&x)[N], int p,
-                                       const double* __restrict__ cs_inv, double (&out)[N]) {
+__device__ inline void cs_tail_exp64_c(const double (&x)[N], int p,
+                                       const double* __restrict__ cs_inv,
+                                       const double* __restrict__ coef, double (&out)[N]) {
 #pragma clang fp contract(off)
   const double lim = (double)(p + 1);
   double X = 0.0;
@@ -114,12 +116,16 @@ __device__ inline void cs_tail_exp64_n(const double (&x)[N], int p,
     t *= X * cs_inv[p + 1 + nt];
   }
   double hh[N], xp[N];
+  const double cn = coef[nt];
 #pragma unroll
-  for (int e = 0; e < N; ++e) hh[e] = xp[e] = 1.0;
-  for (int k = nt; k >= 1; --k) {
-    const double ik = cs_inv[p + 1 + k];
+  for (int e = 0; e < N; ++e) {
+    hh[e] = cn;
+    xp[e] = 1.0;
+  }
+  for (int k = nt - 1; k >= 0; --k) {
+    const double ck = coef[k];
 #pragma unroll
-    for (int e = 0; e < N; ++e) hh[e] = fma(x[e] * ik, hh[e], 1.0);
+    for (int e = 0; e < N; ++e) hh[e] = fma(hh[e], x[e], ck);
   }
   for (int j = 1; j <= p + 1; ++j) {
     const double ij = cs_inv[j];
@@ -130,7 +136,6 @@ __device__ inline void cs_tail_exp64_n(const double (&x)[N], int p,
   for (int e = 0; e < N; ++e) {
     double r = xp[e] * hh[e];
     if (fabs(x[e]) > lim) {
-      // e^x - T_p(x), T_p by Horner from the top
       double tp = 1.0;
       for (int i = p; i >= 1; --i) tp = 1.0 + x[e] * cs_inv[i] * tp;
       r = exp(x[e]) - tp;
@@ -242,7 +247,7 @@ void cs_gram_kernel(CsOps ops, int B, int d, int dv, int p, int h,
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) xs[4 * cb + i] = kacc[rb][cb][i];
-    cs_tail_exp64_n<8>(xs, p, inv, rs);
+    cs_tail_exp64_c<8>(xs, p, inv, inv + CS_NINV, rs);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       double g[4];
