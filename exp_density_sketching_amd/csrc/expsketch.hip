@@ -600,8 +600,9 @@ bool plan_kr_units(sk_sketch* s) {
   }
   // groups by work per key (matrix instructions per key, in 32x32x2 units): the
   // 8-block units 4, a 4-block level-2 unit 2, the level 0/1 units 1 (few matrix
-  // instructions, but each 4-key step waits on its loads); heaviest first, so a
-  // unit's position no longer follows its level
+  // instructions, but each 4-key step waits on its loads); groups sorted
+  // heaviest first, so a unit's position no longer follows its level (the
+  // kernel takes a head's items in the reverse order, lightest group first)
   auto weight = [&](const KrUnit& x) {
     if (x.mode == KR_SMALL) return 1;
     if (x.mode == KR_WIDE) return x.C - 64 * x.ct > 32 ? 4 : 2;
@@ -1159,7 +1160,21 @@ KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
     const char* v = std::getenv("EXPSKETCH_UPDATE_SPLITS");
     return v ? std::max(0, std::atoi(v)) : 0;
   }();
-  if (forced > 0) return kr_splits_for(s, n, std::min<long long>(forced, std::max(1LL, n)));
+  // A head's items are taken lightest group first (EXPSKETCH_KR_REVERSE=0 takes
+  // the heaviest first, tuning aid): a light unit's split runs over the most
+  // keys, so its waves are the longest; started last they set the launch's tail
+  // (measured on MI355X: 32-head workload 23.6 -> 20.5 ms per launch on one box,
+  // 20.5-20.9 -> 20.5 on others; d = 32, p = 3 workload 0.76 -> 0.79 of the fp32
+  // peak; d = 16, p = 4 unchanged).
+  static const int rev = [] {
+    const char* v = std::getenv("EXPSKETCH_KR_REVERSE");
+    return v ? (std::atoi(v) != 0 ? 1 : 0) : 1;
+  }();
+  if (forced > 0) {
+    KrSplits P = kr_splits_for(s, n, std::min<long long>(forced, std::max(1LL, n)));
+    P.rev = rev;
+    return P;
+  }
   const long long simds = (long long)std::max(1, s->dev.num_cu) * 4;
   const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
   KrSplits best = kr_splits_for(s, n, 1);
@@ -1178,6 +1193,7 @@ KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
       best = P;
     }
   }
+  best.rev = rev;
   return best;
 }
 

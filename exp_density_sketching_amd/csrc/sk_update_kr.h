@@ -86,6 +86,7 @@ struct KrSplits {
   int ns[KR_MAXG];               // splits of each group
   long long item0[KR_MAXG + 1];  // first item of each group within a head; item0[ngroup] = items
   long long kps[KR_MAXG];        // keys per split of each group
+  int rev;                       // 1: a head's items taken lightest group first
 };
 
 // src[lane N of this lane's 16-lane row] * y: one v_mul_f32_dpp row_newbcast.
@@ -419,11 +420,12 @@ void sk_update_kr_kernel(const float* __restrict__ K, const float* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // workgroups of one XCD take a contiguous range of items: the items of one key
-  // split (all units of a group) read the same key rows from that XCD's L2
+  // split (all units of a group) read the same key rows from that XCD's L2; with
+  // P.rev a head's items run from its last (lightest group, longest waves) down
   const long long item = xcd_remap(blockIdx.x, nwg) * KR_WAVES + wave;
   if (item >= nitems) return;
   const long long head = item / per_head;
-  const long long li = item - head * per_head;
+  const long long li = P.rev ? per_head - 1 - (item - head * per_head) : item - head * per_head;
   // the item's group (scalar selects: no dynamic index into the argument block)
   long long gbase = P.item0[0], kps = P.kps[0];
   int u0 = P.unit0[0], gn = P.unit0[1] - P.unit0[0], gns = P.ns[0];
