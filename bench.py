@@ -45,10 +45,14 @@ def parse():
     return ap.parse_args()
 
 
+# The sources a kernel's committed traffic counters depend on: the kernel itself
+# and the host file that picks its launch shape (split counts, slices).
 KERNEL_SOURCES = {
-    "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h", "sk_reduce.h"],
-    "sk_update_kr_kernel": ["sk_update_kr.h", "sk_update_kr.hip", "sk_common.h", "sk_reduce.h"],
-    "sk_exact_decode": ["sk_exact.h", "sk_common.h"],
+    "sk_update_kernel": ["sk_update.h", "sk_common.h", "sk_elementwise.h", "sk_reduce.h",
+                         "expsketch.hip"],
+    "sk_update_kr_kernel": ["sk_update_kr.h", "sk_update_kr.hip", "sk_common.h", "sk_reduce.h",
+                            "expsketch.hip"],
+    "sk_exact_decode": ["sk_exact.h", "sk_common.h", "expsketch.hip"],
 }
 
 

@@ -1154,7 +1154,8 @@ KrSplits kr_splits_for(const sk_sketch* s, long long n, long long ns0) {
 
 // Splits of the heaviest group: the fewest key-steps on the busiest SIMD (waves
 // per SIMD times the heaviest group's split length), plus a small charge per
-// partial buffer (written, then read by the reduce); at least 256 keys a split.
+// partial buffer (written, then read by the reduce), plus a tail when a SIMD
+// takes its waves in more than one round; at least 256 keys a split.
 KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
   static const int forced = [] {
     const char* v = std::getenv("EXPSKETCH_UPDATE_SPLITS");
@@ -1187,7 +1188,14 @@ KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
     // wave per SIMD a launch runs about 20% slower than with three (no other wave
     // covers its waits), with two about 5% slower
     const double shape = per_simd == 1 ? 1.2 : per_simd == 2 ? 1.05 : 1.0;
-    const double cost = (double)per_simd * (double)P.kps[0] * (1.0 + 0.003 * P.nsplit) * shape;
+    // with more waves than a SIMD holds at once (three), they start as earlier
+    // ones end and finish unevenly: the launch's tail, measured on MI355X as
+    // about 2.2 wave lengths (32-head d = 64 workload: 8 splits 20.0 ms per
+    // launch, 12 19.5, 16 19.0, 24 18.1-18.4, 32 18.2; one-round launches, where
+    // all waves start together, have no such tail)
+    const double tail = per_simd > 3 ? 2.2 : 0.0;
+    const double cost =
+        (double)P.kps[0] * ((double)per_simd * (1.0 + 0.003 * P.nsplit) * shape + tail);
     if (best_cost < 0.0 || cost < best_cost - 1e-9) {
       best_cost = cost;
       best = P;
