@@ -1130,6 +1130,10 @@ long long kr_max_keys(const sk_sketch* s) {
 
 // Key splits of the digit-organised update for n keys, given the split count of
 // the heaviest group: a lighter group takes proportionally fewer, longer splits.
+// Bytes of each of the two split-partials buffers above which an update call
+// takes per-call partials and reduces them at once instead.
+constexpr size_t kDeferBytes = size_t(1) << 30;
+
 KrSplits kr_splits_for(const sk_sketch* s, long long n, long long ns0) {
   KrSplits P{};
   P.ngroup = (int)s->kweight.size();
@@ -1178,10 +1182,16 @@ KrSplits choose_kr_splits(const sk_sketch* s, long long n) {
   }
   const long long simds = (long long)std::max(1, s->dev.num_cu) * 4;
   const long long max_ns = std::max(1LL, std::min(64LL, n / 256));
+  // split partials that fit the kept buffers (the deferred reduce) are preferred
+  // to more splits that would need per-call buffers
+  const size_t state_bytes = sizeof(float) * (size_t)s->XS * (size_t)s->h;
   KrSplits best = kr_splits_for(s, n, 1);
   double best_cost = -1.0;
   for (long long ns = 1; ns <= max_ns; ++ns) {
     const KrSplits P = kr_splits_for(s, n, ns);
+    if (P.nsplit > 1 && 2 * state_bytes <= kDeferBytes &&
+        (size_t)P.nsplit * state_bytes > kDeferBytes)
+      continue;
     const long long waves = P.item0[P.ngroup] * s->h;
     const long long per_simd = (waves + simds - 1) / simds;   // they share its matrix core
     // measured on MI355X (a SIMD holds three of this kernel's waves): with one
@@ -1242,9 +1252,6 @@ int choose_update_splits(const sk_sketch* s, long long n) {
   return best;
 }
 
-// Bytes of each of the two split-partials buffers above which an update call
-// takes per-call partials and reduces them at once instead.
-constexpr size_t kDeferBytes = size_t(1) << 30;
 
 // Adds the last update call's pending partials into the state (fixed split order).
 int flush_pending(sk_sketch* s) {
