@@ -87,3 +87,24 @@ def test_digit_kernel_long_call_cut(tmp_path):
     keys = [2, 3]
     _child(tmp_path, "cut", keys, EXPSKETCH_UPDATE_MAXKEYS="300")
     _compare(tmp_path, "cut", keys, "digits")
+
+
+def test_digit_kernel_split_cap_large_state():
+    """A 64-head state of 69 MB (d = dv = 64, p = 2) with 8192 keys per head: the
+    update takes its waves in many rounds per SIMD, where the split chooser's cost
+    is lowest at 16 to 24 key splits, whose partials (1.1-1.7 GB) would not fit
+    the kept partial buffers (1 GiB each); the chooser then keeps to the split
+    counts that fit (at most 15), so the call keeps the deferred reduce.  Sampled
+    heads against the float64 oracle's direct route."""
+    from synthetic import WORKLOADS
+    w = WORKLOADS[4].scaled(n=8192, m=32, h=64)
+    K, V, Q = generate(w)
+    say(f"split cap: h={w.h} d={w.d} dv={w.dv} p={w.p} n={w.n} m={w.m}")
+    out, Z, sk = run_sketch(w, *gpu(K, V, Q))
+    out, Z = host(out, Z)
+    sk.destroy()
+    for hh in (0, 29, 63):
+        o_ref, z_ref = oracle.sketch_direct(K[hh], V[hh], Q[hh], w.p)
+        ez, eo = zrel(Z[hh], z_ref), oabs(out[hh], o_ref)
+        say(f"  head {hh}: rel Z {ez:.2e} abs o {eo:.2e}")
+        assert ez <= SK_Z_REL and eo <= SK_O_ABS
