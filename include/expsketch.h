@@ -155,9 +155,10 @@ int sketch_reset(sk_handle s);
  * given sequence of calls the results are deterministic.
  * A launch may split its keys over several workgroups per state entry; the
  * split partials go to two buffers the handle keeps (up to 1 GiB each: split
- * count x state bytes, the count kept within that while two splits fit) and are
- * added into the state by the next launch or the next reader; a state too large
- * for that takes per-call buffers, reduced and released within the call.
+ * count x state bytes; the digit kernel of d = 16, 32, 64 keeps its count within
+ * that while two splits fit) and are added into the state by the next launch or
+ * the next reader; partials beyond that size take per-call buffers, reduced and
+ * released within the call.
  * Errors: SK_EINVAL (NULL/misaligned pointer with n > 0, n < 0), SK_ENOMEM
  * (split workspace), SK_EHIP.
  */
